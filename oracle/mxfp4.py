@@ -1,0 +1,404 @@
+"""Plain, slow CPU oracle for MXFP4 (OCP MX) fake-quantized training.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the library or its binding.
+
+What it computes, and where each step comes from:
+
+* MXFP4 block format -- "ALTO MXFP4 training -- Weight de-oscillation", Jargon
+  ("MXFP4", "E2M1"): 32 values share one scale, each value is a 4-bit element
+  with 2 exponent bits and 1 mantissa bit, range about +-6.  The exact element
+  set {0, .5, 1, 1.5, 2, 3, 4, 6} and the shared-exponent rule
+  floor(log2 amax) - 2 (E8M0 byte = exponent + 127) are the OCP Microscaling
+  Formats (MX) v1.0 conventions; "Unveiling the Potential of Quantization with
+  MXFP4" (abstract) fixes only that the scale is a power of two, and the ALTO
+  page (paragraph on the second cause of oscillation) that it is set by the
+  block's largest magnitude.
+* Q_D (nearest) and Q_S (stochastic) -- "Oscillation-Reduced MXFP4 Training for
+  Vision Transformers" (rebuttal, Question 2) and the ALTO page's Jargon
+  ("Bin", "Stochastic rounding").
+* Group shapes 1x32 / 32x1, the forward product, the STE weight gradient and
+  the double quantization Q_S(Q_D(X)) -- same rebuttal, Question 2 (1) and (2).
+* Random-sign block Hadamard rotation -- ALTO page Jargon ("Randomized Hadamard
+  transform") and "Microscaling FP4 Quantization: MR-GPTQ ..." (section "FP4
+  Quantization with Micro-Rotated GPTQ Algorithm": block-wise Hadamard).
+* Weight de-oscillation -- ALTO page, sections "How does ALTO detect and fix
+  oscillating weights?" and the ratio paragraph (window P = 200, d_w, d_Q,
+  threshold 4.0, snap to the current bin centre).
+
+Readings taken where the pages are silent (each is also listed in the design
+notes): ties round to the even code; values above 6 saturate to 6; the sign bit
+always copies the input's sign bit; an all-zero block has scale byte 0; a
+non-finite block gets scale byte 0xFF and zero codes; stochastic rounding rounds
+up iff r24 < floor(t) with t the 2^24-scaled distance to the lower neighbour and
+r24 the top 24 bits of SplitMix64(seed, idx) (Steele, Lea & Flood, OOPSLA 2014);
+idx is the row-major index in the logical input tensor; codes pack element 2j
+in the low nibble of byte j; 32x1 outputs are stored transposed; the Hadamard
+is the unnormalised Sylvester H32 after a sign flip by a 32-bit mask, computed
+in float32 with stages h = 1, 2, 4, 8, 16.
+
+Parity unpinned (conventions the pages do not fix, checked only for
+self-consistency): the nibble order, the seed offsets of the backward
+quantizers, the float32 butterfly order of the Hadamard.
+
+Every array here is float64 unless stated; inputs are float32 values (bf16
+inputs are widened to float32 by the caller, which is exact).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "E2M1_MAGNITUDES", "ROW", "COL", "RNE", "SR", "BLOCK", "SCALE_NAN",
+    "splitmix64", "sr_bits24", "hadamard_matrix32", "fwht32_f32", "sign_vector",
+    "shared_exponent", "quantize_blocks", "pack_codes", "unpack_codes",
+    "quantize", "dequantize", "requantize", "block_indices",
+    "gemm", "gemm_abs", "gemm_grouped", "linear_fwd", "linear_bwd",
+    "bin_value_f32", "deosc_init", "deosc_step", "bf16_bits_to_f32",
+]
+
+# OCP MX E2M1 magnitudes, indexed by the 3 low bits of a code.
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+BLOCK = 32
+ROW, COL = 0, 1          # 1x32 blocks along the last axis / 32x1 blocks along the first
+RNE, SR = 0, 1           # Q_D (nearest, ties to even) / Q_S (stochastic)
+SCALE_NAN = 0xFF         # E8M0 NaN encoding
+E8M0_BIAS = 127
+EMIN, EMAX = -127, 127
+
+
+# ---------------------------------------------------------------- random bits
+def splitmix64(seed: int, idx) -> np.ndarray:
+    """Output number idx+1 of SplitMix64 started from state `seed` (uint64).
+
+    SplitMix64 (Steele, Lea & Flood, "Fast splittable pseudorandom number
+    generators", OOPSLA 2014): the state advances by the odd constant
+    0x9E3779B97F4A7C15, and each output is the state passed through the
+    variant-13 64-bit finalizer (xor-shift 30, multiply, xor-shift 27,
+    multiply, xor-shift 31).  Counter-based form: state = seed + (idx+1)*gamma.
+    """
+    gamma = np.uint64(0x9E3779B97F4A7C15)
+    m1 = np.uint64(0xBF58476D1CE4E5B9)
+    m2 = np.uint64(0x94D049BB133111EB)
+    i = np.asarray(idx, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = np.uint64(seed % (1 << 64)) + (i + np.uint64(1)) * gamma
+        z = (z ^ (z >> np.uint64(30))) * m1
+        z = (z ^ (z >> np.uint64(27))) * m2
+        z = z ^ (z >> np.uint64(31))
+    return z
+
+
+def sr_bits24(seed: int, idx) -> np.ndarray:
+    """The 24 random bits one stochastic rounding decision uses: the top 24 bits."""
+    return (splitmix64(seed, idx) >> np.uint64(40)).astype(np.int64)
+
+
+# ---------------------------------------------------------------- Hadamard
+def hadamard_matrix32() -> np.ndarray:
+    """Unnormalised Sylvester Hadamard matrix, H[i, j] = (-1)^popcount(i & j)."""
+    i = np.arange(32)[:, None]
+    j = np.arange(32)[None, :]
+    parity = np.vectorize(lambda v: bin(int(v)).count("1") & 1)(i & j)
+    return np.where(parity == 1, -1.0, 1.0)
+
+
+def sign_vector(sign_mask: int) -> np.ndarray:
+    """s_j = -1 where bit j of the 32-bit mask is set, else +1 (float32)."""
+    bits = (np.uint64(sign_mask & 0xFFFFFFFF) >> np.arange(32, dtype=np.uint64)) & np.uint64(1)
+    return np.where(bits == 1, np.float32(-1.0), np.float32(1.0)).astype(np.float32)
+
+
+def fwht32_f32(v: np.ndarray) -> np.ndarray:
+    """Fast Walsh-Hadamard transform of each length-32 vector on the last axis.
+
+    float32 butterflies (a, b) -> (a + b, a - b) between positions i and i + h
+    for h = 1, 2, 4, 8, 16; the result equals hadamard_matrix32() @ v when no
+    rounding happens.
+    """
+    y = np.array(v, dtype=np.float32, copy=True)
+    assert y.shape[-1] == 32
+    h = 1
+    while h < 32:
+        lead = y.shape[:-1]
+        z = y.reshape(lead + (32 // (2 * h), 2, h))
+        a = z[..., 0, :].copy()
+        b = z[..., 1, :].copy()
+        z[..., 0, :] = a + b
+        z[..., 1, :] = a - b
+        y = z.reshape(lead + (32,))
+        h *= 2
+    return y
+
+
+# ---------------------------------------------------------------- quantizer
+def shared_exponent(amax: np.ndarray) -> np.ndarray:
+    """OCP shared exponent floor(log2 amax) - 2, clamped to [-127, 127].
+
+    amax == 0 gives -127.  floor(log2 a) is taken from frexp (a = m * 2^E with
+    m in [0.5, 1) => floor(log2 a) = E - 1), which is exact.
+    Returns int64; non-finite amax is flagged by the caller.
+    """
+    amax = np.asarray(amax, dtype=np.float64)
+    safe = np.where(np.isfinite(amax) & (amax > 0), amax, 1.0)
+    _, E = np.frexp(safe)
+    e = np.clip(E.astype(np.int64) - 1 - 2, EMIN, EMAX)
+    return np.where(amax > 0, e, EMIN)
+
+
+def _round_nearest_even(a: np.ndarray) -> np.ndarray:
+    """Index in E2M1_MAGNITUDES of the element nearest to a (>= 0), ties to the even index.
+
+    Brute force over all 8 candidates; every distance is exact in float64.
+    """
+    d = np.abs(a[..., None] - E2M1_MAGNITUDES)
+    dmin = d.min(axis=-1, keepdims=True)
+    cand = d == dmin
+    even = cand & (np.arange(8) % 2 == 0)
+    return np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1)).astype(np.int64)
+
+
+def _round_stochastic(a: np.ndarray, r24: np.ndarray) -> np.ndarray:
+    """Stochastic rounding of a >= 0 to E2M1 magnitudes.
+
+    a >= 6 saturates to 6.  Otherwise lo <= a < hi are neighbours in the set,
+    t = floor((a - lo) / (hi - lo) * 2^24) and the result is hi iff r24 < t,
+    so P(hi) = floor(t) / 2^24 -- the odds follow the distance to each neighbour.
+    """
+    sat = a >= 6.0
+    a_in = np.where(sat, 0.0, a)
+    k = np.searchsorted(E2M1_MAGNITUDES, a_in, side="right") - 1
+    k = np.clip(k, 0, 6)
+    lo = E2M1_MAGNITUDES[k]
+    hi = E2M1_MAGNITUDES[k + 1]
+    t = np.floor((a_in - lo) / (hi - lo) * float(1 << 24))
+    up = r24.astype(np.float64) < t
+    return np.where(sat, 7, k + up.astype(np.int64)).astype(np.int64)
+
+
+def quantize_blocks(v, idx, rounding: int = RNE, seed: int = 0,
+                    hadamard: bool = False, sign_mask: int = 0):
+    """Quantize blocks of 32 values.
+
+    v: [..., 32] float32 values (one block per row of the last axis).
+    idx: [..., 32] logical element indices (used only by stochastic rounding).
+    Returns (codes [..., 32] uint8, one code per element; scale bytes [...] uint8).
+    """
+    v = np.asarray(v, dtype=np.float32)
+    assert v.shape[-1] == BLOCK
+    if hadamard:
+        v = fwht32_f32(v * sign_vector(sign_mask))
+    x = v.astype(np.float64)
+    amax = np.max(np.abs(x), axis=-1)
+    finite = np.isfinite(amax)
+    e = shared_exponent(amax)
+    a = np.ldexp(np.abs(np.where(np.isfinite(x), x, 0.0)), (-e)[..., None])
+    if rounding == RNE:
+        mag = _round_nearest_even(a)
+    elif rounding == SR:
+        mag = _round_stochastic(a, sr_bits24(seed, idx))
+    else:
+        raise ValueError("rounding must be RNE or SR")
+    sign = np.signbit(v).astype(np.int64)
+    codes = (sign << 3) | mag
+    codes = np.where(finite[..., None], codes, 0).astype(np.uint8)
+    scales = np.where(finite, e + E8M0_BIAS, SCALE_NAN).astype(np.uint8)
+    return codes, scales
+
+
+def pack_codes(codes: np.ndarray) -> np.ndarray:
+    """Two 4-bit codes per byte along the last axis: element 2j low nibble, 2j+1 high."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_codes(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = p & 0x0F
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def block_indices(rows: int, cols: int, axis: int) -> np.ndarray:
+    """Logical row-major indices arranged as blocks: [outer, inner/32, 32]."""
+    lin = np.arange(rows * cols, dtype=np.int64).reshape(rows, cols)
+    if axis == COL:
+        lin = lin.T
+    outer, inner = lin.shape
+    return lin.reshape(outer, inner // BLOCK, BLOCK)
+
+
+def quantize(x, axis: int = ROW, rounding: int = RNE, seed: int = 0,
+             hadamard: bool = False, sign_mask: int = 0):
+    """MXFP4-quantize a [rows, cols] float32 matrix.
+
+    ROW: 1x32 blocks along cols -> codes [rows, cols/2], scales [rows, cols/32].
+    COL: 32x1 blocks along rows, stored transposed -> codes [cols, rows/2],
+         scales [cols, rows/32].
+    """
+    x = np.asarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    m = x if axis == ROW else x.T
+    outer, inner = m.shape
+    if inner % BLOCK:
+        raise ValueError("block axis must be a multiple of 32")
+    blocks = m.reshape(outer, inner // BLOCK, BLOCK)
+    idx = block_indices(rows, cols, axis)
+    codes, scales = quantize_blocks(blocks, idx, rounding, seed, hadamard, sign_mask)
+    return pack_codes(codes.reshape(outer, inner)), scales
+
+
+def dequantize(codes, scales, rows: int, cols: int, axis: int = ROW,
+               hadamard: bool = False, sign_mask: int = 0) -> np.ndarray:
+    """Exact values of a packed MXFP4 matrix, returned in the logical [rows, cols] layout.
+
+    value = (-1)^sign * E2M1[code & 7] * 2^(byte - 127); byte 0xFF -> NaN.
+    With the rotation: x = s * FWHT(y) * 2^-5 per block (float32), since H H^T = 32 I.
+    """
+    outer, inner = (rows, cols) if axis == ROW else (cols, rows)
+    c = unpack_codes(np.asarray(codes, dtype=np.uint8).reshape(outer, inner // 2))
+    c = c.reshape(outer, inner // BLOCK, BLOCK)
+    s = np.asarray(scales, dtype=np.uint8).reshape(outer, inner // BLOCK).astype(np.int64)
+    mag = E2M1_MAGNITUDES[c & 7]
+    val = np.where(c & 8, -mag, mag)
+    val = np.ldexp(val, (s - E8M0_BIAS)[..., None])
+    val = np.where((s == SCALE_NAN)[..., None], np.nan, val)
+    if hadamard:
+        y = val.astype(np.float32)
+        val = (fwht32_f32(y) * np.float32(2.0 ** -5) * sign_vector(sign_mask)).astype(np.float64)
+    val = val.reshape(outer, inner)
+    return val if axis == ROW else val.T.copy()
+
+
+def requantize(codes, scales, rows: int, cols: int, rounding: int = SR, seed: int = 0):
+    """Double quantization Q(Q_D(X)): a row-blocked packed [rows, cols] matrix is
+    dequantized exactly and re-quantized with 32x1 blocks (output transposed)."""
+    deq = dequantize(codes, scales, rows, cols, ROW)
+    return quantize(deq.astype(np.float32), COL, rounding, seed)
+
+
+# ---------------------------------------------------------------- GEMM
+def gemm(a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int,
+         alpha: float = 1.0) -> np.ndarray:
+    """C[m, n] = alpha * sum_k deq(A)[m, k] * deq(B)[n, k]  (A [M, K], B [N, K], both
+    row-blocked along K), in float64 from exactly dequantized operands."""
+    A = dequantize(a_codes, a_scales, M, K, ROW)
+    B = dequantize(b_codes, b_scales, N, K, ROW)
+    return alpha * (A @ B.T)
+
+
+def gemm_abs(a_codes, a_scales, b_codes, b_scales, M: int, N: int, K: int,
+             alpha: float = 1.0) -> np.ndarray:
+    """sum_k |alpha * deq(A)[m, k] * deq(B)[n, k]|: the scale of the GEMM tolerance."""
+    A = dequantize(a_codes, a_scales, M, K, ROW)
+    B = dequantize(b_codes, b_scales, N, K, ROW)
+    return abs(alpha) * (np.abs(A) @ np.abs(B).T)
+
+
+def gemm_grouped(a_codes, a_scales, b_codes, b_scales, offs, N: int, K: int,
+                 alpha: float = 1.0) -> np.ndarray:
+    """Per group g: rows offs[g]..offs[g+1] of C = A_rows . B_g^T, B_g = g-th [N, K] matrix."""
+    offs = [int(o) for o in offs]
+    M = offs[-1]
+    a_codes = np.asarray(a_codes).reshape(M, K // 2)
+    a_scales = np.asarray(a_scales).reshape(M, K // BLOCK)
+    G = len(offs) - 1
+    b_codes = np.asarray(b_codes).reshape(G, N, K // 2)
+    b_scales = np.asarray(b_scales).reshape(G, N, K // BLOCK)
+    C = np.zeros((M, N), dtype=np.float64)
+    for g in range(G):
+        r0, r1 = offs[g], offs[g + 1]
+        if r1 > r0:
+            C[r0:r1] = gemm(a_codes[r0:r1], a_scales[r0:r1], b_codes[g], b_scales[g],
+                            r1 - r0, N, K, alpha)
+    return C
+
+
+# ---------------------------------------------------------------- linear layer
+def linear_fwd(x, w):
+    """Forward of the quantized linear layer: Y = Q_D(X) . Q_D(W)^T with 1x32 RNE
+    blocks along K for both (rebuttal, Question 2 (1)).  Returns Y and the packed
+    operands kept for the backward pass."""
+    x = np.asarray(x, dtype=np.float32)
+    w = np.asarray(w, dtype=np.float32)
+    M, K = x.shape
+    N = w.shape[0]
+    xq = quantize(x, ROW, RNE)
+    wq = quantize(w, ROW, RNE)
+    y = gemm(xq[0], xq[1], wq[0], wq[1], M, N, K)
+    return y, xq, wq
+
+
+def linear_bwd(dy, xq, wq, M: int, N: int, K: int, seed: int):
+    """Backward of the quantized linear layer with straight-through gradients.
+
+    dX = Q_S^(3)(dY) [1x32 along N] . Q_S^(4)(Q_D(W)) [32x1 along N]
+    dW = Q_S^(5)(dY)^T [32x1 along M] . Q_S^(6)(Q_D(X)) [32x1 along M]
+    (rebuttal, Question 2: the weight gradient is taken against Q_D(X), and the
+    double quantization gives the 32x1 group shape; the same reasoning is read
+    for dX against Q_D(W)).  Quantizer q uses seed + q.
+    """
+    dy = np.asarray(dy, dtype=np.float32)
+    q3 = quantize(dy, ROW, SR, seed + 3)                 # [M, N/2]
+    q4 = requantize(wq[0], wq[1], N, K, SR, seed + 4)     # [K, N/2]
+    q5 = quantize(dy, COL, SR, seed + 5)                 # [N, M/2]
+    q6 = requantize(xq[0], xq[1], M, K, SR, seed + 6)     # [K, M/2]
+    dx = gemm(q3[0], q3[1], q4[0], q4[1], M, K, N)
+    dw = gemm(q5[0], q5[1], q6[0], q6[1], N, K, M)
+    return dx, dw, (q3, q4, q5, q6)
+
+
+# ---------------------------------------------------------------- de-oscillation
+def bin_value_f32(w) -> np.ndarray:
+    """Centre of each weight's current bin: deq(Q_D(w)) with 1x32 RNE blocks along
+    the last axis (the forward weight quantizer), as float32."""
+    w = np.asarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    c, s = quantize(w, ROW, RNE)
+    return dequantize(c, s, rows, cols, ROW).astype(np.float32)
+
+
+def deosc_init(w):
+    """State of a fresh window: snapshot w_prev = w, d_w = d_Q = 0 (float32)."""
+    w = np.asarray(w, dtype=np.float32)
+    return w.copy(), np.zeros_like(w), np.zeros_like(w)
+
+
+def deosc_step(w, w_prev, d_w, d_q, end_of_window: bool, threshold: float = 4.0):
+    """One post-optimizer-step de-oscillation update ("ALTO MXFP4 training -- Weight
+    de-oscillation", ratio paragraph), float32 arithmetic in the written order:
+
+      d_w += |w - w_prev|;  d_Q += |q(w) - q(w_prev)|;  w_prev = w
+      at the end of the window: flag = d_Q > threshold * d_w; w = q(w) where
+      flagged; then w_prev = w and d_w = d_Q = 0.
+
+    Returns (w, w_prev, d_w, d_q, flags or None) as new float32 arrays.
+    """
+    w = np.asarray(w, dtype=np.float32).copy()
+    w_prev = np.asarray(w_prev, dtype=np.float32)
+    d_w = np.asarray(d_w, dtype=np.float32)
+    d_q = np.asarray(d_q, dtype=np.float32)
+    q_now = bin_value_f32(w)
+    q_old = bin_value_f32(w_prev)
+    d_w = (d_w + np.abs(w - w_prev)).astype(np.float32)
+    d_q = (d_q + np.abs(q_now - q_old)).astype(np.float32)
+    w_prev = w.copy()
+    flags = None
+    if end_of_window:
+        flag = d_q > (np.float32(threshold) * d_w).astype(np.float32)
+        w = np.where(flag, q_now, w).astype(np.float32)
+        w_prev = w.copy()
+        d_w = np.zeros_like(w)
+        d_q = np.zeros_like(w)
+        flags = flag.astype(np.uint8)
+    return w, w_prev, d_w, d_q, flags
+
+
+# ---------------------------------------------------------------- helpers
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float32 (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
