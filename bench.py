@@ -1,0 +1,333 @@
+"""Benchmark of the MXFP4 training hot path on one MI355X.
+
+Step = one MXFP4 linear forward + backward of the Llama-3-8B MLP up-projection
+(M = 8192 tokens, K = 4096, N = 14336, bf16 activations with 1% outlier
+channels x30, weights N(0, 0.02), dY N(0, 1e-3)):
+
+  quantize X (1x32 RNE), quantize W (1x32 RNE), GEMM Y = Q(X) Q(W)^T,
+  dual-quantize dY (1x32 SR + 32x1 SR), requantize Q(W) and Q(X) (32x1 SR),
+  GEMM dX, GEMM dW
+
+-- the kernels mx_linear_fwd / mx_linear_bwd launch, issued one entry point at
+a time so that every kernel is bracketed by events on the stream it runs on.
+value = 6 M N K / step time (TFLOP/s).  The line also carries the dominant
+kernel's roofline (the GEMM, vs the dense FP4 MFMA peak), the oracle's CPU
+throughput on a bounded sample, and the other rows of the path measured on
+their own workloads (quantizer sweep on 8192^2 bf16, MoE grouped GEMM and the
+de-oscillation step on the 32-expert master weights).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+
+PEAK_HBM_GBPS = 8000.0
+PEAK_FP4_TFLOPS = 10100.0
+METRIC = "MXFP4 quantize GB/s + MXFP4 linear fwd+bwd TFLOP/s (%roofline), 1 MI355X"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-parts", action="store_true", help="skip the quantizer sweep / MoE rows")
+    p.add_argument("--only", default=None, help="run one part only: linear|sweep|moe|deosc")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Timer:
+    """Per-kernel event pairs recorded on the launch stream; durations read at the end."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream, self.pairs = torch, stream, {}
+
+    def run(self, name, fn):
+        t = self.torch
+        a = t.cuda.Event(enable_timing=True)
+        b = t.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        fn()
+        b.record(self.stream)
+        self.pairs.setdefault(name, []).append((a, b))
+
+    def mean_ms(self, name):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs[name]]))
+
+    def count(self, name):
+        return len(self.pairs.get(name, []))
+
+
+def bf16_dev(torch, bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+# ---------------------------------------------------------------- linear fwd + bwd (the step)
+def bench_linear(torch, mx, synth, dev, steps, warmup, seed=3):
+    cfg = synth.llama_config()
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    x = bf16_dev(torch, cfg["x"], dev)
+    w = bf16_dev(torch, cfg["w"], dev)
+    dy = bf16_dev(torch, cfg["dy"], dev)
+    del cfg
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
+    f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
+    y, dx, dw = f32(M, N), f32(M, K), f32(N, K)
+    xq, wq = (u8(M, K // 2), u8(M, K // 32)), (u8(N, K // 2), u8(N, K // 32))
+    q3, q5 = (u8(M, N // 2), u8(M, N // 32)), (u8(N, M // 2), u8(N, M // 32))
+    q4, q6 = (u8(K, N // 2), u8(K, N // 32)), (u8(K, M // 2), u8(K, M // 32))
+    st = torch.cuda.current_stream()
+    T = Timer(torch, st)
+    BF = mx.MX_BF16
+
+    def step(timer):
+        timer.run("quant_x", lambda: mx.mx_quantize(x, BF, M, K, mx.MX_ROW, mx.MX_RNE, 0, 0, 0, *xq, st))
+        timer.run("quant_w", lambda: mx.mx_quantize(w, BF, N, K, mx.MX_ROW, mx.MX_RNE, 0, 0, 0, *wq, st))
+        timer.run("gemm", lambda: mx.mx_gemm(*xq, *wq, M, N, K, 1.0, y, N, st))
+        timer.run("dual_dy", lambda: mx.mx_quantize_dual(dy, BF, M, N, mx.MX_SR, seed + 3, seed + 5,
+                                                        *q3, *q5, st))
+        timer.run("requant_w", lambda: mx.mx_requantize(*wq, N, K, mx.MX_SR, seed + 4, *q4, st))
+        timer.run("requant_x", lambda: mx.mx_requantize(*xq, M, K, mx.MX_SR, seed + 6, *q6, st))
+        timer.run("gemm", lambda: mx.mx_gemm(*q3, *q4, M, K, N, 1.0, dx, K, st))
+        timer.run("gemm", lambda: mx.mx_gemm(*q5, *q6, N, K, M, 1.0, dw, K, st))
+
+    warm = Timer(torch, st)
+    for _ in range(warmup):
+        step(warm)
+    torch.cuda.synchronize()
+    # the composed step equals the library's own linear entry points, bit for bit
+    y2, xq2, wq2 = mx.linear_fwd(x, w)
+    dx2, dw2 = mx.linear_bwd(dy, xq2, wq2, M, N, K, seed)
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for a, b in ((y, y2), (dx, dx2), (dw, dw2)))
+    del y2, xq2, wq2, dx2, dw2
+    torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(st)
+    for _ in range(steps):
+        step(T)
+    end.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / steps
+    flops = 6.0 * M * N * K
+    kern = {k: T.mean_ms(k) for k in T.pairs}
+    gemm_ms = kern["gemm"]
+    gemm_tf = 2.0 * M * N * K / (gemm_ms * 1e-3) / 1e12
+    bytes_q = {
+        "quant_x": M * K * (2 + 0.53125), "quant_w": N * K * (2 + 0.53125),
+        "dual_dy": M * N * (2 + 2 * 0.53125), "requant_w": N * K * 2 * 0.53125,
+        "requant_x": M * K * 2 * 0.53125,
+    }
+    quant = {k: {"us": kern[k] * 1e3, "GBps": bytes_q[k] / (kern[k] * 1e-3) / 1e9,
+                 "frac_hbm": bytes_q[k] / (kern[k] * 1e-3) / 1e9 / PEAK_HBM_GBPS} for k in bytes_q}
+    return {
+        "M": M, "N": N, "K": K, "ms_per_step": ms_step, "wall_s": wall,
+        "tflops": flops / (ms_step * 1e-3) / 1e12, "gemm_ms": gemm_ms, "gemm_tflops": gemm_tf,
+        "gemm_launches": T.count("gemm"), "kernels_us": {k: v * 1e3 for k, v in kern.items()},
+        "quantizers": quant, "matches_linear_entry_points": bool(same),
+    }
+
+
+# ---------------------------------------------------------------- quantizer sweep
+def bench_sweep(torch, mx, synth, dev, iters=20):
+    cfg = synth.sweep_config()
+    rows, cols, mask = cfg["rows"], cfg["cols"], cfg["sign_mask"]
+    # 4 input buffers (4 x 134 MB > the 256 MB Infinity Cache) used in rotation
+    xs = [bf16_dev(torch, cfg["x"], dev) for _ in range(4)]
+    del cfg
+    n = rows * cols
+    st = torch.cuda.current_stream()
+    out = {}
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
+    for axis, an in ((mx.MX_ROW, "row"), (mx.MX_COL, "col")):
+        outer, inner = (rows, cols) if axis == mx.MX_ROW else (cols, rows)
+        c, s = u8(outer, inner // 2), u8(outer, inner // 32)
+        for rnd, rn in ((mx.MX_RNE, "rne"), (mx.MX_SR, "sr")):
+            for had in (0, 1):
+                T = Timer(torch, st)
+                for i in range(iters + 3):
+                    fn = lambda: mx.mx_quantize(xs[i % 4], mx.MX_BF16, rows, cols, axis, rnd, 2, had,
+                                                mask, c, s, st)
+                    (T.run("q", fn) if i >= 3 else fn())
+                torch.cuda.synchronize()
+                ms = T.mean_ms("q")
+                gbps = n * 2.53125 / (ms * 1e-3) / 1e9
+                out[f"{an}_{rn}{'_had' if had else ''}"] = {"us": ms * 1e3, "GBps": gbps,
+                                                             "frac_hbm": gbps / PEAK_HBM_GBPS}
+    # double quantization and the fused dual quantizer on the same tensor
+    c, s = mx.quantize(xs[0])
+    co, so = u8(cols, rows // 2), u8(cols, rows // 32)
+    T = Timer(torch, st)
+    for i in range(iters):
+        T.run("r", lambda: mx.mx_requantize(c, s, rows, cols, mx.MX_SR, 2, co, so, st))
+    cr, sr_ = u8(rows, cols // 2), u8(rows, cols // 32)
+    for i in range(iters):
+        T.run("d", lambda: mx.mx_quantize_dual(xs[i % 4], mx.MX_BF16, rows, cols, mx.MX_SR, 5, 3,
+                                               cr, sr_, co, so, st))
+    torch.cuda.synchronize()
+    for key, name, bpe in (("r", "requant_sr", 1.0625), ("d", "dual_sr", 3.0625)):
+        ms = T.mean_ms(key)
+        gbps = n * bpe / (ms * 1e-3) / 1e9
+        out[name] = {"us": ms * 1e3, "GBps": gbps, "frac_hbm": gbps / PEAK_HBM_GBPS}
+    return out
+
+
+# ---------------------------------------------------------------- MoE + de-oscillation
+def bench_moe(torch, mx, synth, dev, iters=10, deosc_steps=20):
+    cfg = synth.moe_config()
+    E, H, F, offs = cfg["E"], cfg["hidden"], cfg["ffn"], cfg["offs"]
+    w = torch.from_numpy(cfg["w_master"]).to(dev)
+    x_up = bf16_dev(torch, cfg["x_up"], dev)
+    x_dn = bf16_dev(torch, cfg["x_down"], dev)
+    del cfg
+    rows, cols = w.shape
+    st = torch.cuda.current_stream()
+    wq = mx.quantize(w)
+    xq_up, xq_dn = mx.quantize(x_up), mx.quantize(x_dn)
+    c_up = torch.empty((int(offs[-1]), F), dtype=torch.float32, device=dev)
+    c_dn = torch.empty((int(offs[-1]), H), dtype=torch.float32, device=dev)
+    T = Timer(torch, st)
+    for i in range(iters + 2):
+        f_up = lambda: mx.mx_gemm_grouped(*xq_up, wq[0][:E * F], wq[1][:E * F], offs, E, F, H, 1.0, c_up, st)
+        f_dn = lambda: mx.mx_gemm_grouped(*xq_dn, wq[0][E * F:], wq[1][E * F:], offs, E, H, H, 1.0, c_dn, st)
+        if i >= 2:
+            T.run("up", f_up)
+            T.run("down", f_dn)
+        else:
+            f_up()
+            f_dn()
+    torch.cuda.synchronize()
+    R = int(offs[-1])
+    res = {}
+    for key, n_out in (("up", F), ("down", H)):
+        ms = T.mean_ms(key)
+        res[f"grouped_{key}"] = {"us": ms * 1e3,
+                                 "TFLOPs": 2.0 * R * n_out * H / (ms * 1e-3) / 1e12,
+                                 "frac_fp4_peak": 2.0 * R * n_out * H / (ms * 1e-3) / 1e12 / PEAK_FP4_TFLOPS}
+    del c_up, c_dn, xq_up, xq_dn, x_up, x_dn, wq
+    # de-oscillation: 796M fp32 master weights, synthetic optimizer step between passes
+    wp, dw_, dq_ = (torch.empty_like(w) for _ in range(3))
+    flags = torch.empty(w.shape, dtype=torch.uint8, device=dev)
+    mx.mx_deosc_init(w, rows, cols, wp, dw_, dq_, st)
+    T = Timer(torch, st)
+    for t in range(1, deosc_steps + 1):
+        mx.mx_synth_step(w, rows * cols, 4, t, st)
+        end = t == deosc_steps
+        T.run("end" if end else "step",
+              lambda: mx.mx_deosc_step(w, rows, cols, wp, dw_, dq_, end, 4.0, flags, st))
+    torch.cuda.synchronize()
+    n = rows * cols
+    ms = T.mean_ms("step")
+    res["deosc_step"] = {"us": ms * 1e3, "GBps": 28.0 * n / (ms * 1e-3) / 1e9,
+                         "frac_hbm": 28.0 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    ms_end = T.mean_ms("end")
+    res["deosc_window_end"] = {"us": ms_end * 1e3, "GBps": 33.0 * n / (ms_end * 1e-3) / 1e9}
+    return res
+
+
+# ---------------------------------------------------------------- CPU oracle baseline
+def cpu_baseline(synth):
+    """The oracle's linear fwd + bwd on a bounded slice of the same workload
+    (first 512 tokens, first 1024 output features, full K = 4096), one core."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+
+    cfg = synth.llama_config()
+    Ms, Ns, K = 512, 1024, cfg["K"]
+    x = O.bf16_bits_to_f32(cfg["x"][:Ms])
+    w = O.bf16_bits_to_f32(cfg["w"][:Ns])
+    dy = O.bf16_bits_to_f32(cfg["dy"][:Ms, :Ns])
+    del cfg
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        _, xq, wq = O.linear_fwd(x, w)
+        O.linear_bwd(dy, xq, wq, Ms, Ns, K, 3)
+        dt = time.perf_counter() - t0
+    flops = 6.0 * Ms * Ns * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"linear fwd+bwd on X[:{Ms}], W[:{Ns}], dY[:{Ms},:{Ns}] (K={K}) of the "
+                      f"Llama up-projection workload, float64 NumPy, 1 thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: this build has no multi-GPU path "
+              "(the sharding plan is described in the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from mxfp4_microscaling_quantization_amd import mx, synth
+
+    mx.lib()
+    dev = torch.device("cuda:0")
+    parts = {}
+    lin = None
+    if args.only in (None, "linear"):
+        log("linear fwd+bwd (Llama-3-8B up-projection)")
+        lin = bench_linear(torch, mx, synth, dev, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+    if not args.no_parts and args.only in (None, "sweep"):
+        log("quantizer sweep 8192x8192 bf16")
+        parts["quantizer_sweep_8192sq_bf16"] = bench_sweep(torch, mx, synth, dev)
+        torch.cuda.empty_cache()
+    if not args.no_parts and args.only in (None, "moe", "deosc"):
+        log("MoE grouped GEMM + de-oscillation")
+        parts["moe_32x2880"] = bench_moe(torch, mx, synth, dev)
+        torch.cuda.empty_cache()
+    cpu = None
+    if not args.no_cpu_baseline and args.only in (None, "linear"):
+        log("CPU oracle baseline")
+        cpu = cpu_baseline(synth)
+    if lin is None:
+        print(json.dumps({"parts": parts}))
+        return
+    parts["linear_kernels"] = {"kernels_us": lin["kernels_us"], "quantizers": lin["quantizers"],
+                               "gemm_launches_timed": lin["gemm_launches"],
+                               "matches_linear_entry_points": lin["matches_linear_entry_points"]}
+    ach = lin["gemm_tflops"]
+    line = {
+        "metric": METRIC,
+        "value": round(lin["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(lin["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": "llama3-8b-mlp-up-proj-linear-fwd-bwd", "M": lin["M"],
+                   "N": lin["N"], "K": lin["K"], "input_dtype": "bf16",
+                   "parallelism": "single-gpu"},
+        "roofline": {"kernel": "k_gemm_mx (MXFP4 GEMM, 2MNK per launch)", "bound": "mfma",
+                     "achieved": round(ach, 2), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_FP4_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "quantize_GBps": {k: round(v["GBps"], 1) for k, v in
+                          parts.get("quantizer_sweep_8192sq_bf16", {}).items()},
+        "parts": parts,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,221 @@
+/*
+ * mx.h -- C ABI of the MXFP4 (OCP Microscaling) training hot path for AMD
+ * MI355X (gfx950): block quantizer, MXFP4 GEMMs, quantized linear layer and
+ * the post-step weight de-oscillation pass.
+ *
+ * The operations follow these pages:
+ *  [TJ]   "Oscillation-Reduced MXFP4 Training for Vision Transformers"
+ *         (rebuttal, Question 2: Y = Q_D(X) Q_D(W^T), the STE weight gradient,
+ *         1x32 / 32x1 group shapes and the double quantization Q_S(Q_D(X))).
+ *  [ALTO] "ALTO MXFP4 training -- Weight de-oscillation -- What does it mean?"
+ *         (Jargon: MXFP4, E2M1, Bin, RHT, Stochastic rounding; the ratio
+ *         paragraph: window of 200 steps, d_w, d_Q, threshold 4.0, snap to
+ *         the current bin centre, post-step hook).
+ *  [OAS]  "Unveiling the Potential of Quantization with MXFP4" (abstract:
+ *         power-of-two block scale).
+ *  [MRG]  "Microscaling FP4 Quantization: MR-GPTQ ..." (section "FP4
+ *         Quantization with Micro-Rotated GPTQ Algorithm": block-wise Hadamard).
+ * Conventions the pages leave open follow the OCP MX v1.0 specification
+ * (E2M1 values {0, .5, 1, 1.5, 2, 3, 4, 6}; shared exponent
+ * floor(log2 amax) - 2 stored as an E8M0 byte with bias 127; values above 6
+ * saturate to 6).
+ *
+ * Data layout
+ *  - A "packed MXFP4 matrix" with B-element blocks along its last axis is two
+ *    dense row-major arrays: codes [outer][inner/2] (element 2j in the low
+ *    nibble of byte j, bit 3 = sign, bits 0-2 = index of the magnitude) and
+ *    scales [outer][inner/32] (E8M0: value 2^(byte-127), 0xFF = NaN).
+ *  - MX_ROW quantizes 1x32 blocks along the columns of a [rows, cols] input:
+ *    codes [rows][cols/2], scales [rows][cols/32].
+ *  - MX_COL quantizes 32x1 blocks along the rows and stores the result
+ *    transposed: codes [cols][rows/2], scales [cols][rows/32].  So every GEMM
+ *    operand is contiguous along its contraction axis.
+ *  - Stochastic rounding of the element at logical row-major index idx of the
+ *    input rounds up iff r24 < floor(t * 2^24), with t in [0, 1) the relative
+ *    distance to the lower neighbour and r24 the top 24 bits of output idx+1 of
+ *    SplitMix64 started from `seed` (Steele, Lea & Flood, OOPSLA 2014).  The
+ *    result does not depend on tiling or launch shape.
+ *
+ * Ownership and execution
+ *  - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *    `offs` of mx_gemm_grouped (host).  The library never allocates, frees or
+ *    synchronizes; it keeps no state between calls, so every entry point is
+ *    reentrant.  Work is enqueued on `stream` (a hipStream_t; NULL = default
+ *    stream) and the call returns before it runs.
+ *  - Input and output buffers must not overlap unless stated.
+ *
+ * Errors
+ *  - Every entry point returns an mx_status.  Arguments are validated before
+ *    any launch; on a validation error nothing is written and nothing is
+ *    enqueued.  MX_ERR_HIP reports a failed launch (the stream may then hold
+ *    earlier work of the same call).
+ *  - Base pointers of device arrays must be 16-byte aligned (MX_ERR_ALIGN).
+ */
+#ifndef MX355_MX_H
+#define MX355_MX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MX_OK = 0,
+  MX_ERR_NULL = 1,      /* a required pointer is NULL */
+  MX_ERR_SHAPE = 2,     /* a size is negative, a block axis is not a multiple of 32, ... */
+  MX_ERR_ALIGN = 3,     /* a device pointer is not 16-byte aligned */
+  MX_ERR_ENUM = 4,      /* dtype / axis / rounding / flag out of range */
+  MX_ERR_WORKSPACE = 5, /* workspace NULL or smaller than required */
+  MX_ERR_HIP = 6        /* the HIP runtime rejected a launch */
+} mx_status;
+
+enum { MX_F32 = 0, MX_BF16 = 1 };   /* element types of unquantized tensors */
+enum { MX_ROW = 0, MX_COL = 1 };    /* 1x32 blocks along cols / 32x1 blocks along rows */
+enum { MX_RNE = 0, MX_SR = 1 };     /* Q_D: nearest, ties to even / Q_S: stochastic */
+
+/* Largest number of groups mx_gemm_grouped accepts. */
+#define MX_MAX_GROUPS 128
+
+/* Human-readable name of a status code (static string). */
+const char* mx_status_string(int status);
+
+/* ------------------------------------------------------------------ quantizer
+ * mx_quantize: MXFP4-quantize a [rows, cols] row-major tensor x (dtype MX_F32
+ * or MX_BF16) -- [ALTO] Jargon "MXFP4", "E2M1", "Bin", "Stochastic rounding";
+ * [TJ] Question 2 for the two group shapes.
+ *  For each block of 32 values v (after the optional rotation):
+ *    e = clamp(floor(log2 max|v|) - 2, -127, 127) (e = -127 for an all-zero
+ *    block), scale byte = e + 127; a_i = |v_i| 2^-e; the magnitude is the
+ *    nearest of {0,.5,1,1.5,2,3,4,6} with ties to the even code (MX_RNE) or
+ *    one of the two neighbours chosen by stochastic rounding (MX_SR); a_i > 6
+ *    gives 6; the sign bit is the sign bit of v_i (so -0 codes as 0x8).
+ *    A block holding NaN or Inf gets scale byte 0xFF and zero codes.
+ *  axis MX_ROW: cols % 32 == 0; writes codes [rows][cols/2], scales [rows][cols/32].
+ *  axis MX_COL: rows % 32 == 0 and cols % 8 == 0; writes codes [cols][rows/2],
+ *       scales [cols][rows/32] (transposed).
+ *  hadamard != 0: each block is first rotated, v = H32 (s . x), H32 the
+ *    unnormalised Sylvester Hadamard matrix (H H^T = 32 I) and s_j = -1 where
+ *    bit j of sign_mask is set -- [ALTO] Jargon "Randomized Hadamard transform",
+ *    [MRG] block-wise Hadamard.  Computed in float32 with butterfly stages
+ *    h = 1, 2, 4, 8, 16.
+ *  seed is used only by MX_SR.  rows or cols == 0 is a no-op.
+ */
+int mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int axis, int round,
+                uint64_t seed, int hadamard, uint32_t sign_mask,
+                uint8_t* codes, uint8_t* scales, void* stream);
+
+/* mx_quantize_dual: one read of a [rows, cols] tensor, two quantizations:
+ * a MX_ROW one (codes_row [rows][cols/2], scales_row [rows][cols/32], seed
+ * seed_row) and a MX_COL one (codes_col [cols][rows/2], scales_col
+ * [cols][rows/32], seed seed_col), both with rounding `round`.  Equal,
+ * bit for bit, to two mx_quantize calls.  This is the gradient dY of the
+ * backward pass, which both backward GEMMs consume in different group
+ * shapes ([TJ] Question 2 (2)).  rows % 32 == 0, cols % 32 == 0. */
+int mx_quantize_dual(const void* x, int dtype, int64_t rows, int64_t cols, int round,
+                     uint64_t seed_row, uint64_t seed_col,
+                     uint8_t* codes_row, uint8_t* scales_row,
+                     uint8_t* codes_col, uint8_t* scales_col, void* stream);
+
+/* mx_requantize: double quantization Q(Q_D(X)) -- [TJ] Question 2 (2), the
+ * double-quantized operand Q_S^(6)(Q_D^(1)(X)).  Input: a packed MX_ROW matrix
+ * of logical shape [rows, cols] (codes_in [rows][cols/2], scales_in
+ * [rows][cols/32]).  Its exact values are quantized again with 32x1 blocks
+ * (MX_COL, output transposed: codes_out [cols][rows/2], scales_out
+ * [cols][rows/32]) with rounding `round` and `seed`; the stochastic-rounding
+ * index is the logical row-major index in [rows, cols].  Equal to
+ * mx_quantize(dequantized input, MX_COL, ...).  rows % 32 == 0, cols % 32 == 0. */
+int mx_requantize(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows, int64_t cols,
+                  int round, uint64_t seed, uint8_t* codes_out, uint8_t* scales_out, void* stream);
+
+/* mx_dequantize: exact values of a packed matrix of logical shape [rows, cols]
+ * quantized along `axis` (the inverse layout of mx_quantize), written row-major
+ * [rows, cols] as float32 or bf16 (out_dtype).  value = sign * E2M1[code & 7]
+ * * 2^(byte - 127) (exact in both types), byte 0xFF gives NaN.  hadamard != 0
+ * undoes the rotation: x = s . (H32 y) 2^-5 per block in float32 (bf16 output
+ * then rounds to nearest even). */
+int mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                  int axis, int hadamard, uint32_t sign_mask, void* out, int out_dtype,
+                  void* stream);
+
+/* ------------------------------------------------------------------ GEMM
+ * mx_gemm: C[m][n] = alpha * sum_k deq(A)[m][k] * deq(B)[n][k]  -- the MXFP4
+ * matrix product of [TJ] Question 2 (1), (1x32) x (32x1) groups.
+ *  A: packed MX_ROW [M, K] (a_codes [M][K/2], a_scales [M][K/32]);
+ *  B: packed MX_ROW [N, K] (b_codes [N][K/2], b_scales [N][K/32]);
+ *  C: float32 row-major, leading dimension ldc >= N (ldc % 4 == 0), overwritten.
+ *  K % 32 == 0; M, N >= 0 (M or N == 0: no-op; K == 0: C = 0).
+ *  Products of FP4 values and E8M0 scales are exact; sums are float32 in an
+ *  unspecified order (error <= ~K/64 * 2^-24 * sum |a b|). */
+int mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+            const uint8_t* b_codes, const uint8_t* b_scales,
+            int64_t M, int64_t N, int64_t K, float alpha, float* c, int64_t ldc, void* stream);
+
+/* mx_gemm_grouped: per-group products for a mixture-of-experts layer ([ALTO]
+ * news paragraph: the MoE model trained in MXFP4).  offs is a HOST array of
+ * groups+1 non-decreasing row offsets with offs[0] == 0; rows
+ * offs[g] .. offs[g+1]-1 of A and C use B_g, the g-th [N, K] matrix of b
+ * (b_codes + g*N*K/2, b_scales + g*N*K/32).  C is [offs[groups]][N], ldc = N.
+ * 1 <= groups <= MX_MAX_GROUPS, K % 32 == 0, N % 4 == 0. */
+int mx_gemm_grouped(const uint8_t* a_codes, const uint8_t* a_scales,
+                    const uint8_t* b_codes, const uint8_t* b_scales,
+                    const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha,
+                    float* c, void* stream);
+
+/* ------------------------------------------------------------------ linear layer
+ * mx_linear_fwd: forward of the quantized linear layer, Y = Q_D(X) Q_D(W)^T
+ * ([TJ] Question 2 (1)); X [M, K], W [N, K] (nn.Linear layout), both `dtype`;
+ * Q_D is MX_ROW + MX_RNE along K.  Writes y [M][N] float32 and the packed
+ * operands kept for the backward pass: xq_codes [M][K/2], xq_scales [M][K/32],
+ * wq_codes [N][K/2], wq_scales [N][K/32].  M, N, K multiples of 32, N % 4 == 0. */
+int mx_linear_fwd(const void* x, const void* w, int dtype, int64_t M, int64_t N, int64_t K,
+                  float* y, uint8_t* xq_codes, uint8_t* xq_scales,
+                  uint8_t* wq_codes, uint8_t* wq_scales, void* stream);
+
+/* Bytes of device workspace mx_linear_bwd needs for these sizes. */
+size_t mx_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* mx_linear_bwd: backward of the quantized linear layer with straight-through
+ * gradients ([TJ] Question 2 (1) and (2)):
+ *   dX = Q_S^(3)(dY) . Q_S^(4)(Q_D(W))       contraction over N
+ *   dW = Q_S^(5)(dY)^T . Q_S^(6)(Q_D(X))     contraction over M
+ * Q^(3): dY 1x32 along N; Q^(5): dY 32x1 along M; Q^(4), Q^(6): double
+ * quantization of the saved forward operands with 32x1 blocks along N and M.
+ * Stochastic rounding; quantizer q uses seed + q.  dy [M][N] (`dtype`);
+ * the saved operands are mx_linear_fwd's outputs; writes dx [M][K] and
+ * dw [N][K] float32.  workspace: device buffer of at least
+ * mx_linear_bwd_workspace_size(M, N, K) bytes, 16-byte aligned.
+ * M, N, K multiples of 32, K % 4 == 0. */
+int mx_linear_bwd(const void* dy, int dtype, int64_t M, int64_t N, int64_t K,
+                  const uint8_t* xq_codes, const uint8_t* xq_scales,
+                  const uint8_t* wq_codes, const uint8_t* wq_scales,
+                  uint64_t seed, float* dx, float* dw,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ de-oscillation
+ * Weight de-oscillation as a post-optimizer-step pass ([ALTO] "How does ALTO
+ * detect and fix oscillating weights?" and the ratio paragraph).  w is the
+ * float32 master weight [rows, cols]; its bin value q(w) is the forward weight
+ * quantizer's output deq(Q_D(w)) with 1x32 RNE blocks along cols.  The state is
+ * three caller-owned float32 arrays of the same shape: w_prev (snapshot),
+ * d_w (master-weight path length) and d_q (quantized path length).
+ *
+ * mx_deosc_init: w_prev = w, d_w = d_q = 0. */
+int mx_deosc_init(const float* w, int64_t rows, int64_t cols,
+                  float* w_prev, float* d_w, float* d_q, void* stream);
+
+/* mx_deosc_step: call once after every optimizer step, in float32:
+ *   d_w += |w - w_prev|;  d_q += |q(w) - q(w_prev)|;  w_prev = w.
+ * If end_of_window != 0 (every P-th call, P = 200 on the page): flag =
+ * d_q > threshold * d_w (threshold 4.0 on the page); flagged elements are
+ * snapped, w = q(w); then w_prev = w and d_w = d_q = 0; flags (uint8 [rows][cols],
+ * required then, else ignored) receives 1 for flagged elements, 0 otherwise.
+ * cols % 32 == 0.  w is updated in place. */
+int mx_deosc_step(float* w, int64_t rows, int64_t cols, float* w_prev, float* d_w, float* d_q,
+                  int end_of_window, float threshold, uint8_t* flags, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MX355_MX_H */

@@ -1,0 +1,128 @@
+// Quantized linear layer: forward and backward compositions of the quantizer
+// and GEMM kernels ("Oscillation-Reduced MXFP4 Training for Vision
+// Transformers", rebuttal, Question 2):
+//   forward   Y  = Q_D^(1)(X) . Q_D^(2)(W)^T             (1x32 RNE along K)
+//   backward  dX = Q_S^(3)(dY) . Q_S^(4)(Q_D^(2)(W))     (contraction over N)
+//             dW = Q_S^(5)(dY)^T . Q_S^(6)(Q_D^(1)(X))   (contraction over M)
+// Q^(4) and Q^(6) are the double quantizations that give the 32x1 group shape
+// the backward products need; quantizer q draws its stochastic rounding from
+// seed + q.  All launches go to the caller's stream in order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mx_host.h"
+
+namespace mx {
+int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, int axis, int round,
+                  uint64_t seed, int had, uint32_t mask, uint8_t* codes, uint8_t* scales,
+                  hipStream_t st);
+int quantize_dual_impl(const void* x, int dtype, int64_t rows, int64_t cols, int round,
+                       uint64_t seed_row, uint64_t seed_col, uint8_t* codes_row,
+                       uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
+                       hipStream_t st);
+int requantize_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows, int64_t cols,
+                    int round, uint64_t seed, uint8_t* codes, uint8_t* scales, hipStream_t st);
+int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
+              const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha, float* c,
+              int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, hipStream_t st);
+
+static size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Workspace layout: four packed operands, each codes then scales, 256-byte aligned.
+struct BwdLayout {
+  size_t q3c, q3s, q4c, q4s, q5c, q5s, q6c, q6s, total;
+};
+
+static BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K) {
+  BwdLayout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round256(bytes);
+    return at;
+  };
+  L.q3c = take((size_t)M * N / 2);  L.q3s = take((size_t)M * N / 32);   // dY rows   [M][N]
+  L.q4c = take((size_t)K * N / 2);  L.q4s = take((size_t)K * N / 32);   // W^T blocks [K][N]
+  L.q5c = take((size_t)N * M / 2);  L.q5s = take((size_t)N * M / 32);   // dY^T      [N][M]
+  L.q6c = take((size_t)K * M / 2);  L.q6s = take((size_t)K * M / 32);   // X^T blocks [K][M]
+  L.total = o;
+  return L;
+}
+
+}  // namespace mx
+
+using namespace mx;
+
+extern "C" int mx_linear_fwd(const void* x, const void* w, int dtype, int64_t M, int64_t N,
+                             int64_t K, float* y, uint8_t* xq_codes, uint8_t* xq_scales,
+                             uint8_t* wq_codes, uint8_t* wq_scales, void* stream) {
+  MX_REQUIRE(dtype == MX_F32 || dtype == MX_BF16, MX_ERR_ENUM);
+  MX_REQUIRE(M >= 0 && N >= 0 && K >= 0, MX_ERR_SHAPE);
+  MX_REQUIRE(M % 32 == 0 && N % 32 == 0 && K % 32 == 0, MX_ERR_SHAPE);
+  if (M == 0 || N == 0 || K == 0) {
+    if (M > 0 && N > 0 && K == 0) MX_REQUIRE(y, MX_ERR_NULL);
+    if (M == 0 || N == 0) return MX_OK;
+  }
+  MX_REQUIRE(x && w && y && xq_codes && xq_scales && wq_codes && wq_scales, MX_ERR_NULL);
+  MX_REQUIRE(aligned16(x) && aligned16(w) && aligned16(y) && aligned16(xq_codes) &&
+                 aligned16(wq_codes), MX_ERR_ALIGN);
+  const hipStream_t st = as_stream(stream);
+  int s = quantize_impl(x, dtype, M, K, MX_ROW, MX_RNE, 0, 0, 0, xq_codes, xq_scales, st);
+  if (s != MX_OK) return s;
+  s = quantize_impl(w, dtype, N, K, MX_ROW, MX_RNE, 0, 0, 0, wq_codes, wq_scales, st);
+  if (s != MX_OK) return s;
+  const int64_t offs[2] = {0, M};
+  return gemm_impl(xq_codes, xq_scales, wq_codes, wq_scales, offs, 1, N, K, 1.0f, y, N, 0, 0, st);
+}
+
+extern "C" size_t mx_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return 0;
+  return bwd_layout(M, N, K).total;
+}
+
+extern "C" int mx_linear_bwd(const void* dy, int dtype, int64_t M, int64_t N, int64_t K,
+                             const uint8_t* xq_codes, const uint8_t* xq_scales,
+                             const uint8_t* wq_codes, const uint8_t* wq_scales, uint64_t seed,
+                             float* dx, float* dw, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  MX_REQUIRE(dtype == MX_F32 || dtype == MX_BF16, MX_ERR_ENUM);
+  MX_REQUIRE(M >= 0 && N >= 0 && K >= 0, MX_ERR_SHAPE);
+  MX_REQUIRE(M % 32 == 0 && N % 32 == 0 && K % 32 == 0, MX_ERR_SHAPE);
+  if (M == 0 || N == 0 || K == 0) return MX_OK;
+  MX_REQUIRE(dy && xq_codes && xq_scales && wq_codes && wq_scales && dx && dw, MX_ERR_NULL);
+  MX_REQUIRE(aligned16(dy) && aligned16(xq_codes) && aligned16(wq_codes) && aligned16(dx) &&
+                 aligned16(dw), MX_ERR_ALIGN);
+  const BwdLayout L = bwd_layout(M, N, K);
+  MX_REQUIRE(workspace && workspace_bytes >= L.total, MX_ERR_WORKSPACE);
+  MX_REQUIRE(aligned16(workspace), MX_ERR_ALIGN);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const hipStream_t st = as_stream(stream);
+
+  int s = quantize_dual_impl(dy, dtype, M, N, MX_SR, seed + 3, seed + 5, ws + L.q3c, ws + L.q3s,
+                             ws + L.q5c, ws + L.q5s, st);
+  if (s != MX_OK) return s;
+  s = requantize_impl(wq_codes, wq_scales, N, K, MX_SR, seed + 4, ws + L.q4c, ws + L.q4s, st);
+  if (s != MX_OK) return s;
+  s = requantize_impl(xq_codes, xq_scales, M, K, MX_SR, seed + 6, ws + L.q6c, ws + L.q6s, st);
+  if (s != MX_OK) return s;
+  const int64_t offs_dx[2] = {0, M};
+  s = gemm_impl(ws + L.q3c, ws + L.q3s, ws + L.q4c, ws + L.q4s, offs_dx, 1, K, N, 1.0f, dx, K, 0,
+                0, st);
+  if (s != MX_OK) return s;
+  const int64_t offs_dw[2] = {0, N};
+  return gemm_impl(ws + L.q5c, ws + L.q5s, ws + L.q6c, ws + L.q6s, offs_dw, 1, K, M, 1.0f, dw, K,
+                   0, 0, st);
+}
+
+extern "C" const char* mx_status_string(int status) {
+  switch (status) {
+    case MX_OK: return "MX_OK";
+    case MX_ERR_NULL: return "MX_ERR_NULL: a required pointer is NULL";
+    case MX_ERR_SHAPE: return "MX_ERR_SHAPE: unsupported or inconsistent sizes";
+    case MX_ERR_ALIGN: return "MX_ERR_ALIGN: a device pointer is not 16-byte aligned";
+    case MX_ERR_ENUM: return "MX_ERR_ENUM: an enum or flag argument is out of range";
+    case MX_ERR_WORKSPACE: return "MX_ERR_WORKSPACE: workspace missing or too small";
+    case MX_ERR_HIP: return "MX_ERR_HIP: the HIP runtime rejected a launch";
+    default: return "unknown mx_status";
+  }
+}

@@ -1,0 +1,28 @@
+// Host-side helpers shared by the entry points: status codes and checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mx.h"
+
+namespace mx {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MX_OK : MX_ERR_HIP;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t hmin(int64_t a, int64_t b) { return a < b ? a : b; }
+
+}  // namespace mx
+
+#define MX_REQUIRE(cond, status) \
+  do {                           \
+    if (!(cond)) return (status); \
+  } while (0)

@@ -1,0 +1,233 @@
+"""ctypes binding of libmx355.so (include/mx.h, include/mx_synth.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP library.
+The functions named like the C entry points take torch tensors (device memory)
+and the current torch stream; they raise MxError on a non-zero status.  The
+library is loaded on first use and a missing build raises immediately -- there
+is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+
+import torch
+
+MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_ENUM, MX_ERR_WORKSPACE, MX_ERR_HIP = range(7)
+MX_F32, MX_BF16 = 0, 1
+MX_ROW, MX_COL = 0, 1
+MX_RNE, MX_SR = 0, 1
+MX_MAX_GROUPS = 128
+
+LIB_PATH = Path(__file__).resolve().parent / "libmx355.so"
+
+_c_void_p, _i64, _u64, _u32, _i32, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
+                                                  ctypes.c_uint32, ctypes.c_int, ctypes.c_float,
+                                                  ctypes.c_size_t)
+_P = _c_void_p
+SIGNATURES = {
+    "mx_status_string": ([_i32], ctypes.c_char_p),
+    "mx_quantize": ([_P, _i32, _i64, _i64, _i32, _i32, _u64, _i32, _u32, _P, _P, _P], _i32),
+    "mx_quantize_dual": ([_P, _i32, _i64, _i64, _i32, _u64, _u64, _P, _P, _P, _P, _P], _i32),
+    "mx_requantize": ([_P, _P, _i64, _i64, _i32, _u64, _P, _P, _P], _i32),
+    "mx_dequantize": ([_P, _P, _i64, _i64, _i32, _i32, _u32, _P, _i32, _P], _i32),
+    "mx_gemm": ([_P, _P, _P, _P, _i64, _i64, _i64, _f32, _P, _i64, _P], _i32),
+    "mx_gemm_grouped": ([_P, _P, _P, _P, _P, _i64, _i64, _i64, _f32, _P, _P], _i32),
+    "mx_linear_fwd": ([_P, _P, _i32, _i64, _i64, _i64, _P, _P, _P, _P, _P, _P], _i32),
+    "mx_linear_bwd_workspace_size": ([_i64, _i64, _i64], _sz),
+    "mx_linear_bwd": ([_P, _i32, _i64, _i64, _i64, _P, _P, _P, _P, _u64, _P, _P, _P, _sz, _P], _i32),
+    "mx_deosc_init": ([_P, _i64, _i64, _P, _P, _P, _P], _i32),
+    "mx_deosc_step": ([_P, _i64, _i64, _P, _P, _P, _i32, _f32, _P, _P], _i32),
+    "mx_synth_step": ([_P, _i64, _u64, _i64, _P], _i32),
+}
+
+_lib = None
+
+
+class MxError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} -> {status_string(status)}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mxfp4_microscaling_quantization_amd.build`")
+        handle = ctypes.CDLL(str(LIB_PATH))
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().mx_status_string(int(status)).decode()
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(name: str, status: int) -> None:
+    if status != MX_OK:
+        raise MxError(name, status)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MX_F32
+    if t.dtype == torch.bfloat16:
+        return MX_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# ------------------------------------------------------------------ C-named entry points
+def mx_quantize(x, dtype, rows, cols, axis, round, seed, hadamard, sign_mask, codes, scales,
+                stream=None):
+    _check("mx_quantize", lib().mx_quantize(_ptr(x), dtype, rows, cols, axis, round, seed,
+                                            hadamard, sign_mask, _ptr(codes), _ptr(scales),
+                                            _stream(stream)))
+
+
+def mx_quantize_dual(x, dtype, rows, cols, round, seed_row, seed_col, codes_row, scales_row,
+                     codes_col, scales_col, stream=None):
+    _check("mx_quantize_dual", lib().mx_quantize_dual(
+        _ptr(x), dtype, rows, cols, round, seed_row, seed_col, _ptr(codes_row), _ptr(scales_row),
+        _ptr(codes_col), _ptr(scales_col), _stream(stream)))
+
+
+def mx_requantize(codes_in, scales_in, rows, cols, round, seed, codes_out, scales_out, stream=None):
+    _check("mx_requantize", lib().mx_requantize(_ptr(codes_in), _ptr(scales_in), rows, cols, round,
+                                                seed, _ptr(codes_out), _ptr(scales_out),
+                                                _stream(stream)))
+
+
+def mx_dequantize(codes, scales, rows, cols, axis, hadamard, sign_mask, out, out_dtype,
+                  stream=None):
+    _check("mx_dequantize", lib().mx_dequantize(_ptr(codes), _ptr(scales), rows, cols, axis,
+                                                hadamard, sign_mask, _ptr(out), out_dtype,
+                                                _stream(stream)))
+
+
+def mx_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, alpha, c, ldc, stream=None):
+    _check("mx_gemm", lib().mx_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales),
+                                    M, N, K, alpha, _ptr(c), ldc, _stream(stream)))
+
+
+def mx_gemm_grouped(a_codes, a_scales, b_codes, b_scales, offs, groups, N, K, alpha, c,
+                    stream=None):
+    arr = (ctypes.c_int64 * len(offs))(*[int(o) for o in offs])
+    _check("mx_gemm_grouped", lib().mx_gemm_grouped(
+        _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), ctypes.addressof(arr),
+        groups, N, K, alpha, _ptr(c), _stream(stream)))
+
+
+def mx_linear_fwd(x, w, dtype, M, N, K, y, xq_codes, xq_scales, wq_codes, wq_scales, stream=None):
+    _check("mx_linear_fwd", lib().mx_linear_fwd(_ptr(x), _ptr(w), dtype, M, N, K, _ptr(y),
+                                                _ptr(xq_codes), _ptr(xq_scales), _ptr(wq_codes),
+                                                _ptr(wq_scales), _stream(stream)))
+
+
+def mx_linear_bwd_workspace_size(M, N, K) -> int:
+    return int(lib().mx_linear_bwd_workspace_size(M, N, K))
+
+
+def mx_linear_bwd(dy, dtype, M, N, K, xq_codes, xq_scales, wq_codes, wq_scales, seed, dx, dw,
+                  workspace, workspace_bytes, stream=None):
+    _check("mx_linear_bwd", lib().mx_linear_bwd(
+        _ptr(dy), dtype, M, N, K, _ptr(xq_codes), _ptr(xq_scales), _ptr(wq_codes),
+        _ptr(wq_scales), seed, _ptr(dx), _ptr(dw), _ptr(workspace), workspace_bytes,
+        _stream(stream)))
+
+
+def mx_deosc_init(w, rows, cols, w_prev, d_w, d_q, stream=None):
+    _check("mx_deosc_init", lib().mx_deosc_init(_ptr(w), rows, cols, _ptr(w_prev), _ptr(d_w),
+                                                _ptr(d_q), _stream(stream)))
+
+
+def mx_deosc_step(w, rows, cols, w_prev, d_w, d_q, end_of_window, threshold, flags, stream=None):
+    _check("mx_deosc_step", lib().mx_deosc_step(_ptr(w), rows, cols, _ptr(w_prev), _ptr(d_w),
+                                                _ptr(d_q), int(end_of_window), threshold,
+                                                _ptr(flags), _stream(stream)))
+
+
+def mx_synth_step(w, n, seed, step, stream=None):
+    _check("mx_synth_step", lib().mx_synth_step(_ptr(w), n, seed, step, _stream(stream)))
+
+
+# ------------------------------------------------------------------ tensor conveniences
+def _u8(shape, device):
+    return torch.empty(shape, dtype=torch.uint8, device=device)
+
+
+def quantize(x: torch.Tensor, axis=MX_ROW, round=MX_RNE, seed=0, hadamard=False, sign_mask=0,
+             stream=None):
+    """Packed (codes, scales) of a 2-D float32/bf16 device tensor."""
+    rows, cols = x.shape
+    outer, inner = (rows, cols) if axis == MX_ROW else (cols, rows)
+    codes = _u8((outer, inner // 2), x.device)
+    scales = _u8((outer, inner // 32), x.device)
+    mx_quantize(x, dtype_code(x), rows, cols, axis, round, seed, int(bool(hadamard)), sign_mask,
+                codes, scales, stream)
+    return codes, scales
+
+
+def dequantize(codes, scales, rows, cols, axis=MX_ROW, hadamard=False, sign_mask=0,
+               out_dtype=torch.float32, stream=None):
+    out = torch.empty((rows, cols), dtype=out_dtype, device=codes.device)
+    mx_dequantize(codes, scales, rows, cols, axis, int(bool(hadamard)), sign_mask, out,
+                  dtype_code(out), stream)
+    return out
+
+
+def requantize(codes, scales, rows, cols, round=MX_SR, seed=0, stream=None):
+    co = _u8((cols, rows // 2), codes.device)
+    so = _u8((cols, rows // 32), codes.device)
+    mx_requantize(codes, scales, rows, cols, round, seed, co, so, stream)
+    return co, so
+
+
+def gemm(a, b, M, N, K, alpha=1.0, stream=None):
+    c = torch.empty((M, N), dtype=torch.float32, device=a[0].device)
+    mx_gemm(a[0], a[1], b[0], b[1], M, N, K, alpha, c, N, stream)
+    return c
+
+
+def linear_fwd(x: torch.Tensor, w: torch.Tensor, stream=None):
+    M, K = x.shape
+    N = w.shape[0]
+    y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    xq = (_u8((M, K // 2), x.device), _u8((M, K // 32), x.device))
+    wq = (_u8((N, K // 2), x.device), _u8((N, K // 32), x.device))
+    mx_linear_fwd(x, w, dtype_code(x), M, N, K, y, xq[0], xq[1], wq[0], wq[1], stream)
+    return y, xq, wq
+
+
+def linear_bwd(dy: torch.Tensor, xq, wq, M, N, K, seed, workspace=None, stream=None):
+    need = mx_linear_bwd_workspace_size(M, N, K)
+    if workspace is None:
+        workspace = _u8((need,), dy.device)
+    dx = torch.empty((M, K), dtype=torch.float32, device=dy.device)
+    dw = torch.empty((N, K), dtype=torch.float32, device=dy.device)
+    mx_linear_bwd(dy, dtype_code(dy), M, N, K, xq[0], xq[1], wq[0], wq[1], seed, dx, dw,
+                  workspace, workspace.numel(), stream)
+    return dx, dw

@@ -1,0 +1,222 @@
+"""GPU parity of the quantized linear layer (fwd + bwd) and the de-oscillation pass."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mxfp4_microscaling_quantization_amd import mx, synth
+from tests.gpu_util import (DEV, assert_bytes_equal, assert_gemm_close, host, oracle_input,
+                            to_dev_f32, to_dev_u8, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def check_linear(cfg, dtype, seed, sample_rows=None, rng=None):
+    x, w, dy = cfg["x"], cfg["w"], cfg["dy"]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    xf, wf, dyf = (oracle_input(a, dtype) for a in (x, w, dy))
+    dx_, dw_, dy_ = upload(x, dtype), upload(w, dtype), upload(dy, dtype)
+    y, xq, wq = mx.linear_fwd(dx_, dw_)
+    gx, gw = mx.linear_bwd(dy_, xq, wq, M, N, K, seed)
+    # saved forward operands: bit-exact
+    oxq = O.quantize(xf, O.ROW, O.RNE)
+    owq = O.quantize(wf, O.ROW, O.RNE)
+    assert_bytes_equal(host(xq[0]), oxq[0], "Q_D(X) codes")
+    assert_bytes_equal(host(xq[1]), oxq[1], "Q_D(X) scales")
+    assert_bytes_equal(host(wq[0]), owq[0], "Q_D(W) codes")
+    assert_bytes_equal(host(wq[1]), owq[1], "Q_D(W) scales")
+    # backward operands through the public kernels (the same kernels mx_linear_bwd runs)
+    q4 = O.requantize(*owq, N, K, O.SR, seed + 4)
+    q6 = O.requantize(*oxq, M, K, O.SR, seed + 6)
+    g4 = mx.requantize(wq[0], wq[1], N, K, mx.MX_SR, seed + 4)
+    g6 = mx.requantize(xq[0], xq[1], M, K, mx.MX_SR, seed + 6)
+    for got, want, what in zip(g4 + g6, q4 + q6, ["Q4 codes", "Q4 scales", "Q6 codes", "Q6 scales"]):
+        assert_bytes_equal(host(got), want, what)
+    rows = np.arange(M) if sample_rows is None else np.sort(rng.choice(M, sample_rows, replace=False))
+    nrows = np.arange(N) if sample_rows is None else np.sort(rng.choice(N, sample_rows, replace=False))
+    # Y rows
+    want_y = O.gemm(oxq[0][rows], oxq[1][rows], *owq, len(rows), N, K)
+    ab_y = O.gemm_abs(oxq[0][rows], oxq[1][rows], *owq, len(rows), N, K)
+    assert_gemm_close(host(y)[rows], want_y, ab_y, "Y")
+    # dX rows: Q3 = row SR of dY restricted to the sampled rows (indices stay global)
+    idx3 = O.block_indices(M, N, O.ROW)[rows]
+    c3, s3 = O.quantize_blocks(dyf[rows].reshape(len(rows), N // 32, 32), idx3, O.SR, seed + 3)
+    q3 = (O.pack_codes(c3.reshape(len(rows), N)), s3)
+    want_dx = O.gemm(*q3, *q4, len(rows), K, N)
+    ab_dx = O.gemm_abs(*q3, *q4, len(rows), K, N)
+    assert_gemm_close(host(gx)[rows], want_dx, ab_dx, "dX")
+    # dW rows: Q5 = column SR of dY for the sampled columns n
+    idx5 = O.block_indices(M, N, O.COL)[nrows]
+    c5, s5 = O.quantize_blocks(dyf.T[nrows].reshape(len(nrows), M // 32, 32), idx5, O.SR, seed + 5)
+    q5 = (O.pack_codes(c5.reshape(len(nrows), M)), s5)
+    want_dw = O.gemm(*q5, *q6, len(nrows), K, M)
+    ab_dw = O.gemm_abs(*q5, *q6, len(nrows), K, M)
+    assert_gemm_close(host(gw)[nrows], want_dw, ab_dw, "dW")
+
+
+def test_linear_small_f32():
+    rng = np.random.default_rng(0)
+    M, N, K = 96, 160, 224
+    cfg = {"x": rng.standard_normal((M, K)).astype(np.float32),
+           "w": (rng.standard_normal((N, K)) * 0.02).astype(np.float32),
+           "dy": (rng.standard_normal((M, N)) * 1e-3).astype(np.float32), "M": M, "N": N, "K": K}
+    check_linear(cfg, "f32", seed=11)
+
+
+def test_linear_deit_fc1_full():
+    """DeiT-S fc1, X [12608, 384], W [1536, 384], dY [12608, 1536] bf16: every output checked."""
+    check_linear(synth.deit_config(), "bf16", seed=1)
+
+
+@pytest.mark.slow
+def test_linear_llama_up_proj_sampled():
+    """Llama-3-8B up-projection, M=8192, K=4096, N=14336 bf16; quantized operands in full,
+    GEMM outputs on 48 sampled rows of Y, dX and dW."""
+    check_linear(synth.llama_config(), "bf16", seed=3, sample_rows=48, rng=np.random.default_rng(3))
+
+
+def test_moe_grouped_forward_sampled():
+    """32 experts, top-4 routing of 16384 tokens, hidden 2880, up 2880 -> 5760 and down
+    2880 -> 2880 on fp32 master weights quantized with Q_D; sampled rows per expert."""
+    cfg = synth.moe_config()
+    E, H, F = cfg["E"], cfg["hidden"], cfg["ffn"]
+    offs = cfg["offs"]
+    wm = cfg["w_master"]
+    w_dev = to_dev_f32(wm)
+    wq = mx.quantize(w_dev)                          # all expert weights, 1x32 RNE along K
+    rng = np.random.default_rng(4)
+    for name, xin, r0, n_out in (("up", cfg["x_up"], 0, F), ("down", cfg["x_down"], E * F, H)):
+        xq = mx.quantize(upload(xin, "bf16"))
+        wc = wq[0][r0:r0 + E * n_out]
+        ws = wq[1][r0:r0 + E * n_out]
+        c = torch.empty((offs[-1], n_out), dtype=torch.float32, device=DEV)
+        mx.mx_gemm_grouped(xq[0], xq[1], wc, ws, offs, E, n_out, H, 1.0, c)
+        got = host(c)
+        hx = (host(xq[0]), host(xq[1]))
+        # activations and weights quantized bit-exactly on sampled rows
+        xs = rng.choice(offs[-1], 256, replace=False)
+        oq = O.quantize(O.bf16_bits_to_f32(xin[xs]))
+        assert_bytes_equal(hx[0][xs], oq[0], f"{name} X codes")
+        assert_bytes_equal(hx[1][xs], oq[1], f"{name} X scales")
+        for e in rng.choice(E, 6, replace=False):
+            a, b = offs[e], offs[e + 1]
+            rows = np.sort(rng.choice(np.arange(a, b), min(8, b - a), replace=False))
+            wrows = wm[r0 + e * n_out: r0 + (e + 1) * n_out]
+            owq = O.quantize(wrows)
+            assert_bytes_equal(host(wc[e * n_out:(e + 1) * n_out]), owq[0], f"{name} W{e} codes")
+            want = O.gemm(hx[0][rows], hx[1][rows], *owq, len(rows), n_out, H)
+            ab = O.gemm_abs(hx[0][rows], hx[1][rows], *owq, len(rows), n_out, H)
+            assert_gemm_close(got[rows], want, ab, f"{name} expert {e}")
+
+
+# ------------------------------------------------------------------ de-oscillation
+def run_deosc_gpu(w0, steps, seed, thr=4.0):
+    rows, cols = w0.shape
+    w = to_dev_f32(w0)
+    st = [torch.empty_like(w) for _ in range(3)]
+    flags = torch.full((rows, cols), 7, dtype=torch.uint8, device=DEV)
+    mx.mx_deosc_init(w, rows, cols, *st)
+    for t in range(1, steps + 1):
+        mx.mx_synth_step(w, rows * cols, seed, t)
+        mx.mx_deosc_step(w, rows, cols, *st, t == steps, thr, flags)
+    return host(w), [host(s) for s in st], host(flags)
+
+
+def run_deosc_oracle(w0, steps, seed, thr=4.0, idx=None):
+    w = w0.copy()
+    idx = np.arange(w.size).reshape(w.shape) if idx is None else idx
+    w_prev, d_w, d_q = O.deosc_init(w)
+    flags = None
+    for t in range(1, steps + 1):
+        w = (w + synth.deosc_delta_f32(seed, t, idx)).astype(np.float32)
+        w, w_prev, d_w, d_q, flags = O.deosc_step(w, w_prev, d_w, d_q, t == steps, thr)
+    return w, [w_prev, d_w, d_q], flags
+
+
+def test_synthetic_step_matches_cpu_replay():
+    rng = np.random.default_rng(1)
+    w0 = (rng.standard_normal((64, 96)) * 0.02).astype(np.float32)
+    w = to_dev_f32(w0)
+    mx.mx_synth_step(w, w0.size, 4, 17)
+    want = (w0 + synth.deosc_delta_f32(4, 17, np.arange(w0.size)).reshape(w0.shape)).astype(np.float32)
+    assert_bytes_equal(host(w).view(np.uint32), want.view(np.uint32), "w")
+
+
+@pytest.mark.parametrize("thr", [4.0, 1.0])
+def test_deosc_window_matches_oracle(thr):
+    rng = np.random.default_rng(2)
+    w0 = (rng.standard_normal((96, 2880)) * 0.02).astype(np.float32)
+    w0[3, :32] = 0.0
+    steps = 50
+    gw, gst, gf = run_deosc_gpu(w0, steps, 4, thr)
+    ow, ost, of = run_deosc_oracle(w0, steps, 4, thr)
+    assert of.sum() > 0
+    assert_bytes_equal(gf, of, "flags")
+    assert_bytes_equal(gw.view(np.uint32), ow.view(np.uint32), "w")
+    for g, o, name in zip(gst, ost, ["w_prev", "d_w", "d_q"]):
+        assert_bytes_equal(g.view(np.uint32), o.view(np.uint32), name)
+
+
+def test_deosc_mid_window_state_matches_oracle():
+    rng = np.random.default_rng(3)
+    w0 = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    rows, cols = w0.shape
+    w = to_dev_f32(w0)
+    st = [torch.empty_like(w) for _ in range(3)]
+    mx.mx_deosc_init(w, rows, cols, *st)
+    ow = w0.copy()
+    ost = list(O.deosc_init(ow))
+    for t in range(1, 31):
+        mx.mx_synth_step(w, rows * cols, 9, t)
+        mx.mx_deosc_step(w, rows, cols, *st, False, 4.0, None)
+        ow = (ow + synth.deosc_delta_f32(9, t, np.arange(ow.size)).reshape(ow.shape)).astype(np.float32)
+        ow, *ost, _ = O.deosc_step(ow, *ost, False, 4.0)
+    for g, o, name in zip(st, ost, ["w_prev", "d_w", "d_q"]):
+        assert_bytes_equal(host(g).view(np.uint32), o.view(np.uint32), name)
+
+
+def test_deosc_worked_example_on_gpu():
+    """ALTO page worked example driven through the kernel: the oscillating element
+    (ratio 75) is flagged and snapped to 0.25, the drifting one (ratio ~0.8) is not."""
+    w = np.zeros((1, 32), np.float32)
+    w[0, 0] = 3.0
+    lo, hi = np.float32(0.375 - 0.02 / 12), np.float32(0.375 + 0.02 / 12)
+    w[0, 1] = lo
+    w[0, 2] = np.float32(0.55)
+    dev = to_dev_f32(w)
+    st = [torch.empty_like(dev) for _ in range(3)]
+    flags = torch.zeros((1, 32), dtype=torch.uint8, device=DEV)
+    mx.mx_deosc_init(dev, 1, 32, *st)
+    cross = set(np.linspace(10, 190, 6).astype(int).tolist())
+    side = 0
+    for t in range(1, 201):
+        if t in cross:
+            side ^= 1
+            w[0, 1] = hi if side else lo
+        w[0, 2] = np.float32(0.55 + 0.30 * t / 200)
+        dev.copy_(torch.from_numpy(w))
+        mx.mx_deosc_step(dev, 1, 32, *st, t == 200, 4.0, flags)
+    f = host(flags)
+    out = host(dev)
+    assert f[0, 1] == 1 and f[0, 2] == 0 and f[0, 0] == 0
+    assert out[0, 1] == np.float32(0.25) and out[0, 2] == np.float32(0.85)
+
+
+@pytest.mark.slow
+def test_deosc_moe_master_weights_sampled():
+    """All 796,262,400 fp32 MoE master weights over a 200-step window (end at step 200,
+    threshold 4.0); flags and state checked on 2048 sampled 1x32 blocks."""
+    cfg = synth.moe_config()
+    wm = cfg["w_master"]
+    rows, cols = wm.shape
+    gw, gst, gf = run_deosc_gpu(wm, 200, 4)
+    rng = np.random.default_rng(5)
+    r = rng.integers(0, rows, 2048)
+    b = rng.integers(0, cols // 32, 2048)
+    cidx = b[:, None] * 32 + np.arange(32)[None, :]
+    sub = wm[r[:, None], cidx]
+    idx = r[:, None].astype(np.int64) * cols + cidx
+    ow, ost, of = run_deosc_oracle(sub, 200, 4, idx=idx)
+    assert_bytes_equal(gf[r[:, None], cidx], of, "flags")
+    assert_bytes_equal(gw[r[:, None], cidx].view(np.uint32), ow.view(np.uint32), "w")
+    print(f"flagged fraction {gf.mean():.3e}", flush=True)
