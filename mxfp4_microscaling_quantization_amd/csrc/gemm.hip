@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mx_host.h"
 
 namespace mx {
@@ -48,24 +50,98 @@ __device__ __forceinline__ v8i as_v8i(uint4 u) {
   return r;
 }
 
-template <int BM, int BN, int WM, int WN>
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ int64_t lmax(int64_t a, int64_t b) { return a > b ? a : b; }
+
+// Direct global -> LDS loads (no destination VGPRs): lane i's 16 bytes (or 1
+// byte) land at LDS address M0 + 16 i (or M0 + i).  Written as asm so that the
+// compiler does not track these writes itself: the kernel waits on vmcnt
+// explicitly before each barrier, and the "memory" clobber keeps LDS reads
+// from moving above an issue.  M0 is set in the same block.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr_t)p;
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is written on purpose, nothing else here uses it
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_addr(lds)), "v"(g)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(lds_addr(lds)), "v"(g)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma1(const void* g, void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ubyte %1, off"
+               :
+               : "s"(lds_addr(lds)), "v"(g)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Operand tile in LDS, per stage: codes [rows][64 B] with the four 16-byte
+// chunks of row r stored in the order c ^ ((r >> 2) & 3), so that the 16 lanes
+// reading chunk c of 16 consecutive rows hit 16 different bank groups.  One
+// direct-to-LDS load moves 16 rows (4 lanes per row, 64 contiguous bytes of
+// global memory).
+// Scales: a dword DMA puts lane i's 4 bytes at [4i, 4i+4) and a byte DMA puts
+// lane i's byte in the low byte of dword i.  With 4-byte aligned scale rows
+// (K/32 % 4 == 0) one dword per row carries the step's four scale bytes:
+// layout [rows][4] bytes.  Otherwise one byte per dword: layout [4][rows] dwords.
+template <int ROWS, bool SDW>
+struct TileLds {
+  uint4 codes[ROWS * 4];
+  uint32_t scales[SDW ? ROWS : ROWS * 4];
+};
+
+template <int BM, int BN, bool SDW>
+struct StageLds {
+  TileLds<BM, SDW> a;
+  TileLds<BN, SDW> b;
+};
+
+template <int BM, int BN, int WM, int WN, int STAGES, bool SDW>
 __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, int64_t N, int64_t K, float alpha, float* __restrict__ C,
     int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, GemmGroups gg) {
-  constexpr int NT = WM * WN * 64;
+  constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 16;  // 16-row MFMA tiles per wave along m
   constexpr int TN = BN / WN / 16;  // along n
-  constexpr int A_CHUNKS = BM * 4 / NT;
-  constexpr int B_CHUNKS = BN * 4 / NT;
-  constexpr int A_SC = BM * 4 / NT;
-  constexpr int B_SC = BN * 4 / NT;
-  static_assert(A_CHUNKS * NT == BM * 4 && B_CHUNKS * NT == BN * 4, "tile/thread mismatch");
+  constexpr int LA = BM / 16 / NW;  // code DMAs per wave per step, A (16 rows each)
+  constexpr int LB = BN / 16 / NW;
+  constexpr int QG = (BM + BN) / 64;                 // 64-row groups of both operands
+  constexpr int QW = (SDW ? QG : 4 * QG) / NW;       // scale DMAs per wave per step
+  constexpr int L = LA + LB + QW;                    // vector-memory instructions per wave per step
+  static_assert(LA * NW * 16 == BM && LB * NW * 16 == BN, "tile/wave mismatch");
+  static_assert(QW * NW == (SDW ? QG : 4 * QG) && BM % 64 == 0 && BN % 64 == 0, "scale jobs");
+  static_assert(STAGES == 4 && L * (STAGES - 2) < 64, "pipeline depth");
 
-  __shared__ uint4 sA[2][4 * BM];
-  __shared__ uint4 sB[2][4 * BN];
-  __shared__ uint8_t sSA[2][4 * BM];
-  __shared__ uint8_t sSB[2][4 * BN];
+  // One LDS object per stage, every access with a compile-time stage: nothing
+  // in flight to one stage can be confused with reads of another.
+  __shared__ StageLds<BM, BN, SDW> s0, s1, s2, s3;
+  auto stage = [&](auto S) -> StageLds<BM, BN, SDW>& {
+    if constexpr (decltype(S)::value == 0) return s0;
+    else if constexpr (decltype(S)::value == 1) return s1;
+    else if constexpr (decltype(S)::value == 2) return s2;
+    else return s3;
+  };
+  auto bufA = [&](auto S) -> TileLds<BM, SDW>& { return stage(S).a; };
+  auto bufB = [&](auto S) -> TileLds<BN, SDW>& { return stage(S).b; };
 
   // ---- which tile: spread consecutive logical tiles over one XCD (workgroups
   // are dealt round-robin to the 8 XCDs), then walk kGroupM tile rows at a time.
@@ -91,72 +167,75 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
   const int rows_valid = (int)min<int64_t>(BM, grow0 + grows - m0);
   const int64_t n0 = (int64_t)tn_idx * BN;
   const int cols_valid = (int)min<int64_t>(BN, N - n0);
+  const int64_t a_last = gg.row_off[gg.ngroups] - 1;  // last row of A in memory
   const uint8_t* Bg = B + (int64_t)g * b_stride_codes;
   const uint8_t* SBg = SB + (int64_t)g * b_stride_scales;
 
   const int64_t ldk = K / 2;   // code bytes per row
-  const int64_t lds = K / 32;  // scale bytes per row
+  const int64_t lds = K / 32;  // scale bytes (32-blocks) per row
   const int KT = (int)((K + 127) / 128);
+  const int tail_kb = (int)(lds - (int64_t)(KT - 1) * 4);  // valid 32-blocks in the last step
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm_off = (wave / WN) * (BM / WM);
   const int wn_off = (wave % WN) * (BN / WN);
   const int lr = lane & 15;
   const int lk = lane >> 4;
 
-  uint4 ra[A_CHUNKS], rb[B_CHUNKS];
-  uint32_t rsa[A_SC], rsb[B_SC];
+  // Per-lane DMA sources for this wave's rows (row clamped into memory; rows
+  // past the tile's valid range feed outputs that are never stored).
+  const int dr = lane >> 2;                        // row within a 16-row group
+  const int dc = (lane & 3) ^ ((dr >> 2) & 3);     // chunk this lane fetches
+  const uint8_t* a_src[LA];
+  const uint8_t* b_src[LB];
+#pragma unroll
+  for (int j = 0; j < LA; ++j) {
+    const int64_t row = lmin(m0 + (wave * LA + j) * 16 + dr, a_last);
+    a_src[j] = A + row * ldk + dc * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < LB; ++j) {
+    const int64_t row = lmin(n0 + (wave * LB + j) * 16 + dr, N - 1);
+    b_src[j] = Bg + row * ldk + dc * 16;
+  }
+  // scale jobs: job q covers 64 rows (lane = row) of A (q % QG < BM/64) or B,
+  // for all four 32-blocks (dword mode) or for 32-block q / QG (byte mode)
+  const uint8_t* s_src[QW];
+  int s_dst[QW];  // dword offset in the stage's a.scales / b.scales, B marked by +2^20
+#pragma unroll
+  for (int j = 0; j < QW; ++j) {
+    const int q = wave * QW + j;
+    const int grp = q % QG, kb = SDW ? 0 : q / QG;
+    const bool isA = grp < BM / 64;
+    const int r0 = (isA ? grp : grp - BM / 64) * 64;
+    const int64_t row = isA ? lmin(m0 + r0 + lane, a_last) : lmin(n0 + r0 + lane, N - 1);
+    s_src[j] = (isA ? SA : SBg) + row * lds + kb;
+    s_dst[j] = (SDW ? r0 : kb * (isA ? BM : BN) + r0) + (isA ? 0 : (1 << 20));
+  }
 
-  auto load_step = [&](int kt) {
+  auto issue = [&](int kt, auto S) {
+    // the last step may have fewer than 4 valid 32-blocks: clamp the column so
+    // the load stays inside the row; those blocks are masked before the MFMA.
+    TileLds<BM, SDW>& ta = bufA(S);
+    TileLds<BN, SDW>& tb = bufB(S);
+    const int64_t kc = (int64_t)kt * 64;
+    const int64_t coff = lmin(kc, lmax(ldk - 16 - dc * 16, -dc * 16));
 #pragma unroll
-    for (int j = 0; j < A_CHUNKS; ++j) {
-      const int i = tid + j * NT, row = i >> 2, ch = i & 3;
-      const bool ok = row < rows_valid && (int64_t)kt * 4 + ch < lds;
-      ra[j] = ok ? *reinterpret_cast<const uint4*>(A + (m0 + row) * ldk + (int64_t)kt * 64 + ch * 16)
-                 : make_uint4(0, 0, 0, 0);
-    }
+    for (int j = 0; j < LA; ++j) dma16(a_src[j] + coff, &ta.codes[((wave * LA + j) * 16) * 4]);
 #pragma unroll
-    for (int j = 0; j < B_CHUNKS; ++j) {
-      const int i = tid + j * NT, row = i >> 2, ch = i & 3;
-      const bool ok = row < cols_valid && (int64_t)kt * 4 + ch < lds;
-      rb[j] = ok ? *reinterpret_cast<const uint4*>(Bg + (n0 + row) * ldk + (int64_t)kt * 64 + ch * 16)
-                 : make_uint4(0, 0, 0, 0);
-    }
+    for (int j = 0; j < LB; ++j) dma16(b_src[j] + coff, &tb.codes[((wave * LB + j) * 16) * 4]);
 #pragma unroll
-    for (int j = 0; j < A_SC; ++j) {
-      const int i = tid + j * NT, row = i >> 2, kb = i & 3;
-      const bool ok = row < rows_valid && (int64_t)kt * 4 + kb < lds;
-      rsa[j] = ok ? SA[(m0 + row) * lds + (int64_t)kt * 4 + kb] : 127u;
-    }
-#pragma unroll
-    for (int j = 0; j < B_SC; ++j) {
-      const int i = tid + j * NT, row = i >> 2, kb = i & 3;
-      const bool ok = row < cols_valid && (int64_t)kt * 4 + kb < lds;
-      rsb[j] = ok ? SBg[(n0 + row) * lds + (int64_t)kt * 4 + kb] : 127u;
-    }
-  };
-  auto store_step = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < A_CHUNKS; ++j) {
-      const int i = tid + j * NT;
-      sA[buf][(i & 3) * BM + (i >> 2)] = ra[j];
-    }
-#pragma unroll
-    for (int j = 0; j < B_CHUNKS; ++j) {
-      const int i = tid + j * NT;
-      sB[buf][(i & 3) * BN + (i >> 2)] = rb[j];
-    }
-#pragma unroll
-    for (int j = 0; j < A_SC; ++j) {
-      const int i = tid + j * NT;
-      sSA[buf][(i & 3) * BM + (i >> 2)] = (uint8_t)rsa[j];
-    }
-#pragma unroll
-    for (int j = 0; j < B_SC; ++j) {
-      const int i = tid + j * NT;
-      sSB[buf][(i & 3) * BN + (i >> 2)] = (uint8_t)rsb[j];
+    for (int j = 0; j < QW; ++j) {
+      const bool isB = s_dst[j] >= (1 << 20);
+      uint32_t* dst = isB ? &tb.scales[s_dst[j] - (1 << 20)] : &ta.scales[s_dst[j]];
+      if (SDW) {
+        dma4(s_src[j] + (int64_t)kt * 4, dst);
+      } else {
+        const int kb = (wave * QW + j) / QG;
+        dma1(s_src[j] + lmin((int64_t)kt * 4, lds - 1 - kb), dst);
+      }
     }
   };
 
@@ -166,27 +245,52 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
 #pragma unroll
     for (int b = 0; b < TM; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  if (KT > 0) {
-    load_step(0);
-    store_step(0);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) load_step(kt + 1);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  if (0 < KT) issue(0, I0{});
+  if (1 < KT) issue(1, I1{});
+  if (2 < KT) issue(2, I2{});
+
+  auto step = [&](int kt, auto S) {
+    // wait for this step's loads: later steps already issued may stay in flight
+    const int ahead = min(KT - 1 - kt, STAGES - 2);
+    if (ahead >= 2) wait_vmcnt<2 * L>();
+    else if (ahead == 1) wait_vmcnt<L>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // every wave's loads landed; step kt-1's stage is free
+
+    const TileLds<BM, SDW>& ta = bufA(S);
+    const TileLds<BN, SDW>& tb = bufB(S);
     uint4 fa[TM], fb[TN];
     int sa[TM], sb[TN];
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       const int row = wm_off + t * 16 + lr;
-      fa[t] = sA[buf][lk * BM + row];
-      sa[t] = sSA[buf][lk * BM + row];
+      fa[t] = ta.codes[row * 4 + (lk ^ ((row >> 2) & 3))];
+      sa[t] = SDW ? reinterpret_cast<const uint8_t*>(ta.scales)[row * 4 + lk]
+                  : reinterpret_cast<const uint8_t*>(ta.scales)[4 * (lk * BM + row)];
     }
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       const int row = wn_off + t * 16 + lr;
-      fb[t] = sB[buf][lk * BN + row];
-      sb[t] = sSB[buf][lk * BN + row];
+      fb[t] = tb.codes[row * 4 + (lk ^ ((row >> 2) & 3))];
+      sb[t] = SDW ? reinterpret_cast<const uint8_t*>(tb.scales)[row * 4 + lk]
+                  : reinterpret_cast<const uint8_t*>(tb.scales)[4 * (lk * BN + row)];
+    }
+    // refill the stage step kt-1 used (every wave is past its reads)
+    using SN = std::integral_constant<int, (decltype(S)::value + 3) % 4>;
+    if (kt + 3 < KT) issue(kt + 3, SN{});
+    if (kt == KT - 1 && lk >= tail_kb) {
+      // 32-blocks past K: zero A's codes, neutral scales on both sides
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        fa[t] = make_uint4(0, 0, 0, 0);
+        sa[t] = 127;
+      }
+#pragma unroll
+      for (int t = 0; t < TN; ++t) sb[t] = 127;
     }
 #pragma unroll
     for (int a = 0; a < TN; ++a)
@@ -194,8 +298,13 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
       for (int b = 0; b < TM; ++b)
         acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             as_v8i(fb[a]), as_v8i(fa[b]), acc[a][b], kFmtFp4, kFmtFp4, 0, sb[a], 0, sa[b]);
-    if (kt + 1 < KT) store_step(buf ^ 1);
-    __syncthreads();
+  };
+
+  for (int kt = 0; kt < KT; kt += 4) {
+    step(kt, I0{});
+    if (kt + 1 < KT) step(kt + 1, I1{});
+    if (kt + 2 < KT) step(kt + 2, I2{});
+    if (kt + 3 < KT) step(kt + 3, I3{});
   }
 
   // ---- epilogue: lane holds D[n = 4 lk + v][m = lr] of each 16x16 tile
@@ -220,7 +329,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
 }
 
 // ---------------------------------------------------------------- host side
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool SDW>
 static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                        const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha,
                        float* c, int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales,
@@ -237,22 +346,27 @@ static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
   gg.row_off[groups] = offs[groups];
   const int total = gg.tile_start[groups];
   if (total == 0) return MX_OK;
-  k_gemm_mx<BM, BN, WM, WN><<<dim3(total), dim3(WM * WN * 64), 0, st>>>(
+  k_gemm_mx<BM, BN, WM, WN, 4, SDW><<<dim3(total), dim3(WM * WN * 64), 0, st>>>(
       a, sa, b, sb, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, gg);
   return launch_status();
 }
 
-// Large tiles when they still give every CU a few tiles, else smaller ones.
+// Large tiles when they still give every CU a few tiles, else smaller ones;
+// scale rows go by dword loads when every scale row starts 4-byte aligned.
 int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
               const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha, float* c,
               int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, hipStream_t st) {
   int64_t tiles256 = 0;
   for (int64_t g = 0; g < groups; ++g) tiles256 += cdiv(offs[g + 1] - offs[g], 256) * cdiv(N, 256);
-  if (tiles256 >= 512)
-    return launch_gemm<256, 256, 2, 2>(a, sa, b, sb, offs, groups, N, K, alpha, c, ldc,
-                                       b_stride_codes, b_stride_scales, st);
-  return launch_gemm<128, 128, 2, 2>(a, sa, b, sb, offs, groups, N, K, alpha, c, ldc,
-                                     b_stride_codes, b_stride_scales, st);
+  const bool sdw = (K / 32) % 4 == 0 && (reinterpret_cast<uintptr_t>(sa) & 3u) == 0 &&
+                   (reinterpret_cast<uintptr_t>(sb) & 3u) == 0 && b_stride_scales % 4 == 0;
+  const bool big = tiles256 >= 512;
+#define MX_GEMM_ARGS a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, st
+  if (big) return sdw ? launch_gemm<256, 256, 2, 2, true>(MX_GEMM_ARGS)
+                      : launch_gemm<256, 256, 2, 2, false>(MX_GEMM_ARGS);
+  return sdw ? launch_gemm<128, 128, 2, 2, true>(MX_GEMM_ARGS)
+             : launch_gemm<128, 128, 2, 2, false>(MX_GEMM_ARGS);
+#undef MX_GEMM_ARGS
 }
 
 }  // namespace mx

@@ -45,21 +45,21 @@ __device__ __forceinline__ uint32_t e2m1_rne(float a) {
 }
 
 // Stochastic E2M1 rounding of a in [0, 8): the lower neighbour's index plus 1
-// iff r24 < floor(t * 2^24), t = (a - lo) / (hi - lo).  a >= 6 gives 6.
-//  a >= 1: lower index = (bits >> 22) - 252; the 22 dropped mantissa bits are
-//          t * 2^22 exactly, so floor(t * 2^24) = dropped << 2.
-//  a < 1:  spacing 0.5; 2a is exact, t = 2a - floor(2a) exact, t * 2^24 < 2^24.
+// iff r24 < floor(t * 2^24), t = (a - lo) / (hi - lo); a >= 6 gives 6.  Both
+// ranges are written as "add a complement of the random bits below the kept
+// precision and let the carry decide":
+//  a >= 1: the 22 dropped mantissa bits d equal t * 2^22, and r24 < 4d exactly
+//          when floor(r24 / 4) < d, i.e. when d + (2^22 - 1 - floor(r24 / 4))
+//          carries into the kept bit; the carry may run into the exponent (next
+//          binade), and the index is (bits >> 22) - 252 as for nearest rounding.
+//  a < 1:  F = a * 2^25 is exact and F mod 2^24 = t * 2^24 (spacing 0.5), so
+//          the index is (F + 2^24 - 1 - r24) >> 24.
 __device__ __forceinline__ uint32_t e2m1_sr(float a, uint32_t r24) {
   const uint32_t b = __float_as_uint(a);
-  const uint32_t lo_n = (b - 0x3F000000u) >> 22;
-  const uint32_t t_n = (b & 0x3FFFFFu) << 2;
-  const float a2 = a + a;
-  const uint32_t lo_s = a2 >= 1.0f ? 1u : 0u;
-  const uint32_t t_s = (uint32_t)((a2 - (float)lo_s) * 16777216.0f);
-  const bool small = a < 1.0f;
-  const uint32_t lo = small ? lo_s : lo_n;
-  const uint32_t t = small ? t_s : t_n;
-  const uint32_t c = lo + (r24 < t ? 1u : 0u);
+  const uint32_t nrm = (b + (0x3FFFFFu - (r24 >> 2)) - 0x3F000000u) >> 22;
+  const uint32_t F = (uint32_t)(a * 33554432.0f);
+  const uint32_t sub = (F + (0xFFFFFFu - r24)) >> 24;
+  const uint32_t c = a < 1.0f ? sub : nrm;
   return c < 7u ? c : 7u;
 }
 
