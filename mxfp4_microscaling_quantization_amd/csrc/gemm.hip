@@ -33,6 +33,7 @@ namespace mx {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kFmtFp4 = 4;  // cbsz / blgp operand format: FP4 E2M1
 
@@ -102,46 +103,59 @@ __device__ __forceinline__ void dma1(const void* g, void* lds) {
 // lane i's byte in the low byte of dword i.  With 4-byte aligned scale rows
 // (K/32 % 4 == 0) one dword per row carries the step's four scale bytes:
 // layout [rows][4] bytes.  Otherwise one byte per dword: layout [4][rows] dwords.
-template <int ROWS, bool SDW>
+// Scale modes: kScGroup -- K/32 % 16 == 0: one 16-byte load per row brings the
+// scales of four K-steps into a separate double buffer [rows][16 B] once per
+// four steps (a quarter of the cache lines a per-step load touches);
+// kScDword -- K/32 % 4 == 0: one dword per row and step, layout [rows][4];
+// kScByte -- otherwise: one byte per row and step, layout [4][rows] dwords.
+enum { kScGroup = 0, kScDword = 1, kScByte = 2 };
+
+template <int ROWS, int SC>
 struct TileLds {
   uint4 codes[ROWS * 4];
-  uint32_t scales[SDW ? ROWS : ROWS * 4];
+  uint32_t scales[SC == kScGroup ? 1 : (SC == kScDword ? ROWS : ROWS * 4)];
 };
 
-template <int BM, int BN, bool SDW>
+template <int BM, int BN, int SC>
 struct StageLds {
-  TileLds<BM, SDW> a;
-  TileLds<BN, SDW> b;
+  TileLds<BM, SC> a;
+  TileLds<BN, SC> b;
 };
 
-template <int BM, int BN, int WM, int WN, int STAGES, bool SDW>
+template <int BM, int BN>
+struct ScaleGroupLds {
+  uint4 a[BM];
+  uint4 b[BN];
+};
+
+template <int BM, int BN, int WM, int WN, int STAGES, int SC>
 __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, int64_t N, int64_t K, float alpha, float* __restrict__ C,
     int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, GemmGroups gg) {
   constexpr int NW = WM * WN;
-  constexpr int TM = BM / WM / 16;  // 16-row MFMA tiles per wave along m
-  constexpr int TN = BN / WN / 16;  // along n
+  constexpr int TM = BM / WM / 32;  // 32-row MFMA tiles per wave along m
+  constexpr int TN = BN / WN / 32;  // along n
   constexpr int LA = BM / 16 / NW;  // code DMAs per wave per step, A (16 rows each)
   constexpr int LB = BN / 16 / NW;
   constexpr int QG = (BM + BN) / 64;                 // 64-row groups of both operands
-  constexpr int QW = (SDW ? QG : 4 * QG) / NW;       // scale DMAs per wave per step
-  constexpr int L = LA + LB + QW;                    // vector-memory instructions per wave per step
+  constexpr int QW = (SC == kScByte ? 4 * QG : QG) / NW;  // scale DMAs per wave per step (or group)
+  constexpr int LC = LA + LB + (SC == kScGroup ? 0 : QW);  // per-step vector-memory instructions
   static_assert(LA * NW * 16 == BM && LB * NW * 16 == BN, "tile/wave mismatch");
-  static_assert(QW * NW == (SDW ? QG : 4 * QG) && BM % 64 == 0 && BN % 64 == 0, "scale jobs");
-  static_assert(STAGES == 4 && L * (STAGES - 2) < 64, "pipeline depth");
+  static_assert(QW * NW == (SC == kScByte ? 4 * QG : QG) && BM % 64 == 0 && BN % 64 == 0, "scale jobs");
+  static_assert(STAGES == 4 && 2 * LC + QW < 64, "pipeline depth");
 
-  // One LDS object per stage, every access with a compile-time stage: nothing
-  // in flight to one stage can be confused with reads of another.
-  __shared__ StageLds<BM, BN, SDW> s0, s1, s2, s3;
-  auto stage = [&](auto S) -> StageLds<BM, BN, SDW>& {
+  // One LDS object per stage, every access with a compile-time stage.
+  __shared__ StageLds<BM, BN, SC> s0, s1, s2, s3;
+  __shared__ ScaleGroupLds<(SC == kScGroup ? BM : 1), (SC == kScGroup ? BN : 1)> sg[2];
+  auto stage = [&](auto S) -> StageLds<BM, BN, SC>& {
     if constexpr (decltype(S)::value == 0) return s0;
     else if constexpr (decltype(S)::value == 1) return s1;
     else if constexpr (decltype(S)::value == 2) return s2;
     else return s3;
   };
-  auto bufA = [&](auto S) -> TileLds<BM, SDW>& { return stage(S).a; };
-  auto bufB = [&](auto S) -> TileLds<BN, SDW>& { return stage(S).b; };
+  auto bufA = [&](auto S) -> TileLds<BM, SC>& { return stage(S).a; };
+  auto bufB = [&](auto S) -> TileLds<BN, SC>& { return stage(S).b; };
 
   // ---- which tile: spread consecutive logical tiles over one XCD (workgroups
   // are dealt round-robin to the 8 XCDs), then walk kGroupM tile rows at a time.
@@ -181,8 +195,8 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm_off = (wave / WN) * (BM / WM);
   const int wn_off = (wave % WN) * (BN / WN);
-  const int lr = lane & 15;
-  const int lk = lane >> 4;
+  const int lr = lane & 31;  // MFMA operand row of this lane
+  const int lh = lane >> 5;  // which 32-block of the instruction's 64 K-values
 
   // Per-lane DMA sources for this wave's rows (row clamped into memory; rows
   // past the tile's valid range feed outputs that are never stored).
@@ -201,103 +215,173 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
     b_src[j] = Bg + row * ldk + dc * 16;
   }
   // scale jobs: job q covers 64 rows (lane = row) of A (q % QG < BM/64) or B,
-  // for all four 32-blocks (dword mode) or for 32-block q / QG (byte mode)
+  // for all 32-blocks of a step (dword), of four steps (group) or for 32-block
+  // q / QG (byte mode)
   const uint8_t* s_src[QW];
-  int s_dst[QW];  // dword offset in the stage's a.scales / b.scales, B marked by +2^20
+  int s_dst[QW];  // dword / uint4 offset in the A or B scale area, B marked by +2^20
 #pragma unroll
   for (int j = 0; j < QW; ++j) {
     const int q = wave * QW + j;
-    const int grp = q % QG, kb = SDW ? 0 : q / QG;
+    const int grp = q % QG, kb = SC == kScByte ? q / QG : 0;
     const bool isA = grp < BM / 64;
     const int r0 = (isA ? grp : grp - BM / 64) * 64;
     const int64_t row = isA ? lmin(m0 + r0 + lane, a_last) : lmin(n0 + r0 + lane, N - 1);
     s_src[j] = (isA ? SA : SBg) + row * lds + kb;
-    s_dst[j] = (SDW ? r0 : kb * (isA ? BM : BN) + r0) + (isA ? 0 : (1 << 20));
+    s_dst[j] = (SC == kScByte ? kb * (isA ? BM : BN) + r0 : r0) + (isA ? 0 : (1 << 20));
   }
 
   auto issue = [&](int kt, auto S) {
     // the last step may have fewer than 4 valid 32-blocks: clamp the column so
     // the load stays inside the row; those blocks are masked before the MFMA.
-    TileLds<BM, SDW>& ta = bufA(S);
-    TileLds<BN, SDW>& tb = bufB(S);
+    TileLds<BM, SC>& ta = bufA(S);
+    TileLds<BN, SC>& tb = bufB(S);
     const int64_t kc = (int64_t)kt * 64;
     const int64_t coff = lmin(kc, lmax(ldk - 16 - dc * 16, -dc * 16));
 #pragma unroll
     for (int j = 0; j < LA; ++j) dma16(a_src[j] + coff, &ta.codes[((wave * LA + j) * 16) * 4]);
 #pragma unroll
     for (int j = 0; j < LB; ++j) dma16(b_src[j] + coff, &tb.codes[((wave * LB + j) * 16) * 4]);
+    if constexpr (SC != kScGroup) {
 #pragma unroll
-    for (int j = 0; j < QW; ++j) {
-      const bool isB = s_dst[j] >= (1 << 20);
-      uint32_t* dst = isB ? &tb.scales[s_dst[j] - (1 << 20)] : &ta.scales[s_dst[j]];
-      if (SDW) {
-        dma4(s_src[j] + (int64_t)kt * 4, dst);
-      } else {
-        const int kb = (wave * QW + j) / QG;
-        dma1(s_src[j] + lmin((int64_t)kt * 4, lds - 1 - kb), dst);
+      for (int j = 0; j < QW; ++j) {
+        const bool isB = s_dst[j] >= (1 << 20);
+        uint32_t* dst = isB ? &tb.scales[s_dst[j] - (1 << 20)] : &ta.scales[s_dst[j]];
+        if (SC == kScDword) {
+          dma4(s_src[j] + (int64_t)kt * 4, dst);
+        } else {
+          const int kb = (wave * QW + j) / QG;
+          dma1(s_src[j] + lmin((int64_t)kt * 4, lds - 1 - kb), dst);
+        }
+      }
+    }
+  };
+  // group mode: scales of steps 4 g .. 4 g + 3 (16 bytes per row) into sg[g & 1]
+  auto issue_scales = [&](int grp) {
+    if constexpr (SC == kScGroup) {
+      ScaleGroupLds<(SC == kScGroup ? BM : 1), (SC == kScGroup ? BN : 1)>& t = sg[grp & 1];
+#pragma unroll
+      for (int j = 0; j < QW; ++j) {
+        const bool isB = s_dst[j] >= (1 << 20);
+        uint4* dst = isB ? &t.b[s_dst[j] - (1 << 20)] : &t.a[s_dst[j]];
+        dma16(s_src[j] + (int64_t)grp * 16, dst);
       }
     }
   };
 
-  v4f acc[TN][TM];
+  v16f acc[TN][TM];
 #pragma unroll
   for (int a = 0; a < TN; ++a)
 #pragma unroll
-    for (int b = 0; b < TM; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < TM; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
+  issue_scales(0);
   if (0 < KT) issue(0, I0{});
   if (1 < KT) issue(1, I1{});
   if (2 < KT) issue(2, I2{});
 
   auto step = [&](int kt, auto S) {
-    // wait for this step's loads: later steps already issued may stay in flight
+    constexpr int P = decltype(S)::value;  // kt % 4
+    // Wait for this step's loads; later loads already issued may stay in
+    // flight: the code loads of steps kt+1, kt+2 and, in group mode, the next
+    // scale group if it was issued after this step's codes (at step 4*(kt/4)).
     const int ahead = min(KT - 1 - kt, STAGES - 2);
-    if (ahead >= 2) wait_vmcnt<2 * L>();
-    else if (ahead == 1) wait_vmcnt<L>();
-    else wait_vmcnt<0>();
+    if (ahead >= 2) {
+      if (SC == kScGroup && P != 0 && kt + 4 - P < KT) wait_vmcnt<2 * LC + QW>();
+      else wait_vmcnt<2 * LC>();
+    } else {
+      wait_vmcnt<0>();
+    }
     __builtin_amdgcn_s_barrier();  // every wave's loads landed; step kt-1's stage is free
 
-    const TileLds<BM, SDW>& ta = bufA(S);
-    const TileLds<BN, SDW>& tb = bufB(S);
-    uint4 fa[TM], fb[TN];
-    int sa[TM], sb[TN];
+    const TileLds<BM, SC>& ta = bufA(S);
+    const TileLds<BN, SC>& tb = bufB(S);
+    const uint8_t* sab = SC == kScGroup ? reinterpret_cast<const uint8_t*>(sg[(kt >> 2) & 1].a)
+                                        : reinterpret_cast<const uint8_t*>(ta.scales);
+    const uint8_t* sbb = SC == kScGroup ? reinterpret_cast<const uint8_t*>(sg[(kt >> 2) & 1].b)
+                                        : reinterpret_cast<const uint8_t*>(tb.scales);
+    // Two 64-wide K halves per step; the lane supplies 32-block kb = 2 h + lh of
+    // its row.  Scales: one dword per row holds the step's four blocks; shifted
+    // right by 8 lh, blocks lh and 2 + lh sit in bytes 0 and 2, which the MFMA
+    // selects with its scale op_sel (0 for the first half, 2 for the second).
+    uint4 fa[2][TM], fb[2][TN];
+    uint32_t sa[TM], sb[TN];
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
-      const int row = wm_off + t * 16 + lr;
-      fa[t] = ta.codes[row * 4 + (lk ^ ((row >> 2) & 3))];
-      sa[t] = SDW ? reinterpret_cast<const uint8_t*>(ta.scales)[row * 4 + lk]
-                  : reinterpret_cast<const uint8_t*>(ta.scales)[4 * (lk * BM + row)];
+      const int row = wm_off + t * 32 + lr;
+      if constexpr (SC == kScByte) {
+        sa[t] = (uint32_t)sab[4 * (lh * BM + row)] | ((uint32_t)sab[4 * ((2 + lh) * BM + row)] << 16);
+      } else {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(
+            sab + (SC == kScGroup ? row * 16 + P * 4 : row * 4));
+        sa[t] = w >> (8 * lh);
+      }
     }
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      const int row = wn_off + t * 16 + lr;
-      fb[t] = tb.codes[row * 4 + (lk ^ ((row >> 2) & 3))];
-      sb[t] = SDW ? reinterpret_cast<const uint8_t*>(tb.scales)[row * 4 + lk]
-                  : reinterpret_cast<const uint8_t*>(tb.scales)[4 * (lk * BN + row)];
+      const int row = wn_off + t * 32 + lr;
+      if constexpr (SC == kScByte) {
+        sb[t] = (uint32_t)sbb[4 * (lh * BN + row)] | ((uint32_t)sbb[4 * ((2 + lh) * BN + row)] << 16);
+      } else {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(
+            sbb + (SC == kScGroup ? row * 16 + P * 4 : row * 4));
+        sb[t] = w >> (8 * lh);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kb = 2 * h + lh;
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const int row = wm_off + t * 32 + lr;
+        fa[h][t] = ta.codes[row * 4 + (kb ^ ((row >> 2) & 3))];
+      }
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int row = wn_off + t * 32 + lr;
+        fb[h][t] = tb.codes[row * 4 + (kb ^ ((row >> 2) & 3))];
+      }
     }
     // refill the stage step kt-1 used (every wave is past its reads)
     using SN = std::integral_constant<int, (decltype(S)::value + 3) % 4>;
     if (kt + 3 < KT) issue(kt + 3, SN{});
-    if (kt == KT - 1 && lk >= tail_kb) {
-      // 32-blocks past K: zero A's codes, neutral scales on both sides
+    if (P == 0 && kt + 4 < KT) issue_scales((kt >> 2) + 1);  // the group after this one
+    if (kt == KT - 1) {
+      // 32-blocks past K: zero A's codes, neutral scales (127) on both sides
 #pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        fa[t] = make_uint4(0, 0, 0, 0);
-        sa[t] = 127;
+      for (int h = 0; h < 2; ++h) {
+        if (2 * h + lh >= tail_kb) {
+          const uint32_t keep = h ? 0x0000FFFFu : 0xFFFF0000u;
+          const uint32_t neutral = h ? 0x007F0000u : 0x0000007Fu;
+#pragma unroll
+          for (int t = 0; t < TM; ++t) {
+            fa[h][t] = make_uint4(0, 0, 0, 0);
+            sa[t] = (sa[t] & keep) | neutral;
+          }
+#pragma unroll
+          for (int t = 0; t < TN; ++t) sb[t] = (sb[t] & keep) | neutral;
+        }
       }
-#pragma unroll
-      for (int t = 0; t < TN; ++t) sb[t] = 127;
     }
 #pragma unroll
     for (int a = 0; a < TN; ++a)
 #pragma unroll
       for (int b = 0; b < TM; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            as_v8i(fb[a]), as_v8i(fa[b]), acc[a][b], kFmtFp4, kFmtFp4, 0, sb[a], 0, sa[b]);
+        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            as_v8i(fb[0][a]), as_v8i(fa[0][b]), acc[a][b], kFmtFp4, kFmtFp4, 0, (int)sb[a], 0,
+            (int)sa[b]);
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+      for (int b = 0; b < TM; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            as_v8i(fb[1][a]), as_v8i(fa[1][b]), acc[a][b], kFmtFp4, kFmtFp4, 2, (int)sb[a], 2,
+            (int)sa[b]);
   };
 
   for (int kt = 0; kt < KT; kt += 4) {
@@ -307,29 +391,33 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
     if (kt + 3 < KT) step(kt + 3, I3{});
   }
 
-  // ---- epilogue: lane holds D[n = 4 lk + v][m = lr] of each 16x16 tile
+  // ---- epilogue: lane holds D[n = 8 g + 4 lh + v][m = lr], g, v = 0..3, of each 32x32 tile
 #pragma unroll
   for (int b = 0; b < TM; ++b) {
-    const int mrow = wm_off + b * 16 + lr;
+    const int mrow = wm_off + b * 32 + lr;
     if (mrow >= rows_valid) continue;
     float* crow = C + (m0 + mrow) * ldc + n0;
 #pragma unroll
     for (int a = 0; a < TN; ++a) {
-      const int ncol = wn_off + a * 16 + lk * 4;
-      const v4f v = acc[a][b] * alpha;
-      if (ncol + 3 < cols_valid) {
-        *reinterpret_cast<float4*>(crow + ncol) = make_float4(v[0], v[1], v[2], v[3]);
-      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (ncol + e < cols_valid) crow[ncol + e] = v[e];
+      for (int gq = 0; gq < 4; ++gq) {
+        const int ncol = wn_off + a * 32 + gq * 8 + lh * 4;
+        const float v0 = acc[a][b][4 * gq] * alpha, v1 = acc[a][b][4 * gq + 1] * alpha;
+        const float v2 = acc[a][b][4 * gq + 2] * alpha, v3 = acc[a][b][4 * gq + 3] * alpha;
+        if (ncol + 3 < cols_valid) {
+          *reinterpret_cast<float4*>(crow + ncol) = make_float4(v0, v1, v2, v3);
+        } else {
+          if (ncol + 0 < cols_valid) crow[ncol + 0] = v0;
+          if (ncol + 1 < cols_valid) crow[ncol + 1] = v1;
+          if (ncol + 2 < cols_valid) crow[ncol + 2] = v2;
+        }
       }
     }
   }
 }
 
 // ---------------------------------------------------------------- host side
-template <int BM, int BN, int WM, int WN, bool SDW>
+template <int BM, int BN, int WM, int WN, int SC>
 static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                        const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha,
                        float* c, int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales,
@@ -346,7 +434,7 @@ static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
   gg.row_off[groups] = offs[groups];
   const int total = gg.tile_start[groups];
   if (total == 0) return MX_OK;
-  k_gemm_mx<BM, BN, WM, WN, 4, SDW><<<dim3(total), dim3(WM * WN * 64), 0, st>>>(
+  k_gemm_mx<BM, BN, WM, WN, 4, SC><<<dim3(total), dim3(WM * WN * 64), 0, st>>>(
       a, sa, b, sb, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, gg);
   return launch_status();
 }
@@ -358,14 +446,21 @@ int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8
               int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, hipStream_t st) {
   int64_t tiles256 = 0;
   for (int64_t g = 0; g < groups; ++g) tiles256 += cdiv(offs[g + 1] - offs[g], 256) * cdiv(N, 256);
-  const bool sdw = (K / 32) % 4 == 0 && (reinterpret_cast<uintptr_t>(sa) & 3u) == 0 &&
+  const bool al4 = (reinterpret_cast<uintptr_t>(sa) & 3u) == 0 &&
                    (reinterpret_cast<uintptr_t>(sb) & 3u) == 0 && b_stride_scales % 4 == 0;
+  const bool al16 = (reinterpret_cast<uintptr_t>(sa) & 15u) == 0 &&
+                    (reinterpret_cast<uintptr_t>(sb) & 15u) == 0 && b_stride_scales % 16 == 0;
+  const int sc = ((K / 32) % 16 == 0 && al16) ? kScGroup : (((K / 32) % 4 == 0 && al4) ? kScDword : kScByte);
   const bool big = tiles256 >= 512;
 #define MX_GEMM_ARGS a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, st
-  if (big) return sdw ? launch_gemm<256, 256, 2, 2, true>(MX_GEMM_ARGS)
-                      : launch_gemm<256, 256, 2, 2, false>(MX_GEMM_ARGS);
-  return sdw ? launch_gemm<128, 128, 2, 2, true>(MX_GEMM_ARGS)
-             : launch_gemm<128, 128, 2, 2, false>(MX_GEMM_ARGS);
+  if (big) {
+    if (sc == kScGroup) return launch_gemm<256, 256, 2, 2, kScGroup>(MX_GEMM_ARGS);
+    if (sc == kScDword) return launch_gemm<256, 256, 2, 2, kScDword>(MX_GEMM_ARGS);
+    return launch_gemm<256, 256, 2, 2, kScByte>(MX_GEMM_ARGS);
+  }
+  if (sc == kScGroup) return launch_gemm<128, 128, 2, 2, kScGroup>(MX_GEMM_ARGS);
+  if (sc == kScDword) return launch_gemm<128, 128, 2, 2, kScDword>(MX_GEMM_ARGS);
+  return launch_gemm<128, 128, 2, 2, kScByte>(MX_GEMM_ARGS);
 #undef MX_GEMM_ARGS
 }
 
