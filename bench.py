@@ -29,6 +29,23 @@ import numpy as np
 
 PEAK_HBM_GBPS = 8000.0
 PEAK_FP4_TFLOPS = 10100.0
+# HBM bytes per GEMM launch (mean of the fwd, dX and dW launches of the step),
+# from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB copy, valid for
+# the GEMM source with this sha256 only (the per-launch table is kept with the
+# committed profiles).
+GEMM_TRAFFIC = {"sha256": "bff6c0370dc90652edd013ecd1f58efbebcbe952034ef056a1c2a574c7927b1f",
+                "bytes_per_launch": 670795827}
+
+
+def gemm_traffic():
+    import hashlib
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                       "mxfp4_microscaling_quantization_amd", "csrc", "gemm.hip")
+    try:
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    return GEMM_TRAFFIC["bytes_per_launch"] if h == GEMM_TRAFFIC["sha256"] else None
 METRIC = "MXFP4 quantize GB/s + MXFP4 linear fwd+bwd TFLOP/s (%roofline), 1 MI355X"
 
 
@@ -40,6 +57,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parts", action="store_true", help="skip the quantizer sweep / MoE rows")
     p.add_argument("--only", default=None, help="run one part only: linear|sweep|moe|deosc")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device copy (known HBM bytes) for counter scaling")
     return p.parse_args()
 
 
@@ -277,6 +296,15 @@ def main():
 
     mx.lib()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 28  # 2^28 float32 = 1 GiB read + 1 GiB written per copy
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": 4 * n, "copies": 3}))
+        return
     parts = {}
     lin = None
     if args.only in (None, "linear"):
@@ -320,7 +348,7 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": {"kernel": "k_gemm_mx (MXFP4 GEMM, 2MNK per launch)", "bound": "mfma",
                      "achieved": round(ach, 2), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / PEAK_FP4_TFLOPS, 4), "traffic": None},
+                     "frac": round(ach / PEAK_FP4_TFLOPS, 4), "traffic": gemm_traffic()},
         "cpu_baseline": cpu,
         "quantize_GBps": {k: round(v["GBps"], 1) for k, v in
                           parts.get("quantizer_sweep_8192sq_bf16", {}).items()},
