@@ -5,23 +5,24 @@
 // (1x32) x (32x1) MXFP4 product of "Oscillation-Reduced MXFP4 Training for
 // Vision Transformers" (rebuttal, Question 2 (1) and (2)).
 //
-// Each V_MFMA_SCALE_F32_16X16X128_F8F6F4 multiplies a 16x128 FP4 tile by a
-// 128x16 FP4 tile and applies one E8M0 scale per 32 K-values of every row /
+// Each V_MFMA_SCALE_F32_32X32X64_F8F6F4 multiplies a 32x64 FP4 tile by a
+// 64x32 FP4 tile and applies one E8M0 scale per 32 K-values of every row /
 // column, so the block scales go straight to the instruction and the products
 // are exact; only the fp32 accumulation rounds.  Per lane, an operand is 16
-// bytes: row (lane % 16), K-values [32 (lane / 16), 32 (lane / 16) + 32), and
-// the scale operand is that row's byte for the same 32 K-values.
+// bytes: row (lane % 32), K-values [32 (lane / 32), 32 (lane / 32) + 32) of the
+// instruction's 64, and the scale operand holds that row's bytes (the scale
+// op_sel picks the byte).
 //
 // The instruction is fed B as its first operand and A as its second, so it
 // produces D[n][m]: a lane then holds 4 consecutive n of one output row m and
 // writes them with one 16-byte store.
 //
-// Tiling: a workgroup of WM x WN waves owns a BM x BN tile of C and walks K in
-// steps of 128 (64 code bytes per row).  Codes are staged in LDS as
-// [4 chunks of 32 K-values][rows][16 B], so the 16 lanes that read one chunk
-// read 256 contiguous bytes; scales as [4][rows] bytes.  Two LDS buffers: the
-// next step's global loads are issued before the current step's MFMAs and
-// written to the other buffer afterwards (one barrier per step).
+// Tiling: a workgroup of WM x WN waves owns a BM x BN tile of C (256 x 256 for
+// large problems: 128 x 128 per wave, 16 accumulator tiles) and walks K in
+// steps of 128 (64 code bytes per row) through a 4-stage LDS ring.  Direct
+// global-to-LDS loads fill a stage three steps ahead; each step reads the
+// second K-half's fragments while the first half's MFMAs run, and the next
+// step's first half while the second half's run, with one barrier per step.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -145,15 +146,11 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
   static_assert(QW * NW == (SC == kScByte ? 4 * QG : QG) && BM % 64 == 0 && BN % 64 == 0, "scale jobs");
   static_assert(STAGES == 4 && 2 * LC + QW < 64, "pipeline depth");
 
-  // One LDS object per stage, every access with a compile-time stage.
-  __shared__ StageLds<BM, BN, SC> s0, s1, s2, s3;
+  // The LDS ring (contiguous, reused by the epilogue); every access uses a
+  // compile-time stage index.
+  __shared__ StageLds<BM, BN, SC> ring[STAGES];
   __shared__ ScaleGroupLds<(SC == kScGroup ? BM : 1), (SC == kScGroup ? BN : 1)> sg[2];
-  auto stage = [&](auto S) -> StageLds<BM, BN, SC>& {
-    if constexpr (decltype(S)::value == 0) return s0;
-    else if constexpr (decltype(S)::value == 1) return s1;
-    else if constexpr (decltype(S)::value == 2) return s2;
-    else return s3;
-  };
+  auto stage = [&](auto S) -> StageLds<BM, BN, SC>& { return ring[decltype(S)::value]; };
   auto bufA = [&](auto S) -> TileLds<BM, SC>& { return stage(S).a; };
   auto bufB = [&](auto S) -> TileLds<BN, SC>& { return stage(S).b; };
 
@@ -285,32 +282,18 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
   if (1 < KT) issue(1, I1{});
   if (2 < KT) issue(2, I2{});
 
-  auto step = [&](int kt, auto S) {
-    constexpr int P = decltype(S)::value;  // kt % 4
-    // Wait for this step's loads; later loads already issued may stay in
-    // flight: the code loads of steps kt+1, kt+2 and, in group mode, the next
-    // scale group if it was issued after this step's codes (at step 4*(kt/4)).
-    const int ahead = min(KT - 1 - kt, STAGES - 2);
-    if (ahead >= 2) {
-      if (SC == kScGroup && P != 0 && kt + 4 - P < KT) wait_vmcnt<2 * LC + QW>();
-      else wait_vmcnt<2 * LC>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __builtin_amdgcn_s_barrier();  // every wave's loads landed; step kt-1's stage is free
+  // Fragment registers: f?[h] holds the lane's 16 code bytes for K-half h of
+  // the current step; s?c the current step's scale dwords, s?n the next one's.
+  uint4 fa[2][TM], fb[2][TN];
+  uint32_t sac[TM], sbc[TN];
 
-    const TileLds<BM, SC>& ta = bufA(S);
-    const TileLds<BN, SC>& tb = bufB(S);
+  // read scales of step kt (stage S) into sa/sb
+  auto read_scales = [&](int kt, auto S, uint32_t (&sa)[TM], uint32_t (&sb)[TN]) {
+    constexpr int P = decltype(S)::value;
     const uint8_t* sab = SC == kScGroup ? reinterpret_cast<const uint8_t*>(sg[(kt >> 2) & 1].a)
-                                        : reinterpret_cast<const uint8_t*>(ta.scales);
+                                        : reinterpret_cast<const uint8_t*>(bufA(S).scales);
     const uint8_t* sbb = SC == kScGroup ? reinterpret_cast<const uint8_t*>(sg[(kt >> 2) & 1].b)
-                                        : reinterpret_cast<const uint8_t*>(tb.scales);
-    // Two 64-wide K halves per step; the lane supplies 32-block kb = 2 h + lh of
-    // its row.  Scales: one dword per row holds the step's four blocks; shifted
-    // right by 8 lh, blocks lh and 2 + lh sit in bytes 0 and 2, which the MFMA
-    // selects with its scale op_sel (0 for the first half, 2 for the second).
-    uint4 fa[2][TM], fb[2][TN];
-    uint32_t sa[TM], sb[TN];
+                                        : reinterpret_cast<const uint8_t*>(bufB(S).scales);
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       const int row = wm_off + t * 32 + lr;
@@ -333,83 +316,199 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
         sb[t] = w >> (8 * lh);
       }
     }
+  };
+  auto read_frags = [&](int h, auto S) {
+    const TileLds<BM, SC>& ta = bufA(S);
+    const TileLds<BN, SC>& tb = bufB(S);
+    const int kb = 2 * h + lh;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kb = 2 * h + lh;
+    for (int t = 0; t < TM; ++t) {
+      const int row = wm_off + t * 32 + lr;
+      fa[h][t] = ta.codes[row * 4 + (kb ^ ((row >> 2) & 3))];
+    }
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const int row = wn_off + t * 32 + lr;
+      fb[h][t] = tb.codes[row * 4 + (kb ^ ((row >> 2) & 3))];
+    }
+  };
+  // 32-blocks past K in the last step: zero A's codes, neutral scales (127)
+  auto mask_tail = [&](int h, uint32_t (&sa)[TM], uint32_t (&sb)[TN]) {
+    if (2 * h + lh >= tail_kb) {
+      const uint32_t keep = h ? 0x0000FFFFu : 0xFFFF0000u;
+      const uint32_t neutral = h ? 0x007F0000u : 0x0000007Fu;
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
-        const int row = wm_off + t * 32 + lr;
-        fa[h][t] = ta.codes[row * 4 + (kb ^ ((row >> 2) & 3))];
+        fa[h][t] = make_uint4(0, 0, 0, 0);
+        sa[t] = (sa[t] & keep) | neutral;
       }
 #pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        const int row = wn_off + t * 32 + lr;
-        fb[h][t] = tb.codes[row * 4 + (kb ^ ((row >> 2) & 3))];
-      }
+      for (int t = 0; t < TN; ++t) sb[t] = (sb[t] & keep) | neutral;
     }
-    // refill the stage step kt-1 used (every wave is past its reads)
-    using SN = std::integral_constant<int, (decltype(S)::value + 3) % 4>;
-    if (kt + 3 < KT) issue(kt + 3, SN{});
-    if (P == 0 && kt + 4 < KT) issue_scales((kt >> 2) + 1);  // the group after this one
-    if (kt == KT - 1) {
-      // 32-blocks past K: zero A's codes, neutral scales (127) on both sides
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (2 * h + lh >= tail_kb) {
-          const uint32_t keep = h ? 0x0000FFFFu : 0xFFFF0000u;
-          const uint32_t neutral = h ? 0x007F0000u : 0x0000007Fu;
-#pragma unroll
-          for (int t = 0; t < TM; ++t) {
-            fa[h][t] = make_uint4(0, 0, 0, 0);
-            sa[t] = (sa[t] & keep) | neutral;
-          }
-#pragma unroll
-          for (int t = 0; t < TN; ++t) sb[t] = (sb[t] & keep) | neutral;
-        }
-      }
-    }
+  };
+  auto mfma_half = [&](auto H, const uint32_t (&sa)[TM], const uint32_t (&sb)[TN]) {
+    constexpr int h = decltype(H)::value;
 #pragma unroll
     for (int a = 0; a < TN; ++a)
 #pragma unroll
       for (int b = 0; b < TM; ++b)
         acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            as_v8i(fb[0][a]), as_v8i(fa[0][b]), acc[a][b], kFmtFp4, kFmtFp4, 0, (int)sb[a], 0,
-            (int)sa[b]);
-#pragma unroll
-    for (int a = 0; a < TN; ++a)
-#pragma unroll
-      for (int b = 0; b < TM; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            as_v8i(fb[1][a]), as_v8i(fa[1][b]), acc[a][b], kFmtFp4, kFmtFp4, 2, (int)sb[a], 2,
-            (int)sa[b]);
+            as_v8i(fb[h][a]), as_v8i(fa[h][b]), acc[a][b], kFmtFp4, kFmtFp4, h ? 2 : 0, (int)sb[a],
+            h ? 2 : 0, (int)sa[b]);
   };
 
-  for (int kt = 0; kt < KT; kt += 4) {
-    step(kt, I0{});
-    if (kt + 1 < KT) step(kt + 1, I1{});
-    if (kt + 2 < KT) step(kt + 2, I2{});
-    if (kt + 3 < KT) step(kt + 3, I3{});
+  // Barrier that also drains this wave's LDS reads, so a stage is never
+  // refilled while a read of it is in flight, whatever order the compiler
+  // gives the surrounding code.
+  auto barrier = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  // stage 0 (and scale group 0) landed for every wave
+  if (2 < KT) wait_vmcnt<2 * LC>();
+  else if (1 < KT) wait_vmcnt<LC>();
+  else wait_vmcnt<0>();
+  barrier();
+  read_scales(0, I0{}, sac, sbc);
+  read_frags(0, I0{});
+
+  // Step kt: read K-half 1 of stage kt; MFMAs of half 0; wait for stage kt+1
+  // and barrier (every wave is then also done with stage kt-1); refill stage
+  // kt-1 with step kt+3; read half 0 and the scales of step kt+1; MFMAs of
+  // half 1.  LDS reads thus overlap the other half's MFMAs.  FULL steps have
+  // kt + 7 < KT rounded down to a multiple of 4: every load is issued and no
+  // K tail, so the step is straight-line code the scheduler keeps in order.
+  auto step = [&](int kt, auto S, auto FULL) {
+    constexpr int P = decltype(S)::value;  // kt % 4
+    constexpr bool F = decltype(FULL)::value;
+    using SN1 = std::integral_constant<int, (P + 1) % 4>;
+    using SN3 = std::integral_constant<int, (P + 3) % 4>;
+    // vector-memory instructions issued after step kt+1's loads may stay in
+    // flight at the barrier: step kt+2's loads and, in group mode, a scale
+    // group issued at step kt-2 (before them) or kt-1 (after them)
+    constexpr int G2 = (SC == kScGroup && P == 2) ? QW : 0;
+    constexpr int G1 = (SC == kScGroup && P == 1) ? QW : 0;
+    uint32_t san[TM], sbn[TN];
+    read_frags(1, S);
+    if (!F && kt == KT - 1) mask_tail(0, sac, sbc);
+    mfma_half(I0{}, sac, sbc);
+    if constexpr (F) {
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<LC + G1 + G2>();
+      barrier();
+      issue(kt + 3, SN3{});
+      if (P == 0) issue_scales((kt >> 2) + 1);
+      read_scales(kt + 1, SN1{}, san, sbn);
+      read_frags(0, SN1{});
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(I1{}, sac, sbc);
+#pragma unroll
+      for (int t = 0; t < TM; ++t) sac[t] = san[t];
+#pragma unroll
+      for (int t = 0; t < TN; ++t) sbc[t] = sbn[t];
+    } else {
+      if (kt + 1 < KT) {
+        if (kt + 3 < KT) wait_vmcnt<LC + G1 + G2>();
+        else if (kt + 2 < KT) wait_vmcnt<LC + G2>();
+        else wait_vmcnt<0>();
+        barrier();
+        if (kt + 3 < KT) issue(kt + 3, SN3{});
+        if (P == 0 && kt + 4 < KT) issue_scales((kt >> 2) + 1);
+        read_scales(kt + 1, SN1{}, san, sbn);
+      }
+      if (kt == KT - 1) mask_tail(1, sac, sbc);
+      mfma_half(I1{}, sac, sbc);
+      if (kt + 1 < KT) {
+        read_frags(0, SN1{});
+#pragma unroll
+        for (int t = 0; t < TM; ++t) sac[t] = san[t];
+#pragma unroll
+        for (int t = 0; t < TN; ++t) sbc[t] = sbn[t];
+      }
+    }
+  };
+
+  using Full = std::true_type;
+  using Part = std::false_type;
+  int kt = 0;
+  for (; kt + 7 < KT; kt += 4) {
+    step(kt, I0{}, Full{});
+    step(kt + 1, I1{}, Full{});
+    step(kt + 2, I2{}, Full{});
+    step(kt + 3, I3{}, Full{});
+  }
+  for (; kt < KT; kt += 4) {
+    step(kt, I0{}, Part{});
+    if (kt + 1 < KT) step(kt + 1, I1{}, Part{});
+    if (kt + 2 < KT) step(kt + 2, I2{}, Part{});
+    if (kt + 3 < KT) step(kt + 3, I3{}, Part{});
   }
 
   // ---- epilogue: lane holds D[n = 8 g + 4 lh + v][m = lr], g, v = 0..3, of each 32x32 tile
+  if constexpr (TM == 4 && TN == 4) {
+    // The LDS ring is idle now: each wave stages its 128 x 128 sub-tile there
+    // in two passes of 64 rows (32 KB per wave; row pitch 512 B, 16-byte chunk
+    // index XORed with row & 15, so the 16-row writes and the row reads are
+    // free of bank conflicts) and reads it back so that every store
+    // instruction writes two whole 512-byte row segments of C.
+    static_assert(sizeof(ring) >= 4 * 32768, "staging space");
+    __syncthreads();  // every wave is done reading the ring
+    char* stg = reinterpret_cast<char*>(ring) + wave * 32768;
 #pragma unroll
-  for (int b = 0; b < TM; ++b) {
-    const int mrow = wm_off + b * 32 + lr;
-    if (mrow >= rows_valid) continue;
-    float* crow = C + (m0 + mrow) * ldc + n0;
+    for (int p = 0; p < 2; ++p) {
 #pragma unroll
-    for (int a = 0; a < TN; ++a) {
+      for (int bb = 0; bb < 2; ++bb) {
+        const int b = 2 * p + bb;
+        const int rl = bb * 32 + lr;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int ncol = wn_off + a * 32 + gq * 8 + lh * 4;
-        const float v0 = acc[a][b][4 * gq] * alpha, v1 = acc[a][b][4 * gq + 1] * alpha;
-        const float v2 = acc[a][b][4 * gq + 2] * alpha, v3 = acc[a][b][4 * gq + 3] * alpha;
-        if (ncol + 3 < cols_valid) {
-          *reinterpret_cast<float4*>(crow + ncol) = make_float4(v0, v1, v2, v3);
-        } else {
-          if (ncol + 0 < cols_valid) crow[ncol + 0] = v0;
-          if (ncol + 1 < cols_valid) crow[ncol + 1] = v1;
-          if (ncol + 2 < cols_valid) crow[ncol + 2] = v2;
+        for (int a = 0; a < TN; ++a)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int ch = a * 8 + gq * 2 + lh;
+            *reinterpret_cast<float4*>(stg + rl * 512 + ((ch ^ (rl & 15)) * 16)) =
+                make_float4(acc[a][b][4 * gq] * alpha, acc[a][b][4 * gq + 1] * alpha,
+                            acc[a][b][4 * gq + 2] * alpha, acc[a][b][4 * gq + 3] * alpha);
+          }
+      }
+#pragma unroll 4
+      for (int it = 0; it < 32; ++it) {
+        const int rl = it * 2 + (lane >> 5), ch = lane & 31;
+        const float4 v =
+            *reinterpret_cast<const float4*>(stg + rl * 512 + ((ch ^ (rl & 15)) * 16));
+        const int mrow = wm_off + p * 64 + rl;
+        const int ncol = wn_off + ch * 4;
+        if (mrow < rows_valid) {
+          float* crow = C + (m0 + mrow) * ldc + n0;
+          if (ncol + 3 < cols_valid) {
+            *reinterpret_cast<float4*>(crow + ncol) = v;
+          } else {
+            if (ncol + 0 < cols_valid) crow[ncol + 0] = v.x;
+            if (ncol + 1 < cols_valid) crow[ncol + 1] = v.y;
+            if (ncol + 2 < cols_valid) crow[ncol + 2] = v.z;
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < TM; ++b) {
+      const int mrow = wm_off + b * 32 + lr;
+      if (mrow >= rows_valid) continue;
+      float* crow = C + (m0 + mrow) * ldc + n0;
+#pragma unroll
+      for (int a = 0; a < TN; ++a) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int ncol = wn_off + a * 32 + gq * 8 + lh * 4;
+          const float v0 = acc[a][b][4 * gq] * alpha, v1 = acc[a][b][4 * gq + 1] * alpha;
+          const float v2 = acc[a][b][4 * gq + 2] * alpha, v3 = acc[a][b][4 * gq + 3] * alpha;
+          if (ncol + 3 < cols_valid) {
+            *reinterpret_cast<float4*>(crow + ncol) = make_float4(v0, v1, v2, v3);
+          } else {
+            if (ncol + 0 < cols_valid) crow[ncol + 0] = v0;
+            if (ncol + 1 < cols_valid) crow[ncol + 1] = v1;
+            if (ncol + 2 < cols_valid) crow[ncol + 2] = v2;
+          }
         }
       }
     }

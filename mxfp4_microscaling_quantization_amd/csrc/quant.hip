@@ -64,40 +64,59 @@ __device__ __forceinline__ uint32_t quant8(const float v[8], uint32_t byte, uint
   return packed;
 }
 
+// A workgroup takes 64 x kRowU consecutive blocks per iteration; its quad j
+// handles blocks base + 64 u + j, u < kRowU, whose loads are all issued before
+// any of them is quantized (more bytes in flight per lane).
+constexpr int kRowU = 4;
+
 template <typename T, int ROUND, bool HAD>
 __global__ __launch_bounds__(256) void k_quant_row(const T* __restrict__ x, int64_t nblk,
                                                    uint64_t seed, uint32_t sign_mask,
                                                    uint32_t* __restrict__ codes,
                                                    uint8_t* __restrict__ scales) {
   const int q = threadIdx.x & 3;
-  const int64_t stride = (int64_t)gridDim.x * (blockDim.x >> 2);
-  for (int64_t b = (int64_t)blockIdx.x * (blockDim.x >> 2) + (threadIdx.x >> 2); b < nblk;
-       b += stride) {
-    float v[8];
-    load8<T>(x + b * 32 + q * 8, v);
-    if (HAD) {
+  const int j = threadIdx.x >> 2;
+  for (int64_t base = (int64_t)blockIdx.x * 64 * kRowU; base < nblk;
+       base += (int64_t)gridDim.x * 64 * kRowU) {
+    float v[kRowU][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = apply_sign(v[i], sign_mask, q * 8 + i);
-      fwht32_quad(v, q);
+    for (int u = 0; u < kRowU; ++u) {
+      // unconditional (clamped) loads, so that all of them are in flight at once
+      const int64_t b = min(base + u * 64 + j, nblk - 1);
+      load8<T>(x + b * 32 + q * 8, v[u]);
     }
-    uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
-    m = quad_max_u32(m);
-    const uint32_t byte = scale_byte_of(m);
-    codes[b * 4 + q] = quant8<ROUND>(v, byte, seed, (uint64_t)b * 32 + q * 8);
-    if (q == 0) scales[b] = (uint8_t)byte;
+    for (int u = 0; u < kRowU; ++u) {
+      const int64_t b = base + u * 64 + j;
+      if (b >= nblk) break;  // quads past the end: whole quads, so the DPP partners agree
+      if (HAD) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[u][i] = apply_sign(v[u][i], sign_mask, q * 8 + i);
+        fwht32_quad(v[u], q);
+      }
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[u][i]) & 0x7FFFFFFFu);
+      m = quad_max_u32(m);
+      const uint32_t byte = scale_byte_of(m);
+      codes[b * 4 + q] = quant8<ROUND>(v[u], byte, seed, (uint64_t)b * 32 + q * 8);
+      if (q == 0) scales[b] = (uint8_t)byte;
+    }
   }
 }
 
 // ============================================================== column blocks
-// A workgroup owns a tile of 256 rows (8 row blocks) x 64 columns, staged in
-// LDS in the input type.  Thread (c, g) quantizes column c for row blocks
-// 2g, 2g+1 from LDS (consecutive lanes read consecutive columns of one row),
-// and the codes go through a second LDS buffer so that each output row
-// (= input column) is written as 128 contiguous bytes.
-constexpr int kColTileR = 256;
-constexpr int kColTileC = 64;
+// A workgroup owns a tile of kTileR = 128 rows x 256 bytes of input (128 bf16
+// or 64 f32 columns).  Each thread loads 8 chunks of 16 bytes (coalesced) and
+// writes them to LDS.  Column pass: thread (p, rb) reads one dword per row of
+// row block rb (the column pair 2p, 2p+1 of bf16, or column p of f32; the 64
+// lanes of a wave read 64 consecutive dwords) and quantizes those 32x1
+// blocks; their codes are staged so that each output row (= input column) gets
+// 64 contiguous bytes per tile.  With ROW set (dual quantization) the chunks
+// are also quantized as 1x32 blocks straight from registers: the 32 / E lanes
+// holding one row block are adjacent, E = elements per chunk.
+constexpr int kTileR = 128;
+constexpr int kTileRowBytes = 256;
 
 // Quantize 32 values of one column block; returns the 16 code bytes as uint4.
 template <int ROUND>
@@ -133,135 +152,205 @@ __device__ __forceinline__ uint4 quant_col32(float v[32], uint32_t& byte_out, ui
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Writes the staged codes/scales of a column tile: out row (col0 + c) gets
-// bytes [row0/2, row0/2 + nrb*16) of codes and [row0/32, row0/32 + nrb) of scales.
+// Writes staged column-block codes/scales: output row (col0 + c) gets bytes
+// [row0/2, row0/2 + 16 nrb) of codes and [row0/32, row0/32 + nrb) of scales,
+// for c < ncols; staging layout [c][rb], NRB row blocks per column.
+template <int NC, int NRB>
 __device__ __forceinline__ void store_col_tile(const uint4* s_codes, const uint8_t* s_scales,
                                                int64_t rows, int64_t col0, int ncols, int64_t row0,
                                                int nrb, uint8_t* __restrict__ codes,
                                                uint8_t* __restrict__ scales) {
   const int64_t ld_c = rows / 2, ld_s = rows / 32;
-  for (int i = threadIdx.x; i < kColTileC * 8; i += blockDim.x) {
-    const int c = i >> 3, rb = i & 7;
+  for (int i = threadIdx.x; i < NC * NRB; i += blockDim.x) {
+    const int c = i / NRB, rb = i % NRB;
     if (c < ncols && rb < nrb) {
-      *reinterpret_cast<uint4*>(codes + (col0 + c) * ld_c + row0 / 2 + rb * 16) = s_codes[c * 8 + rb];
-      scales[(col0 + c) * ld_s + row0 / 32 + rb] = s_scales[c * 8 + rb];
+      *reinterpret_cast<uint4*>(codes + (col0 + c) * ld_c + row0 / 2 + rb * 16) = s_codes[i];
+      scales[(col0 + c) * ld_s + row0 / 32 + rb] = s_scales[i];
     }
   }
 }
 
-template <typename T, int ROUND, bool HAD>
-__global__ __launch_bounds__(256) void k_quant_col(const T* __restrict__ x, int64_t rows,
-                                                   int64_t cols, uint64_t seed, uint32_t sign_mask,
-                                                   uint8_t* __restrict__ codes,
-                                                   uint8_t* __restrict__ scales) {
-  __shared__ T s_in[kColTileR * kColTileC];
-  __shared__ uint4 s_codes[kColTileC * 8];
-  __shared__ uint8_t s_scales[kColTileC * 8];
+// max over the 32 / E adjacent lanes that hold one row block
+template <int E>
+__device__ __forceinline__ uint32_t rowblock_max_u32(uint32_t m) {
+  m = quad_max_u32(m);
+  if constexpr (E == 4) m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+  return m;
+}
 
-  const int64_t col0 = (int64_t)blockIdx.x * kColTileC;
-  const int64_t row0 = (int64_t)blockIdx.y * kColTileR;
-  const int ncols = (int)min<int64_t>(kColTileC, cols - col0);
-  const int nrows = (int)min<int64_t>(kColTileR, rows - row0);
+template <typename T, int ROUND, bool ROW, bool HAD>
+__global__ __launch_bounds__(256) void k_quant_tile(
+    const T* __restrict__ x, int64_t rows, int64_t cols, uint64_t seed_row, uint64_t seed_col,
+    uint32_t sign_mask, uint8_t* __restrict__ codes_row, uint8_t* __restrict__ scales_row,
+    uint8_t* __restrict__ codes_col, uint8_t* __restrict__ scales_col) {
+  constexpr int E = 16 / sizeof(T);               // elements per 16-byte chunk
+  constexpr int TC = kTileRowBytes / sizeof(T);   // tile columns
+  constexpr int CPR = kTileRowBytes / 16;         // chunks per tile row (16)
+  constexpr int CPT = 4 / sizeof(T);              // columns per thread in the column pass
+  constexpr int NRB = kTileR / 32;                // row blocks per tile (4)
+  constexpr int NLOAD = kTileR * CPR / 256;       // chunks per thread (8)
+  __shared__ uint32_t s_in[kTileR * kTileRowBytes / 4];
+  __shared__ uint4 s_codes[TC * NRB];
+  __shared__ uint8_t s_scales[TC * NRB];
+
+  const int64_t col0 = (int64_t)blockIdx.x * TC;
+  const int64_t row0 = (int64_t)blockIdx.y * kTileR;
+  const int ncols = (int)min<int64_t>(TC, cols - col0);
+  const int nrows = (int)min<int64_t>(kTileR, rows - row0);
   const int nrb = nrows / 32;
+  const int tid = threadIdx.x;
 
-  // global -> LDS, 16-byte chunks (cols % 8 == 0, so chunks never straddle the edge)
-  constexpr int kPerChunk = 16 / sizeof(T);
-  constexpr int kChunksPerRow = kColTileC / kPerChunk;
-  for (int i = threadIdx.x; i < kColTileR * kChunksPerRow; i += blockDim.x) {
-    const int r = i / kChunksPerRow, ch = i % kChunksPerRow;
-    if (r < nrows && ch * kPerChunk < ncols) {
-      *reinterpret_cast<uint4*>(&s_in[r * kColTileC + ch * kPerChunk]) =
-          *reinterpret_cast<const uint4*>(x + (row0 + r) * cols + col0 + ch * kPerChunk);
-    }
+  // ---- load: chunk (r, c) = (j * 16 + tid / 16, tid % 16)
+  const int lc = tid % CPR;
+  uint4 ch[NLOAD];
+#pragma unroll
+  for (int j = 0; j < NLOAD; ++j) {
+    const int r = j * (256 / CPR) + tid / CPR;
+    ch[j] = make_uint4(0, 0, 0, 0);
+    if (r < nrows && lc * E < ncols)
+      ch[j] = *reinterpret_cast<const uint4*>(x + (row0 + r) * cols + col0 + lc * E);
   }
-  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NLOAD; ++j) {
+    const int r = j * (256 / CPR) + tid / CPR;
+    *reinterpret_cast<uint4*>(&s_in[r * (kTileRowBytes / 4) + lc * 4]) = ch[j];
+  }
 
-  const int c = threadIdx.x & 63;
-  const int g = threadIdx.x >> 6;
+  // ---- row pass (1x32 blocks) from registers
+  if constexpr (ROW) {
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int rb = g * 2 + k;
-    if (rb < nrb && c < ncols) {
-      float v[32];
+    for (int j = 0; j < NLOAD; ++j) {
+      const int r = j * (256 / CPR) + tid / CPR;
+      if (r >= nrows || lc * E >= ncols) continue;  // whole row blocks drop out together
+      float v[E];
+      const uint32_t w[4] = {ch[j].x, ch[j].y, ch[j].z, ch[j].w};
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const T e = s_in[(rb * 32 + i) * kColTileC + c];
-        if constexpr (sizeof(T) == 2) {
-          v[i] = __uint_as_float((uint32_t)e << 16);
-        } else {
-          v[i] = e;
+      for (int i = 0; i < E; ++i) {
+        if constexpr (sizeof(T) == 2) v[i] = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+        else v[i] = __uint_as_float(w[i]);
+      }
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < E; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+      m = rowblock_max_u32<E>(m);
+      const uint32_t byte = scale_byte_of(m);
+      const uint64_t idx0 = (uint64_t)(row0 + r) * (uint64_t)cols + (uint64_t)(col0 + lc * E);
+      uint32_t packed = 0;
+      if (byte != 255u) {
+        const float inv = inv_scale_of(byte);
+        uint64_t z = ROUND == MX_SR ? sm64_state(seed_row, idx0) : 0;
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const float a = fabsf(v[i]) * inv;
+          uint32_t c;
+          if (ROUND == MX_SR) {
+            c = e2m1_sr(a, sm64_top24(z));
+            z += kGamma;
+          } else {
+            c = e2m1_rne(a);
+          }
+          c |= (__float_as_uint(v[i]) >> 28) & 8u;
+          packed |= c << (4 * i);
         }
       }
-      if (HAD) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = apply_sign(v[i], sign_mask, i);
-        fwht32_lane(v);
-      }
-      uint32_t byte;
-      const uint64_t idx0 = (uint64_t)(row0 + rb * 32) * (uint64_t)cols + (uint64_t)(col0 + c);
-      s_codes[c * 8 + rb] = quant_col32<ROUND>(v, byte, seed, idx0, (uint64_t)cols);
-      s_scales[c * 8 + rb] = (uint8_t)byte;
+      if constexpr (E == 8) reinterpret_cast<uint32_t*>(codes_row)[idx0 / 8] = packed;
+      else reinterpret_cast<uint16_t*>(codes_row)[idx0 / 4] = (uint16_t)packed;
+      if (lc % (32 / E) == 0) scales_row[idx0 / 32] = (uint8_t)byte;
     }
   }
   __syncthreads();
-  store_col_tile(s_codes, s_scales, rows, col0, ncols, row0, nrb, codes, scales);
+
+  // ---- column pass (32x1 blocks) from LDS
+  {
+    const int p = tid % 64, rb = tid / 64;
+    if (rb < nrb && p * CPT < ncols) {
+      uint32_t raw[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) raw[i] = s_in[(rb * 32 + i) * (kTileRowBytes / 4) + p];
+#pragma unroll
+      for (int cc = 0; cc < CPT; ++cc) {
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          if constexpr (sizeof(T) == 2) v[i] = cc ? bf16_hi(raw[i]) : bf16_lo(raw[i]);
+          else v[i] = __uint_as_float(raw[i]);
+        }
+        if (HAD) {
+#pragma unroll
+          for (int i = 0; i < 32; ++i) v[i] = apply_sign(v[i], sign_mask, i);
+          fwht32_lane(v);
+        }
+        const int c = p * CPT + cc;
+        uint32_t byte;
+        const uint64_t idx0 = (uint64_t)(row0 + rb * 32) * (uint64_t)cols + (uint64_t)(col0 + c);
+        s_codes[c * NRB + rb] = quant_col32<ROUND>(v, byte, seed_col, idx0, (uint64_t)cols);
+        s_scales[c * NRB + rb] = (uint8_t)byte;
+      }
+    }
+  }
+  __syncthreads();
+  store_col_tile<TC, NRB>(s_codes, s_scales, rows, col0, ncols, row0, nrb, codes_col, scales_col);
 }
 
 // ============================================================== double quantization
 // Input: packed row-blocked [rows, cols] (codes [rows][cols/2], scales
-// [rows][cols/32]).  A workgroup stages 256 rows x 64 columns of codes (32 B
-// per row) and their 2 scale bytes per row, decodes each column's 32 values
-// exactly and quantizes them as a 32x1 block (output transposed).
+// [rows][cols/32]).  A workgroup owns 256 rows x 128 columns; thread (o, rb)
+// takes the 4 columns 4o .. 4o+3 (two code bytes per row, read straight from
+// global memory: the 32 lanes of a half-wave read 64 contiguous bytes of one
+// row) over row block rb, decodes each value exactly (E2M1 magnitude times
+// 2^(scale - 127); a 0xFF input scale makes the whole column block NaN) and
+// quantizes the four 32x1 blocks.  Codes are staged for 128-byte row stores.
+constexpr int kRqR = 256;
+constexpr int kRqC = 128;
+
 template <int ROUND>
 __global__ __launch_bounds__(256) void k_requant(const uint8_t* __restrict__ codes_in,
                                                  const uint8_t* __restrict__ scales_in,
                                                  int64_t rows, int64_t cols, uint64_t seed,
                                                  uint8_t* __restrict__ codes,
                                                  uint8_t* __restrict__ scales) {
-  __shared__ uint4 s_in[kColTileR * 2];          // 256 rows x 32 bytes
-  __shared__ uint8_t s_sc[kColTileR * 2];        // 256 rows x 2 scale bytes
-  __shared__ uint4 s_codes[kColTileC * 8];
-  __shared__ uint8_t s_scales[kColTileC * 8];
+  constexpr int NRB = kRqR / 32;
+  __shared__ uint4 s_codes[kRqC * NRB];
+  __shared__ uint8_t s_scales[kRqC * NRB];
 
-  const int64_t col0 = (int64_t)blockIdx.x * kColTileC;
-  const int64_t row0 = (int64_t)blockIdx.y * kColTileR;
-  const int ncols = (int)min<int64_t>(kColTileC, cols - col0);   // multiple of 32
-  const int nrows = (int)min<int64_t>(kColTileR, rows - row0);
+  const int64_t col0 = (int64_t)blockIdx.x * kRqC;
+  const int64_t row0 = (int64_t)blockIdx.y * kRqR;
+  const int ncols = (int)min<int64_t>(kRqC, cols - col0);   // multiple of 32
+  const int nrows = (int)min<int64_t>(kRqR, rows - row0);
   const int nrb = nrows / 32;
   const int64_t ld_in = cols / 2, ld_sin = cols / 32;
+  const int o = threadIdx.x % 32, rb = threadIdx.x / 32;
 
-  for (int i = threadIdx.x; i < kColTileR * 2; i += blockDim.x) {
-    const int r = i >> 1, ch = i & 1;
-    if (r < nrows && ch * 32 < ncols) {
-      s_in[i] = *reinterpret_cast<const uint4*>(codes_in + (row0 + r) * ld_in + col0 / 2 + ch * 16);
-      s_sc[i] = scales_in[(row0 + r) * ld_sin + col0 / 32 + ch];
-    }
-  }
-  __syncthreads();
-
-  const int c = threadIdx.x & 63;
-  const int g = threadIdx.x >> 6;
-  const uint8_t* s_bytes = reinterpret_cast<const uint8_t*>(s_in);
+  if (rb < nrb && o * 4 < ncols) {
+    const int64_t c0 = col0 + o * 4;
+    const uint8_t* cp = codes_in + (row0 + rb * 32) * ld_in + c0 / 2;
+    const uint8_t* sp = scales_in + (row0 + rb * 32) * ld_sin + c0 / 32;
+    uint32_t cw[32], sw[32];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int rb = g * 2 + k;
-    if (rb < nrb && c < ncols) {
+    for (int i = 0; i < 32; ++i) {
+      cw[i] = *reinterpret_cast<const uint16_t*>(cp + i * ld_in);
+      sw[i] = sp[i * ld_sin];
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
       float v[32];
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        const int r = rb * 32 + i;
-        const uint32_t byte = s_bytes[r * 32 + (c >> 1)];
-        const uint32_t code = (c & 1) ? (byte >> 4) : (byte & 15u);
-        v[i] = e2m1_decode(code, s_sc[r * 2 + (c >> 5)]);
+        const uint32_t code = (cw[i] >> (4 * cc)) & 15u;
+        const uint32_t twice = (0xC8643210u >> ((code & 7u) * 4u)) & 0xFu;  // 2 |value|
+        const float mag = __builtin_amdgcn_ldexpf((float)twice, (int)sw[i] - 128);
+        const float sv = __uint_as_float(__float_as_uint(mag) | ((code & 8u) << 28));
+        v[i] = sw[i] == 255u ? __uint_as_float(0x7FC00000u) : sv;
       }
-      uint32_t sb;
+      uint32_t byte;
+      const int c = o * 4 + cc;
       const uint64_t idx0 = (uint64_t)(row0 + rb * 32) * (uint64_t)cols + (uint64_t)(col0 + c);
-      s_codes[c * 8 + rb] = quant_col32<ROUND>(v, sb, seed, idx0, (uint64_t)cols);
-      s_scales[c * 8 + rb] = (uint8_t)sb;
+      s_codes[c * NRB + rb] = quant_col32<ROUND>(v, byte, seed, idx0, (uint64_t)cols);
+      s_scales[c * NRB + rb] = (uint8_t)byte;
     }
   }
   __syncthreads();
-  store_col_tile(s_codes, s_scales, rows, col0, ncols, row0, nrb, codes, scales);
+  store_col_tile<kRqC, NRB>(s_codes, s_scales, rows, col0, ncols, row0, nrb, codes, scales);
 }
 
 // ============================================================== dequantization
@@ -345,8 +434,12 @@ __global__ __launch_bounds__(256) void k_dequant_col(const uint8_t* __restrict__
 }
 
 // ============================================================== launchers
+static int grid_for_row(int64_t nblk) {
+  // 64 kRowU blocks per 256-thread workgroup and iteration; at most 64 workgroups per CU
+  const int64_t g = cdiv(nblk, 64 * kRowU);
+  return (int)hmin(g, 256 * 64);
+}
 static int grid_for_blocks(int64_t nblk) {
-  // 64 blocks per 256-thread workgroup; cap so that each thread loops a few times
   const int64_t g = cdiv(nblk, 64);
   return (int)hmin(g, 256 * 32);
 }
@@ -356,7 +449,7 @@ static int launch_quant_row(const T* x, int64_t rows, int64_t cols, int round, u
                             int had, uint32_t mask, uint8_t* codes, uint8_t* scales,
                             hipStream_t st) {
   const int64_t nblk = rows * cols / 32;
-  const dim3 grid(grid_for_blocks(nblk)), block(256);
+  const dim3 grid(grid_for_row(nblk)), block(256);
   uint32_t* c32 = reinterpret_cast<uint32_t*>(codes);
   if (round == MX_RNE) {
     if (had) k_quant_row<T, MX_RNE, true><<<grid, block, 0, st>>>(x, nblk, seed, mask, c32, scales);
@@ -368,18 +461,23 @@ static int launch_quant_row(const T* x, int64_t rows, int64_t cols, int round, u
   return launch_status();
 }
 
-template <typename T>
-static int launch_quant_col(const T* x, int64_t rows, int64_t cols, int round, uint64_t seed,
-                            int had, uint32_t mask, uint8_t* codes, uint8_t* scales,
-                            hipStream_t st) {
-  const dim3 grid((unsigned)cdiv(cols, kColTileC), (unsigned)cdiv(rows, kColTileR)), block(256);
+// Column blocks (ROW = false) or both block shapes from one read (ROW = true).
+template <typename T, bool ROW>
+static int launch_quant_tile(const T* x, int64_t rows, int64_t cols, int round, uint64_t seed_row,
+                             uint64_t seed_col, int had, uint32_t mask, uint8_t* codes_row,
+                             uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
+                             hipStream_t st) {
+  constexpr int TC = kTileRowBytes / sizeof(T);
+  const dim3 grid((unsigned)cdiv(cols, TC), (unsigned)cdiv(rows, kTileR)), block(256);
+#define MX_TILE_ARGS x, rows, cols, seed_row, seed_col, mask, codes_row, scales_row, codes_col, scales_col
   if (round == MX_RNE) {
-    if (had) k_quant_col<T, MX_RNE, true><<<grid, block, 0, st>>>(x, rows, cols, seed, mask, codes, scales);
-    else k_quant_col<T, MX_RNE, false><<<grid, block, 0, st>>>(x, rows, cols, seed, mask, codes, scales);
+    if (had) k_quant_tile<T, MX_RNE, ROW, true><<<grid, block, 0, st>>>(MX_TILE_ARGS);
+    else k_quant_tile<T, MX_RNE, ROW, false><<<grid, block, 0, st>>>(MX_TILE_ARGS);
   } else {
-    if (had) k_quant_col<T, MX_SR, true><<<grid, block, 0, st>>>(x, rows, cols, seed, mask, codes, scales);
-    else k_quant_col<T, MX_SR, false><<<grid, block, 0, st>>>(x, rows, cols, seed, mask, codes, scales);
+    if (had) k_quant_tile<T, MX_SR, ROW, true><<<grid, block, 0, st>>>(MX_TILE_ARGS);
+    else k_quant_tile<T, MX_SR, ROW, false><<<grid, block, 0, st>>>(MX_TILE_ARGS);
   }
+#undef MX_TILE_ARGS
   return launch_status();
 }
 
@@ -395,16 +493,17 @@ int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, int axis
                                   codes, scales, st);
   }
   return dtype == MX_BF16
-             ? launch_quant_col(static_cast<const uint16_t*>(x), rows, cols, round, seed, had, mask,
-                                codes, scales, st)
-             : launch_quant_col(static_cast<const float*>(x), rows, cols, round, seed, had, mask,
-                                codes, scales, st);
+             ? launch_quant_tile<uint16_t, false>(static_cast<const uint16_t*>(x), rows, cols, round,
+                                                  0, seed, had, mask, nullptr, nullptr, codes,
+                                                  scales, st)
+             : launch_quant_tile<float, false>(static_cast<const float*>(x), rows, cols, round, 0,
+                                               seed, had, mask, nullptr, nullptr, codes, scales, st);
 }
 
 int requantize_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows, int64_t cols,
                     int round, uint64_t seed, uint8_t* codes, uint8_t* scales, hipStream_t st) {
   if (rows == 0 || cols == 0) return MX_OK;
-  const dim3 grid((unsigned)cdiv(cols, kColTileC), (unsigned)cdiv(rows, kColTileR)), block(256);
+  const dim3 grid((unsigned)cdiv(cols, kRqC), (unsigned)cdiv(rows, kRqR)), block(256);
   if (round == MX_RNE)
     k_requant<MX_RNE><<<grid, block, 0, st>>>(codes_in, scales_in, rows, cols, seed, codes, scales);
   else
@@ -416,11 +515,14 @@ int quantize_dual_impl(const void* x, int dtype, int64_t rows, int64_t cols, int
                        uint64_t seed_row, uint64_t seed_col, uint8_t* codes_row,
                        uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
                        hipStream_t st) {
-  const int s = quantize_impl(x, dtype, rows, cols, MX_ROW, round, seed_row, 0, 0, codes_row,
-                              scales_row, st);
-  if (s != MX_OK) return s;
-  return quantize_impl(x, dtype, rows, cols, MX_COL, round, seed_col, 0, 0, codes_col, scales_col,
-                       st);
+  if (rows == 0 || cols == 0) return MX_OK;
+  return dtype == MX_BF16
+             ? launch_quant_tile<uint16_t, true>(static_cast<const uint16_t*>(x), rows, cols, round,
+                                                 seed_row, seed_col, 0, 0, codes_row, scales_row,
+                                                 codes_col, scales_col, st)
+             : launch_quant_tile<float, true>(static_cast<const float*>(x), rows, cols, round,
+                                              seed_row, seed_col, 0, 0, codes_row, scales_row,
+                                              codes_col, scales_col, st);
 }
 
 }  // namespace mx
