@@ -110,16 +110,20 @@ def bench_linear(torch, mx, synth, dev, steps, warmup, seed=3):
     T = Timer(torch, st)
     BF = mx.MX_BF16
 
-    def step(timer):
-        timer.run("quant_x", lambda: mx.mx_quantize(x, BF, M, K, mx.MX_ROW, mx.MX_RNE, 0, 0, 0, *xq, st))
-        timer.run("quant_w", lambda: mx.mx_quantize(w, BF, N, K, mx.MX_ROW, mx.MX_RNE, 0, 0, 0, *wq, st))
-        timer.run("gemm", lambda: mx.mx_gemm(*xq, *wq, M, N, K, 1.0, y, N, st))
-        timer.run("dual_dy", lambda: mx.mx_quantize_dual(dy, BF, M, N, mx.MX_SR, seed + 3, seed + 5,
-                                                        *q3, *q5, st))
-        timer.run("requant_w", lambda: mx.mx_requantize(*wq, N, K, mx.MX_SR, seed + 4, *q4, st))
-        timer.run("requant_x", lambda: mx.mx_requantize(*xq, M, K, mx.MX_SR, seed + 6, *q6, st))
-        timer.run("gemm", lambda: mx.mx_gemm(*q3, *q4, M, K, N, 1.0, dx, K, st))
-        timer.run("gemm", lambda: mx.mx_gemm(*q5, *q6, N, K, M, 1.0, dw, K, st))
+    def step(timer, timed=("gemm",)):
+        """One linear fwd+bwd.  Only the kernels named in `timed` get event pairs
+        (an event record between kernels costs a few microseconds)."""
+        def run(name, fn):
+            (timer.run(name, fn) if name in timed else fn())
+        run("quant_x", lambda: mx.mx_quantize(x, BF, M, K, mx.MX_ROW, mx.MX_RNE, 0, 0, 0, *xq, st))
+        run("quant_w", lambda: mx.mx_quantize(w, BF, N, K, mx.MX_ROW, mx.MX_RNE, 0, 0, 0, *wq, st))
+        run("gemm", lambda: mx.mx_gemm(*xq, *wq, M, N, K, 1.0, y, N, st))
+        run("dual_dy", lambda: mx.mx_quantize_dual(dy, BF, M, N, mx.MX_SR, seed + 3, seed + 5,
+                                                  *q3, *q5, st))
+        run("requant_w", lambda: mx.mx_requantize(*wq, N, K, mx.MX_SR, seed + 4, *q4, st))
+        run("requant_x", lambda: mx.mx_requantize(*xq, M, K, mx.MX_SR, seed + 6, *q6, st))
+        run("gemm", lambda: mx.mx_gemm(*q3, *q4, M, K, N, 1.0, dx, K, st))
+        run("gemm", lambda: mx.mx_gemm(*q5, *q6, N, K, M, 1.0, dw, K, st))
 
     warm = Timer(torch, st)
     for _ in range(warmup):
@@ -144,7 +148,13 @@ def bench_linear(torch, mx, synth, dev, steps, warmup, seed=3):
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / steps
     flops = 6.0 * M * N * K
-    kern = {k: T.mean_ms(k) for k in T.pairs}
+    # per-kernel breakdown of the quantizers: a separate pass with every kernel timed
+    B = Timer(torch, st)
+    for _ in range(5):
+        step(B, timed=("quant_x", "quant_w", "dual_dy", "requant_w", "requant_x", "gemm"))
+    torch.cuda.synchronize()
+    kern = {k: B.mean_ms(k) for k in B.pairs}
+    kern["gemm"] = T.mean_ms("gemm")  # the GEMM launches of the timed region itself
     gemm_ms = kern["gemm"]
     gemm_tf = 2.0 * M * N * K / (gemm_ms * 1e-3) / 1e12
     bytes_q = {

@@ -45,6 +45,14 @@ struct GemmGroups {
   int64_t row_off[MX_MAX_GROUPS + 1];       // rows of A / C per group
 };
 
+// Split-K: split s of n covers K-values [s kchunk, min((s + 1) kchunk, K)) and
+// writes its partial sums to C + s c_stride (alpha applied per split).
+struct GemmSplit {
+  int n;
+  int64_t kchunk;    // multiple of 512
+  int64_t c_stride;  // elements between the splits' outputs
+};
+
 constexpr int kGroupM = 4;  // tile rows walked together (L2 reuse of B tiles)
 
 __device__ __forceinline__ v8i as_v8i(uint4 u) {
@@ -133,7 +141,7 @@ template <int BM, int BN, int WM, int WN, int STAGES, int SC>
 __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, int64_t N, int64_t K, float alpha, float* __restrict__ C,
-    int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, GemmGroups gg) {
+    int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, GemmGroups gg, GemmSplit sp) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32;  // 32-row MFMA tiles per wave along m
   constexpr int TN = BN / WN / 32;  // along n
@@ -156,12 +164,15 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
 
   // ---- which tile: spread consecutive logical tiles over one XCD (workgroups
   // are dealt round-robin to the 8 XCDs), then walk kGroupM tile rows at a time.
-  const int total = gg.tile_start[gg.ngroups];
+  const int tiles = gg.tile_start[gg.ngroups];
+  const int total = tiles * sp.n;
   int id = blockIdx.x;
   {
     const int q = total / 8, r = total % 8, x = id % 8;
     id = x * q + min(x, r) + id / 8;
   }
+  const int split = id / tiles;
+  id -= split * tiles;
   int g = 0;
   while (g + 1 < gg.ngroups && gg.tile_start[g + 1] <= id) ++g;
   const int lt = id - gg.tile_start[g];
@@ -184,8 +195,12 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
 
   const int64_t ldk = K / 2;   // code bytes per row
   const int64_t lds = K / 32;  // scale bytes (32-blocks) per row
-  const int KT = (int)((K + 127) / 128);
-  const int tail_kb = (int)(lds - (int64_t)(KT - 1) * 4);  // valid 32-blocks in the last step
+  const int64_t k0 = split * sp.kchunk;
+  const int64_t kc_len = lmin(sp.kchunk, K - k0);  // K-values of this split
+  const int64_t kc_bytes = kc_len / 2, kc_blocks = kc_len / 32;
+  const int KT = (int)((kc_len + 127) / 128);
+  const int tail_kb = (int)(kc_blocks - (int64_t)(KT - 1) * 4);  // valid 32-blocks in the last step
+  C += split * sp.c_stride;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -204,12 +219,12 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
 #pragma unroll
   for (int j = 0; j < LA; ++j) {
     const int64_t row = lmin(m0 + (wave * LA + j) * 16 + dr, a_last);
-    a_src[j] = A + row * ldk + dc * 16;
+    a_src[j] = A + row * ldk + k0 / 2 + dc * 16;
   }
 #pragma unroll
   for (int j = 0; j < LB; ++j) {
     const int64_t row = lmin(n0 + (wave * LB + j) * 16 + dr, N - 1);
-    b_src[j] = Bg + row * ldk + dc * 16;
+    b_src[j] = Bg + row * ldk + k0 / 2 + dc * 16;
   }
   // scale jobs: job q covers 64 rows (lane = row) of A (q % QG < BM/64) or B,
   // for all 32-blocks of a step (dword), of four steps (group) or for 32-block
@@ -223,7 +238,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
     const bool isA = grp < BM / 64;
     const int r0 = (isA ? grp : grp - BM / 64) * 64;
     const int64_t row = isA ? lmin(m0 + r0 + lane, a_last) : lmin(n0 + r0 + lane, N - 1);
-    s_src[j] = (isA ? SA : SBg) + row * lds + kb;
+    s_src[j] = (isA ? SA : SBg) + row * lds + k0 / 32 + kb;
     s_dst[j] = (SC == kScByte ? kb * (isA ? BM : BN) + r0 : r0) + (isA ? 0 : (1 << 20));
   }
 
@@ -233,7 +248,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
     TileLds<BM, SC>& ta = bufA(S);
     TileLds<BN, SC>& tb = bufB(S);
     const int64_t kc = (int64_t)kt * 64;
-    const int64_t coff = lmin(kc, lmax(ldk - 16 - dc * 16, -dc * 16));
+    const int64_t coff = lmin(kc, lmax(kc_bytes - 16 - dc * 16, -dc * 16));
 #pragma unroll
     for (int j = 0; j < LA; ++j) dma16(a_src[j] + coff, &ta.codes[((wave * LA + j) * 16) * 4]);
 #pragma unroll
@@ -247,7 +262,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
           dma4(s_src[j] + (int64_t)kt * 4, dst);
         } else {
           const int kb = (wave * QW + j) / QG;
-          dma1(s_src[j] + lmin((int64_t)kt * 4, lds - 1 - kb), dst);
+          dma1(s_src[j] + lmin((int64_t)kt * 4, kc_blocks - 1 - kb), dst);
         }
       }
     }
@@ -520,7 +535,7 @@ template <int BM, int BN, int WM, int WN, int SC>
 static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                        const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha,
                        float* c, int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales,
-                       hipStream_t st) {
+                       GemmSplit sp, hipStream_t st) {
   GemmGroups gg;
   gg.ngroups = (int)groups;
   gg.tiles_n = (int)cdiv(N, BN);
@@ -533,16 +548,17 @@ static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
   gg.row_off[groups] = offs[groups];
   const int total = gg.tile_start[groups];
   if (total == 0) return MX_OK;
-  k_gemm_mx<BM, BN, WM, WN, 4, SC><<<dim3(total), dim3(WM * WN * 64), 0, st>>>(
-      a, sa, b, sb, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, gg);
+  k_gemm_mx<BM, BN, WM, WN, 4, SC><<<dim3(total * sp.n), dim3(WM * WN * 64), 0, st>>>(
+      a, sa, b, sb, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, gg, sp);
   return launch_status();
 }
 
 // Large tiles when they still give every CU a few tiles, else smaller ones;
 // scale rows go by dword loads when every scale row starts 4-byte aligned.
-int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
-              const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha, float* c,
-              int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, hipStream_t st) {
+static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
+                       const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha,
+                       float* c, int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales,
+                       GemmSplit sp, hipStream_t st) {
   int64_t tiles256 = 0;
   for (int64_t g = 0; g < groups; ++g) tiles256 += cdiv(offs[g + 1] - offs[g], 256) * cdiv(N, 256);
   const bool al4 = (reinterpret_cast<uintptr_t>(sa) & 3u) == 0 &&
@@ -550,8 +566,8 @@ int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8
   const bool al16 = (reinterpret_cast<uintptr_t>(sa) & 15u) == 0 &&
                     (reinterpret_cast<uintptr_t>(sb) & 15u) == 0 && b_stride_scales % 16 == 0;
   const int sc = ((K / 32) % 16 == 0 && al16) ? kScGroup : (((K / 32) % 4 == 0 && al4) ? kScDword : kScByte);
-  const bool big = tiles256 >= 512;
-#define MX_GEMM_ARGS a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, st
+  const bool big = tiles256 * sp.n >= 512;
+#define MX_GEMM_ARGS a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, sp, st
   if (big) {
     if (sc == kScGroup) return launch_gemm<256, 256, 2, 2, kScGroup>(MX_GEMM_ARGS);
     if (sc == kScDword) return launch_gemm<256, 256, 2, 2, kScDword>(MX_GEMM_ARGS);
@@ -561,6 +577,66 @@ int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8
   if (sc == kScDword) return launch_gemm<128, 128, 2, 2, kScDword>(MX_GEMM_ARGS);
   return launch_gemm<128, 128, 2, 2, kScByte>(MX_GEMM_ARGS);
 #undef MX_GEMM_ARGS
+}
+
+int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
+              const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha, float* c,
+              int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, hipStream_t st) {
+  const GemmSplit one = {1, K, 0};
+  return gemm_launch(a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes,
+                     b_stride_scales, one, st);
+}
+
+// ---------------------------------------------------------------- split-K
+// When an M x N output gives the CUs too few 128 x 128 tiles, the contraction
+// is cut into chunks (multiples of 512, at least 1024 long) whose partial sums
+// go to a caller workspace and are added in split order by a second kernel,
+// so the result does not depend on timing.
+SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K) {
+  SplitPlan p = {1, K};
+  const int64_t tiles128 = cdiv(M, 128) * cdiv(N, 128);
+  if (cdiv(M, 256) * cdiv(N, 256) >= 512 || tiles128 >= 256 || K < 2048) return p;
+  int64_t n = hmin(cdiv(512, tiles128), K / 1024);
+  if (n < 2) return p;
+  const int64_t chunk = cdiv(cdiv(K, n), 512) * 512;
+  n = cdiv(K, chunk);
+  if (n < 2) return p;
+  p.n = (int)n;
+  p.kchunk = chunk;
+  return p;
+}
+
+__global__ __launch_bounds__(256) void k_splitk_sum(const float4* __restrict__ part, int n,
+                                                    int64_t rows, int64_t cols4, float alpha,
+                                                    float* __restrict__ c, int64_t ldc) {
+  const int64_t total = rows * cols4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float4 s = part[i];
+    for (int k = 1; k < n; ++k) {
+      const float4 v = part[k * total + i];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    const int64_t r = i / cols4, q = i % cols4;
+    *reinterpret_cast<float4*>(c + r * ldc + q * 4) =
+        make_float4(s.x * alpha, s.y * alpha, s.z * alpha, s.w * alpha);
+  }
+}
+
+// C[M][N] (ldc) = alpha * A . B^T with the plan's splits; part: plan.n * M * N
+// floats of workspace (16-byte aligned); N % 4 == 0.
+int gemm_split_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
+                    int64_t M, int64_t N, int64_t K, float alpha, float* c, int64_t ldc,
+                    SplitPlan plan, float* part, hipStream_t st) {
+  const int64_t offs[2] = {0, M};
+  if (plan.n <= 1) return gemm_impl(a, sa, b, sb, offs, 1, N, K, alpha, c, ldc, 0, 0, st);
+  const GemmSplit sp = {plan.n, plan.kchunk, M * N};
+  int s = gemm_launch(a, sa, b, sb, offs, 1, N, K, 1.0f, part, N, 0, 0, sp, st);
+  if (s != MX_OK) return s;
+  const int64_t n4 = M * (N / 4);
+  k_splitk_sum<<<dim3((unsigned)hmin(cdiv(n4, 256), 4096)), dim3(256), 0, st>>>(
+      reinterpret_cast<const float4*>(part), plan.n, M, N / 4, alpha, c, ldc);
+  return launch_status();
 }
 
 }  // namespace mx

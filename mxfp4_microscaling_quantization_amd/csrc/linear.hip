@@ -6,7 +6,10 @@
 //             dW = Q_S^(5)(dY)^T . Q_S^(6)(Q_D^(1)(X))   (contraction over M)
 // Q^(4) and Q^(6) are the double quantizations that give the 32x1 group shape
 // the backward products need; quantizer q draws its stochastic rounding from
-// seed + q.  All launches go to the caller's stream in order.
+// seed + q.  A backward product whose output has too few tiles for the chip
+// (a short, wide contraction such as dW of a ViT MLP) is split along its
+// contraction into the workspace.  All launches go to the caller's stream in
+// order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -25,12 +28,19 @@ int requantize_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t r
 int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
               const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha, float* c,
               int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, hipStream_t st);
+SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K);
+int gemm_split_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
+                    int64_t M, int64_t N, int64_t K, float alpha, float* c, int64_t ldc,
+                    SplitPlan plan, float* part, hipStream_t st);
 
 static size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Workspace layout: four packed operands, each codes then scales, 256-byte aligned.
+// Workspace layout: four packed operands, each codes then scales, then the
+// split-K partial sums of the dX / dW products when they are split (shared:
+// the two products run one after the other), all 256-byte aligned.
 struct BwdLayout {
-  size_t q3c, q3s, q4c, q4s, q5c, q5s, q6c, q6s, total;
+  size_t q3c, q3s, q4c, q4s, q5c, q5s, q6c, q6s, part, total;
+  SplitPlan dx, dw;
 };
 
 static BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K) {
@@ -45,6 +55,11 @@ static BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K) {
   L.q4c = take((size_t)K * N / 2);  L.q4s = take((size_t)K * N / 32);   // W^T blocks [K][N]
   L.q5c = take((size_t)N * M / 2);  L.q5s = take((size_t)N * M / 32);   // dY^T      [N][M]
   L.q6c = take((size_t)K * M / 2);  L.q6s = take((size_t)K * M / 32);   // X^T blocks [K][M]
+  L.dx = gemm_split_plan(M, K, N);   // dX [M][K], contraction over N
+  L.dw = gemm_split_plan(N, K, M);   // dW [N][K], contraction over M
+  const size_t px = L.dx.n > 1 ? (size_t)L.dx.n * M * K * 4 : 0;
+  const size_t pw = L.dw.n > 1 ? (size_t)L.dw.n * N * K * 4 : 0;
+  L.part = take(px > pw ? px : pw);
   L.total = o;
   return L;
 }
@@ -105,13 +120,12 @@ extern "C" int mx_linear_bwd(const void* dy, int dtype, int64_t M, int64_t N, in
   if (s != MX_OK) return s;
   s = requantize_impl(xq_codes, xq_scales, M, K, MX_SR, seed + 6, ws + L.q6c, ws + L.q6s, st);
   if (s != MX_OK) return s;
-  const int64_t offs_dx[2] = {0, M};
-  s = gemm_impl(ws + L.q3c, ws + L.q3s, ws + L.q4c, ws + L.q4s, offs_dx, 1, K, N, 1.0f, dx, K, 0,
-                0, st);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  s = gemm_split_impl(ws + L.q3c, ws + L.q3s, ws + L.q4c, ws + L.q4s, M, K, N, 1.0f, dx, K, L.dx,
+                      part, st);
   if (s != MX_OK) return s;
-  const int64_t offs_dw[2] = {0, N};
-  return gemm_impl(ws + L.q5c, ws + L.q5s, ws + L.q6c, ws + L.q6s, offs_dw, 1, K, M, 1.0f, dw, K,
-                   0, 0, st);
+  return gemm_split_impl(ws + L.q5c, ws + L.q5s, ws + L.q6c, ws + L.q6s, N, K, M, 1.0f, dw, K,
+                         L.dw, part, st);
 }
 
 extern "C" const char* mx_status_string(int status) {

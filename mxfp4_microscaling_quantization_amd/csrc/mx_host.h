@@ -18,6 +18,12 @@ inline int launch_status() {
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Split-K plan of a GEMM: n chunks of kchunk K-values (the last may be shorter).
+struct SplitPlan {
+  int n;
+  int64_t kchunk;
+};
 inline int64_t hmin(int64_t a, int64_t b) { return a < b ? a : b; }
 
 }  // namespace mx

@@ -63,6 +63,19 @@ def test_linear_small_f32():
     check_linear(cfg, "f32", seed=11)
 
 
+def test_linear_bwd_split_contraction_with_ragged_last_chunk():
+    """dW [256, 128] contracts over M = 3104: too few output tiles, so the product is split
+    along M (chunks of 1536, 1536 and 32) into the workspace; every output checked."""
+    rng = np.random.default_rng(21)
+    M, N, K = 3104, 256, 128
+    assert mx.mx_linear_bwd_workspace_size(M, N, K) > 3 * N * K * 4  # partial sums included
+    b16 = synth.f32_to_bf16_bits
+    cfg = {"x": b16(rng.standard_normal((M, K)).astype(np.float32)),
+           "w": b16((rng.standard_normal((N, K)) * 0.02).astype(np.float32)),
+           "dy": b16((rng.standard_normal((M, N)) * 1e-3).astype(np.float32)), "M": M, "N": N, "K": K}
+    check_linear(cfg, "bf16", seed=5)
+
+
 def test_linear_deit_fc1_full():
     """DeiT-S fc1, X [12608, 384], W [1536, 384], dY [12608, 1536] bf16: every output checked."""
     check_linear(synth.deit_config(), "bf16", seed=1)
