@@ -25,6 +25,9 @@ What it computes, and where each step comes from:
 * Weight de-oscillation -- ALTO page, sections "How does ALTO detect and fix
   oscillating weights?" and the ratio paragraph (window P = 200, d_w, d_Q,
   threshold 4.0, snap to the current bin centre).
+* Q-EMA -- the TetraJet rebuttal (Question 4; the overhead and hyperparameter
+  answers): the forward pass quantizes an exponential moving average of the
+  weights, decay beta = 0.998 by default.
 
 Readings taken where the pages are silent (each is also listed in the design
 notes): ties round to the even code; values above 6 saturate to 6; the sign bit
@@ -56,7 +59,8 @@ __all__ = [
     "shared_exponent", "quantize_blocks", "pack_codes", "unpack_codes",
     "quantize", "dequantize", "requantize", "block_indices",
     "gemm", "gemm_abs", "gemm_grouped", "linear_fwd", "linear_bwd",
-    "bin_value_f32", "deosc_init", "deosc_step", "bf16_bits_to_f32",
+    "bin_value_f32", "deosc_init", "deosc_step", "deosc_step_quantized", "qema_step",
+    "bf16_bits_to_f32",
 ]
 
 # OCP MX E2M1 magnitudes, indexed by the 3 low bits of a code.
@@ -395,6 +399,42 @@ def deosc_step(w, w_prev, d_w, d_q, end_of_window: bool, threshold: float = 4.0)
         d_q = np.zeros_like(w)
         flags = flag.astype(np.uint8)
     return w, w_prev, d_w, d_q, flags
+
+
+def deosc_step_quantized(w, w_prev, d_w, d_q, end_of_window: bool, threshold: float = 4.0):
+    """De-oscillation step that also returns the next forward's weight operand:
+    deosc_step, then Q_D of the updated weight (1x32 RNE along the columns).
+    The ALTO page runs its post-step hook and the next forward's weight
+    quantization as separate passes; this is the same result from one pass.
+
+    Returns (w, w_prev, d_w, d_q, flags or None, codes, scales).
+    """
+    w, w_prev, d_w, d_q, flags = deosc_step(w, w_prev, d_w, d_q, end_of_window, threshold)
+    codes, scales = quantize(w, ROW, RNE)
+    return w, w_prev, d_w, d_q, flags, codes, scales
+
+
+# ---------------------------------------------------------------- Q-EMA
+def qema_step(w, ema, beta: float = 0.998):
+    """Q-EMA post-step update ("Oscillation-Reduced MXFP4 Training for Vision
+    Transformers", rebuttal: Question 4 -- one extra EMA copy per linear layer's
+    weight; the overhead answer -- the EMA is updated when the parameters are
+    and is what the forward pass quantizes; the hyperparameter answer -- decay
+    beta, 0.998 by default).  The pages give no formula; the plain exponential
+    moving average is taken, in float32 in this order:
+
+      ema = (beta * ema) + ((1 - beta) * w),   1 - beta rounded to float32 first
+
+    Returns (ema, codes, scales): the new EMA and its Q_D (1x32 RNE along the
+    columns), the weight operand of the next forward.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    ema = np.asarray(ema, dtype=np.float32)
+    b = np.float32(beta)
+    omb = np.float32(np.float32(1.0) - b)
+    ema = ((b * ema).astype(np.float32) + (omb * w).astype(np.float32)).astype(np.float32)
+    codes, scales = quantize(ema, ROW, RNE)
+    return ema, codes, scales
 
 
 # ---------------------------------------------------------------- helpers
