@@ -266,6 +266,31 @@ def bench_moe(torch, mx, synth, dev, iters=10, deosc_steps=20):
                          "frac_hbm": 28.0 * n / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
     ms_end = T.mean_ms("end")
     res["deosc_window_end"] = {"us": ms_end * 1e3, "GBps": 33.0 * n / (ms_end * 1e-3) / 1e9}
+    # the same pass emitting the next forward's Q_D(W) (+0.53125 B/elem), against the
+    # two-pass alternative (de-oscillation, then a 4.53125 B/elem weight quantization)
+    wc = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    ws = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+    T = Timer(torch, st)
+    for t in range(deosc_steps + 1, deosc_steps + 11):
+        mx.mx_synth_step(w, rows * cols, 4, t, st)
+        T.run("fused", lambda: mx.mx_deosc_step_quantize(w, rows, cols, wp, dw_, dq_, False, 4.0,
+                                                         flags, wc, ws, st))
+        T.run("quant", lambda: mx.mx_quantize(w, mx.MX_F32, rows, cols, mx.MX_ROW, mx.MX_RNE, 0, 0, 0,
+                                              wc, ws, st))
+    torch.cuda.synchronize()
+    ms_f, ms_q = T.mean_ms("fused"), T.mean_ms("quant")
+    res["deosc_step_quantize"] = {"us": ms_f * 1e3, "GBps": 28.53125 * n / (ms_f * 1e-3) / 1e9,
+                                  "frac_hbm": 28.53125 * n / (ms_f * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                                  "two_pass_us": (ms + ms_q) * 1e3}
+    # Q-EMA: read w and the EMA, write the EMA and its Q_D (12.53125 B/elem)
+    ema = w.clone()
+    T = Timer(torch, st)
+    for t in range(10):
+        T.run("qema", lambda: mx.mx_qema_step(w, ema, rows, cols, 0.998, wc, ws, st))
+    torch.cuda.synchronize()
+    ms_e = T.mean_ms("qema")
+    res["qema_step"] = {"us": ms_e * 1e3, "GBps": 12.53125 * n / (ms_e * 1e-3) / 1e9,
+                        "frac_hbm": 12.53125 * n / (ms_e * 1e-3) / 1e9 / PEAK_HBM_GBPS}
     return res
 
 

@@ -215,6 +215,31 @@ int mx_deosc_init(const float* w, int64_t rows, int64_t cols,
 int mx_deosc_step(float* w, int64_t rows, int64_t cols, float* w_prev, float* d_w, float* d_q,
                   int end_of_window, float threshold, uint8_t* flags, void* stream);
 
+/* mx_deosc_step_quantize: mx_deosc_step, and in the same pass the next forward's
+ * weight operand Q_D(w) of the updated w (1x32 blocks along cols, nearest
+ * rounding), written to wq_codes [rows][cols/2] and wq_scales [rows][cols/32]
+ * (caller-owned device memory; wq_codes 16-byte aligned) -- bit-identical to
+ * mx_quantize(w, MX_F32, rows, cols, MX_ROW, MX_RNE, ...) after the step.  The
+ * ALTO page runs the hook and the forward's weight quantization separately;
+ * snapping to the bin value keeps every code and scale, so one pass gives both.
+ * Arguments and errors otherwise as mx_deosc_step. */
+int mx_deosc_step_quantize(float* w, int64_t rows, int64_t cols, float* w_prev, float* d_w,
+                           float* d_q, int end_of_window, float threshold, uint8_t* flags,
+                           uint8_t* wq_codes, uint8_t* wq_scales, void* stream);
+
+/* mx_qema_step: Q-EMA post-step update ("Oscillation-Reduced MXFP4 Training for
+ * Vision Transformers", rebuttal: Question 4 -- one EMA copy per linear weight;
+ * the overhead answer -- it is updated with the parameters and it is what the
+ * forward quantizes; the hyperparameter answer -- beta 0.998 by default).  In
+ * float32, in this order:  ema = (beta * ema) + ((1 - beta) * w), 1 - beta
+ * rounded to float32 first; then wq_codes / wq_scales = Q_D(ema) (1x32 blocks
+ * along cols, nearest rounding), the next forward's weight operand.
+ * w [rows][cols] float32 (read), ema [rows][cols] float32 (updated in place;
+ * the caller starts it as a copy of w).  cols % 32 == 0; w, ema, wq_codes
+ * 16-byte aligned device memory owned by the caller. */
+int mx_qema_step(const float* w, float* ema, int64_t rows, int64_t cols, float beta,
+                 uint8_t* wq_codes, uint8_t* wq_scales, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

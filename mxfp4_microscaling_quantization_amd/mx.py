@@ -39,6 +39,8 @@ SIGNATURES = {
     "mx_linear_bwd": ([_P, _i32, _i64, _i64, _i64, _P, _P, _P, _P, _u64, _P, _P, _P, _sz, _P], _i32),
     "mx_deosc_init": ([_P, _i64, _i64, _P, _P, _P, _P], _i32),
     "mx_deosc_step": ([_P, _i64, _i64, _P, _P, _P, _i32, _f32, _P, _P], _i32),
+    "mx_deosc_step_quantize": ([_P, _i64, _i64, _P, _P, _P, _i32, _f32, _P, _P, _P, _P], _i32),
+    "mx_qema_step": ([_P, _P, _i64, _i64, _f32, _P, _P, _P], _i32),
     "mx_synth_step": ([_P, _i64, _u64, _i64, _P], _i32),
 }
 
@@ -168,6 +170,19 @@ def mx_deosc_step(w, rows, cols, w_prev, d_w, d_q, end_of_window, threshold, fla
     _check("mx_deosc_step", lib().mx_deosc_step(_ptr(w), rows, cols, _ptr(w_prev), _ptr(d_w),
                                                 _ptr(d_q), int(end_of_window), threshold,
                                                 _ptr(flags), _stream(stream)))
+
+
+def mx_deosc_step_quantize(w, rows, cols, w_prev, d_w, d_q, end_of_window, threshold, flags,
+                           wq_codes, wq_scales, stream=None):
+    _check("mx_deosc_step_quantize",
+           lib().mx_deosc_step_quantize(_ptr(w), rows, cols, _ptr(w_prev), _ptr(d_w), _ptr(d_q),
+                                        int(end_of_window), threshold, _ptr(flags),
+                                        _ptr(wq_codes), _ptr(wq_scales), _stream(stream)))
+
+
+def mx_qema_step(w, ema, rows, cols, beta, wq_codes, wq_scales, stream=None):
+    _check("mx_qema_step", lib().mx_qema_step(_ptr(w), _ptr(ema), rows, cols, beta,
+                                              _ptr(wq_codes), _ptr(wq_scales), _stream(stream)))
 
 
 def mx_synth_step(w, n, seed, step, stream=None):

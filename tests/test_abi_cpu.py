@@ -118,6 +118,19 @@ def test_deosc_validation(L):
     assert L.mx_deosc_step(GOOD, 4, 32, GOOD, GOOD, GOOD, 2, 4.0, GOOD, None) == mx.MX_ERR_ENUM
     assert L.mx_deosc_step(GOOD, 4, 32, BAD, GOOD, GOOD, 0, 4.0, None, None) == mx.MX_ERR_ALIGN
     assert L.mx_deosc_init(GOOD, 4, 32, GOOD, None, GOOD, None) == mx.MX_ERR_NULL
+    q = L.mx_deosc_step_quantize
+    assert q(GOOD, 4, 40, GOOD, GOOD, GOOD, 0, 4.0, None, GOOD, GOOD, None) == mx.MX_ERR_SHAPE
+    assert q(GOOD, 4, 32, GOOD, GOOD, GOOD, 0, 4.0, None, None, GOOD, None) == mx.MX_ERR_NULL
+    assert q(GOOD, 4, 32, GOOD, GOOD, GOOD, 1, 4.0, None, GOOD, GOOD, None) == mx.MX_ERR_NULL
+    assert q(GOOD, 4, 32, GOOD, GOOD, GOOD, 3, 4.0, GOOD, GOOD, GOOD, None) == mx.MX_ERR_ENUM
+    assert q(GOOD, 4, 32, GOOD, GOOD, GOOD, 0, 4.0, None, BAD, GOOD, None) == mx.MX_ERR_ALIGN
+    assert q(GOOD, 0, 32, None, None, None, 0, 4.0, None, None, None, None) == mx.MX_OK
+    e = L.mx_qema_step
+    assert e(GOOD, GOOD, 4, 48, 0.998, GOOD, GOOD, None) == mx.MX_ERR_SHAPE
+    assert e(GOOD, None, 4, 32, 0.998, GOOD, GOOD, None) == mx.MX_ERR_NULL
+    assert e(GOOD, GOOD, 4, 32, 0.998, GOOD, None, None) == mx.MX_ERR_NULL
+    assert e(BAD, GOOD, 4, 32, 0.998, GOOD, GOOD, None) == mx.MX_ERR_ALIGN
+    assert e(None, None, 4, 0, 0.998, None, None, None) == mx.MX_OK
     assert L.mx_synth_step(GOOD, 1 << 41, 0, 1, None) == mx.MX_ERR_SHAPE
     assert L.mx_synth_step(BAD, 16, 0, 1, None) == mx.MX_ERR_ALIGN
 

@@ -170,6 +170,65 @@ def test_deosc_window_matches_oracle(thr):
         assert_bytes_equal(g.view(np.uint32), o.view(np.uint32), name)
 
 
+@pytest.mark.parametrize("thr", [4.0, 1.0])
+def test_deosc_step_quantize_matches_oracle(thr):
+    """The fused pass: every state array and flag as mx_deosc_step, plus Q_D of the new
+    weight on every step (including the window end, where elements are snapped)."""
+    rng = np.random.default_rng(6)
+    w0 = (rng.standard_normal((96, 352)) * 0.02).astype(np.float32)
+    w0[5, 64:96] = 0.0
+    rows, cols = w0.shape
+    steps, seed = 40, 7
+    w = to_dev_f32(w0)
+    st = [torch.empty_like(w) for _ in range(3)]
+    flags = torch.full((rows, cols), 7, dtype=torch.uint8, device=DEV)
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=DEV)
+    mx.mx_deosc_init(w, rows, cols, *st)
+    ow = w0.copy()
+    ost = list(O.deosc_init(ow))
+    idx = np.arange(ow.size).reshape(ow.shape)
+    for t in range(1, steps + 1):
+        end = t == steps
+        mx.mx_synth_step(w, rows * cols, seed, t)
+        mx.mx_deosc_step_quantize(w, rows, cols, *st, end, thr, flags, codes, scales)
+        ow = (ow + synth.deosc_delta_f32(seed, t, idx)).astype(np.float32)
+        ow, *ost, of, oc, os_ = O.deosc_step_quantized(ow, *ost, end, thr)
+        if t % 13 == 0 or end:
+            assert_bytes_equal(host(codes), oc, f"codes step {t}")
+            assert_bytes_equal(host(scales), os_, f"scales step {t}")
+    assert of.sum() > 0
+    assert_bytes_equal(host(flags), of, "flags")
+    assert_bytes_equal(host(w).view(np.uint32), ow.view(np.uint32), "w")
+    for g, o, name in zip(st, ost, ["w_prev", "d_w", "d_q"]):
+        assert_bytes_equal(host(g).view(np.uint32), o.view(np.uint32), name)
+    # the emitted operand is what the forward quantizer makes of the new weight
+    fc, fs = mx.quantize(w)
+    assert torch.equal(fc, codes) and torch.equal(fs, scales)
+
+
+def test_qema_step_matches_oracle():
+    rng = np.random.default_rng(7)
+    rows, cols = 80, 224
+    w0 = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    w0[7, 32:64] = 0.0
+    w0[9, 40] = np.inf          # a non-finite block: scale 0xFF, zero codes
+    ema = to_dev_f32(w0)
+    oe = w0.copy()
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=DEV)
+    ow = w0.copy()
+    for t in range(1, 26):
+        ow = (ow + (rng.standard_normal((rows, cols)) * 1e-3).astype(np.float32)).astype(np.float32)
+        beta = 0.998 if t < 20 else 0.9
+        mx.mx_qema_step(to_dev_f32(ow), ema, rows, cols, beta, codes, scales)
+        oe, oc, os_ = O.qema_step(ow, oe, beta)
+        assert_bytes_equal(host(ema).view(np.uint32), oe.view(np.uint32), f"ema step {t}")
+        assert_bytes_equal(host(codes), oc, f"codes step {t}")
+        assert_bytes_equal(host(scales), os_, f"scales step {t}")
+    assert (host(scales) == 255).sum() == 1
+
+
 def test_deosc_mid_window_state_matches_oracle():
     rng = np.random.default_rng(3)
     w0 = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)
