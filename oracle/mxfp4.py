@@ -59,6 +59,7 @@ __all__ = [
     "shared_exponent", "quantize_blocks", "pack_codes", "unpack_codes",
     "quantize", "dequantize", "requantize", "block_indices",
     "gemm", "gemm_abs", "gemm_grouped", "linear_fwd", "linear_bwd",
+    "HADAMARD_ALPHA", "requantize_rht", "linear_fwd_rht", "linear_bwd_rht",
     "bin_value_f32", "deosc_init", "deosc_step", "deosc_step_quantized", "qema_step",
     "bf16_bits_to_f32",
 ]
@@ -352,6 +353,52 @@ def linear_bwd(dy, xq, wq, M: int, N: int, K: int, seed: int):
     q6 = requantize(xq[0], xq[1], M, K, SR, seed + 6)     # [K, M/2]
     dx = gemm(q3[0], q3[1], q4[0], q4[1], M, K, N)
     dw = gemm(q5[0], q5[1], q6[0], q6[1], N, K, M)
+    return dx, dw, (q3, q4, q5, q6)
+
+
+# ---------------------------------------------------------------- rotated linear layer
+HADAMARD_ALPHA = 2.0 ** -5   # H H^T = 32 I: a product of two rotated operands is 32x too large
+
+
+def requantize_rht(codes, scales, rows: int, cols: int, rounding: int = SR, seed: int = 0,
+                   sign_mask: int = 0):
+    """Double quantization of an operand saved in the rotated domain: the packed
+    [rows, cols] matrix holds Q_D of X rotated along cols (1x32 blocks, sign mask
+    s); the rotation is undone exactly as `dequantize` does it, and the result is
+    rotated along rows (32x1 blocks, same mask) and quantized there (output
+    transposed, like `requantize`)."""
+    x = dequantize(codes, scales, rows, cols, ROW, True, sign_mask).astype(np.float32)
+    return quantize(x, COL, rounding, seed, True, sign_mask)
+
+
+def linear_fwd_rht(x, w, sign_mask: int):
+    """Forward with the random-sign block Hadamard ("ALTO MXFP4 training -- Weight
+    de-oscillation", Jargon "RHT", and the "MXFP4 + RHT + stochastic rounding"
+    rows of its steps table): both operands are rotated along the contraction
+    axis K with the same signs before Q_D, so Y = 2^-5 Q_D(H X) Q_D(H W)^T.
+    Returns Y and the packed (rotated-domain) operands kept for the backward."""
+    x = np.asarray(x, dtype=np.float32)
+    w = np.asarray(w, dtype=np.float32)
+    M, K = x.shape
+    N = w.shape[0]
+    xq = quantize(x, ROW, RNE, 0, True, sign_mask)
+    wq = quantize(w, ROW, RNE, 0, True, sign_mask)
+    y = gemm(xq[0], xq[1], wq[0], wq[1], M, N, K, HADAMARD_ALPHA)
+    return y, xq, wq
+
+
+def linear_bwd_rht(dy, xq, wq, M: int, N: int, K: int, seed: int, sign_mask: int):
+    """Backward of the rotated layer: every product rotates both operands along its
+    own contraction axis with the same signs (N for dX, M for dW) and takes 2^-5;
+    the saved operands are brought back from the K rotation before their 32x1
+    double quantization.  Quantizer q uses seed + q as in `linear_bwd`."""
+    dy = np.asarray(dy, dtype=np.float32)
+    q3 = quantize(dy, ROW, SR, seed + 3, True, sign_mask)
+    q4 = requantize_rht(wq[0], wq[1], N, K, SR, seed + 4, sign_mask)
+    q5 = quantize(dy, COL, SR, seed + 5, True, sign_mask)
+    q6 = requantize_rht(xq[0], xq[1], M, K, SR, seed + 6, sign_mask)
+    dx = gemm(q3[0], q3[1], q4[0], q4[1], M, K, N, HADAMARD_ALPHA)
+    dw = gemm(q5[0], q5[1], q6[0], q6[1], N, K, M, HADAMARD_ALPHA)
     return dx, dw, (q3, q4, q5, q6)
 
 
