@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parts", action="store_true", help="skip the quantizer sweep / MoE rows")
-    p.add_argument("--only", default=None, help="run one part only: linear|sweep|moe|deosc")
+    p.add_argument("--only", default=None, help="run one part only: linear|rht|sweep|moe|deosc")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (known HBM bytes) for counter scaling")
     return p.parse_args()
@@ -170,6 +170,39 @@ def bench_linear(torch, mx, synth, dev, steps, warmup, seed=3):
         "gemm_launches": T.count("gemm"), "kernels_us": {k: v * 1e3 for k, v in kern.items()},
         "quantizers": quant, "matches_linear_entry_points": bool(same),
     }
+
+
+# ---------------------------------------------------------------- rotated linear layer
+def bench_linear_rht(torch, mx, synth, dev, steps=10, seed=3, mask=0x9E3779B9):
+    """The Llama up-projection through the random-sign Hadamard layer
+    (mx_linear_fwd_rht + mx_linear_bwd_rht), forward and backward timed apart."""
+    cfg = synth.llama_config()
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    x = bf16_dev(torch, cfg["x"], dev)
+    w = bf16_dev(torch, cfg["w"], dev)
+    dy = bf16_dev(torch, cfg["dy"], dev)
+    del cfg
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
+    y, dx, dw = (torch.empty(s, dtype=torch.float32, device=dev) for s in ((M, N), (M, K), (N, K)))
+    xq, wq = (u8(M, K // 2), u8(M, K // 32)), (u8(N, K // 2), u8(N, K // 32))
+    ws = u8(mx.mx_linear_bwd_workspace_size(M, N, K))
+    st = torch.cuda.current_stream()
+    BF = mx.MX_BF16
+    fwd = lambda: mx.mx_linear_fwd_rht(x, w, BF, M, N, K, mask, y, *xq, *wq, st)
+    bwd = lambda: mx.mx_linear_bwd_rht(dy, BF, M, N, K, *xq, *wq, seed, mask, dx, dw, ws,
+                                       ws.numel(), st)
+    for _ in range(2):
+        fwd()
+        bwd()
+    T = Timer(torch, st)
+    for _ in range(steps):
+        T.run("fwd", fwd)
+        T.run("bwd", bwd)
+    torch.cuda.synchronize()
+    f, b = T.mean_ms("fwd"), T.mean_ms("bwd")
+    fl = 2.0 * M * N * K
+    return {"fwd_us": f * 1e3, "bwd_us": b * 1e3, "fwd_bwd_ms": f + b,
+            "TFLOPs": 3 * fl / ((f + b) * 1e-3) / 1e12, "sign_mask": mask}
 
 
 # ---------------------------------------------------------------- quantizer sweep
@@ -345,6 +378,10 @@ def main():
     if args.only in (None, "linear"):
         log("linear fwd+bwd (Llama-3-8B up-projection)")
         lin = bench_linear(torch, mx, synth, dev, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+    if not args.no_parts and args.only in (None, "rht"):
+        log("rotated linear fwd+bwd (Llama-3-8B up-projection)")
+        parts["linear_rht_llama_up_proj"] = bench_linear_rht(torch, mx, synth, dev)
         torch.cuda.empty_cache()
     if not args.no_parts and args.only in (None, "sweep"):
         log("quantizer sweep 8192x8192 bf16")

@@ -118,6 +118,18 @@ int mx_quantize_dual(const void* x, int dtype, int64_t rows, int64_t cols, int r
                      uint8_t* codes_row, uint8_t* scales_row,
                      uint8_t* codes_col, uint8_t* scales_col, void* stream);
 
+/* mx_quantize_dual_rht: mx_quantize_dual with the random-sign block Hadamard
+ * ([ALTO] Jargon "Randomized Hadamard transform"; the "MXFP4 + RHT +
+ * stochastic rounding" rows of its steps table) on both outputs: each row
+ * block and each column block is rotated, y = H32 (s . x) with s from
+ * sign_mask (bit j set: element j of the block negated), before it is
+ * quantized -- equal, bit for bit, to two mx_quantize calls with hadamard = 1.
+ * Arguments otherwise as mx_quantize_dual. */
+int mx_quantize_dual_rht(const void* x, int dtype, int64_t rows, int64_t cols, int round,
+                         uint64_t seed_row, uint64_t seed_col, uint32_t sign_mask,
+                         uint8_t* codes_row, uint8_t* scales_row,
+                         uint8_t* codes_col, uint8_t* scales_col, void* stream);
+
 /* mx_requantize: double quantization Q(Q_D(X)) -- [TJ] Question 2 (2), the
  * double-quantized operand Q_S^(6)(Q_D^(1)(X)).  Input: a packed MX_ROW matrix
  * of logical shape [rows, cols] (codes_in [rows][cols/2], scales_in
@@ -128,6 +140,18 @@ int mx_quantize_dual(const void* x, int dtype, int64_t rows, int64_t cols, int r
  * mx_quantize(dequantized input, MX_COL, ...).  rows % 32 == 0, cols % 32 == 0. */
 int mx_requantize(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows, int64_t cols,
                   int round, uint64_t seed, uint8_t* codes_out, uint8_t* scales_out, void* stream);
+
+/* mx_requantize_rht: double quantization of an operand kept in the rotated
+ * domain (the rotated layer's saved Q_D(H X), rotated along cols with
+ * sign_mask): the input's row blocks are decoded and rotated back exactly as
+ * mx_dequantize with hadamard = 1 does it (float32), then each 32x1 column
+ * block is rotated with the same signs and quantized (output transposed, as
+ * mx_requantize; the stochastic-rounding index is the logical row-major index
+ * of the rotated position).  Equal to mx_quantize(mx_dequantize(in, MX_ROW,
+ * hadamard = 1), MX_COL, hadamard = 1).  rows % 32 == 0, cols % 32 == 0. */
+int mx_requantize_rht(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
+                      int64_t cols, int round, uint64_t seed, uint32_t sign_mask,
+                      uint8_t* codes_out, uint8_t* scales_out, void* stream);
 
 /* mx_dequantize: exact values of a packed matrix of logical shape [rows, cols]
  * quantized along `axis` (the inverse layout of mx_quantize), written row-major
@@ -192,6 +216,28 @@ int mx_linear_bwd(const void* dy, int dtype, int64_t M, int64_t N, int64_t K,
                   const uint8_t* wq_codes, const uint8_t* wq_scales,
                   uint64_t seed, float* dx, float* dw,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* mx_linear_fwd_rht / mx_linear_bwd_rht: the same layer with the random-sign
+ * block Hadamard on every product ([ALTO] Jargon "Randomized Hadamard
+ * transform", the "MXFP4 + RHT + stochastic rounding" rows of its steps
+ * table): both operands of a product are rotated along that product's
+ * contraction axis with the same signs (sign_mask), and since H H^T = 32 I the
+ * product is scaled by alpha = 2^-5 (exact):
+ *   Y  = 2^-5 Q_D(H_K X) Q_D(H_K W)^T
+ *   dX = 2^-5 Q_S^(3)(H_N dY) . Q_S^(4)(H_N W~)      W~ = H_K^-1 deq(Q_D(H_K W))
+ *   dW = 2^-5 Q_S^(5)(H_M dY)^T . Q_S^(6)(H_M X~)    X~ = H_K^-1 deq(Q_D(H_K X))
+ * The saved operands (xq, wq) are in the K-rotated domain; the backward takes
+ * them back before its own rotations (mx_requantize_rht).  Arguments, layouts,
+ * seeds (seed + q), workspace (mx_linear_bwd_workspace_size) and errors as
+ * mx_linear_fwd / mx_linear_bwd. */
+int mx_linear_fwd_rht(const void* x, const void* w, int dtype, int64_t M, int64_t N, int64_t K,
+                      uint32_t sign_mask, float* y, uint8_t* xq_codes, uint8_t* xq_scales,
+                      uint8_t* wq_codes, uint8_t* wq_scales, void* stream);
+int mx_linear_bwd_rht(const void* dy, int dtype, int64_t M, int64_t N, int64_t K,
+                      const uint8_t* xq_codes, const uint8_t* xq_scales,
+                      const uint8_t* wq_codes, const uint8_t* wq_scales,
+                      uint64_t seed, uint32_t sign_mask, float* dx, float* dw,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------ de-oscillation
  * Weight de-oscillation as a post-optimizer-step pass ([ALTO] "How does ALTO

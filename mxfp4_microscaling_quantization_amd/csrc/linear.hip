@@ -20,11 +20,14 @@ int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, int axis
                   uint64_t seed, int had, uint32_t mask, uint8_t* codes, uint8_t* scales,
                   hipStream_t st);
 int quantize_dual_impl(const void* x, int dtype, int64_t rows, int64_t cols, int round,
-                       uint64_t seed_row, uint64_t seed_col, uint8_t* codes_row,
-                       uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
-                       hipStream_t st);
+                       uint64_t seed_row, uint64_t seed_col, int had, uint32_t mask,
+                       uint8_t* codes_row, uint8_t* scales_row, uint8_t* codes_col,
+                       uint8_t* scales_col, hipStream_t st);
 int requantize_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows, int64_t cols,
                     int round, uint64_t seed, uint8_t* codes, uint8_t* scales, hipStream_t st);
+int requantize_rht_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
+                        int64_t cols, int round, uint64_t seed, uint32_t mask, uint8_t* codes,
+                        uint8_t* scales, hipStream_t st);
 int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
               const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha, float* c,
               int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, hipStream_t st);
@@ -64,13 +67,13 @@ static BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K) {
   return L;
 }
 
-}  // namespace mx
+// Two rotated operands carry a factor 32 (H H^T = 32 I): the product takes 2^-5.
+constexpr float kHadamardAlpha = 0.03125f;
 
-using namespace mx;
-
-extern "C" int mx_linear_fwd(const void* x, const void* w, int dtype, int64_t M, int64_t N,
-                             int64_t K, float* y, uint8_t* xq_codes, uint8_t* xq_scales,
-                             uint8_t* wq_codes, uint8_t* wq_scales, void* stream) {
+static int linear_fwd_impl(const void* x, const void* w, int dtype, int64_t M, int64_t N,
+                           int64_t K, int had, uint32_t mask, float* y, uint8_t* xq_codes,
+                           uint8_t* xq_scales, uint8_t* wq_codes, uint8_t* wq_scales,
+                           hipStream_t st) {
   MX_REQUIRE(dtype == MX_F32 || dtype == MX_BF16, MX_ERR_ENUM);
   MX_REQUIRE(M >= 0 && N >= 0 && K >= 0, MX_ERR_SHAPE);
   MX_REQUIRE(M % 32 == 0 && N % 32 == 0 && K % 32 == 0, MX_ERR_SHAPE);
@@ -81,13 +84,73 @@ extern "C" int mx_linear_fwd(const void* x, const void* w, int dtype, int64_t M,
   MX_REQUIRE(x && w && y && xq_codes && xq_scales && wq_codes && wq_scales, MX_ERR_NULL);
   MX_REQUIRE(aligned16(x) && aligned16(w) && aligned16(y) && aligned16(xq_codes) &&
                  aligned16(wq_codes), MX_ERR_ALIGN);
-  const hipStream_t st = as_stream(stream);
-  int s = quantize_impl(x, dtype, M, K, MX_ROW, MX_RNE, 0, 0, 0, xq_codes, xq_scales, st);
+  int s = quantize_impl(x, dtype, M, K, MX_ROW, MX_RNE, 0, had, mask, xq_codes, xq_scales, st);
   if (s != MX_OK) return s;
-  s = quantize_impl(w, dtype, N, K, MX_ROW, MX_RNE, 0, 0, 0, wq_codes, wq_scales, st);
+  s = quantize_impl(w, dtype, N, K, MX_ROW, MX_RNE, 0, had, mask, wq_codes, wq_scales, st);
   if (s != MX_OK) return s;
   const int64_t offs[2] = {0, M};
-  return gemm_impl(xq_codes, xq_scales, wq_codes, wq_scales, offs, 1, N, K, 1.0f, y, N, 0, 0, st);
+  return gemm_impl(xq_codes, xq_scales, wq_codes, wq_scales, offs, 1, N, K,
+                   had ? kHadamardAlpha : 1.0f, y, N, 0, 0, st);
+}
+
+static int linear_bwd_impl(const void* dy, int dtype, int64_t M, int64_t N, int64_t K,
+                           const uint8_t* xq_codes, const uint8_t* xq_scales,
+                           const uint8_t* wq_codes, const uint8_t* wq_scales, uint64_t seed,
+                           int had, uint32_t mask, float* dx, float* dw, void* workspace,
+                           size_t workspace_bytes, hipStream_t st) {
+  MX_REQUIRE(dtype == MX_F32 || dtype == MX_BF16, MX_ERR_ENUM);
+  MX_REQUIRE(M >= 0 && N >= 0 && K >= 0, MX_ERR_SHAPE);
+  MX_REQUIRE(M % 32 == 0 && N % 32 == 0 && K % 32 == 0, MX_ERR_SHAPE);
+  if (M == 0 || N == 0 || K == 0) return MX_OK;
+  MX_REQUIRE(dy && xq_codes && xq_scales && wq_codes && wq_scales && dx && dw, MX_ERR_NULL);
+  MX_REQUIRE(aligned16(dy) && aligned16(xq_codes) && aligned16(wq_codes) && aligned16(dx) &&
+                 aligned16(dw), MX_ERR_ALIGN);
+  const BwdLayout L = bwd_layout(M, N, K);
+  MX_REQUIRE(workspace && workspace_bytes >= L.total, MX_ERR_WORKSPACE);
+  MX_REQUIRE(aligned16(workspace), MX_ERR_ALIGN);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+
+  int s = quantize_dual_impl(dy, dtype, M, N, MX_SR, seed + 3, seed + 5, had, mask, ws + L.q3c,
+                             ws + L.q3s, ws + L.q5c, ws + L.q5s, st);
+  if (s != MX_OK) return s;
+  if (had) {
+    s = requantize_rht_impl(wq_codes, wq_scales, N, K, MX_SR, seed + 4, mask, ws + L.q4c,
+                            ws + L.q4s, st);
+    if (s != MX_OK) return s;
+    s = requantize_rht_impl(xq_codes, xq_scales, M, K, MX_SR, seed + 6, mask, ws + L.q6c,
+                            ws + L.q6s, st);
+  } else {
+    s = requantize_impl(wq_codes, wq_scales, N, K, MX_SR, seed + 4, ws + L.q4c, ws + L.q4s, st);
+    if (s != MX_OK) return s;
+    s = requantize_impl(xq_codes, xq_scales, M, K, MX_SR, seed + 6, ws + L.q6c, ws + L.q6s, st);
+  }
+  if (s != MX_OK) return s;
+  const float alpha = had ? kHadamardAlpha : 1.0f;
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  s = gemm_split_impl(ws + L.q3c, ws + L.q3s, ws + L.q4c, ws + L.q4s, M, K, N, alpha, dx, K, L.dx,
+                      part, st);
+  if (s != MX_OK) return s;
+  return gemm_split_impl(ws + L.q5c, ws + L.q5s, ws + L.q6c, ws + L.q6s, N, K, M, alpha, dw, K,
+                         L.dw, part, st);
+}
+
+}  // namespace mx
+
+using namespace mx;
+
+extern "C" int mx_linear_fwd(const void* x, const void* w, int dtype, int64_t M, int64_t N,
+                             int64_t K, float* y, uint8_t* xq_codes, uint8_t* xq_scales,
+                             uint8_t* wq_codes, uint8_t* wq_scales, void* stream) {
+  return linear_fwd_impl(x, w, dtype, M, N, K, 0, 0, y, xq_codes, xq_scales, wq_codes, wq_scales,
+                         as_stream(stream));
+}
+
+extern "C" int mx_linear_fwd_rht(const void* x, const void* w, int dtype, int64_t M, int64_t N,
+                                 int64_t K, uint32_t sign_mask, float* y, uint8_t* xq_codes,
+                                 uint8_t* xq_scales, uint8_t* wq_codes, uint8_t* wq_scales,
+                                 void* stream) {
+  return linear_fwd_impl(x, w, dtype, M, N, K, 1, sign_mask, y, xq_codes, xq_scales, wq_codes,
+                         wq_scales, as_stream(stream));
 }
 
 extern "C" size_t mx_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K) {
@@ -100,32 +163,17 @@ extern "C" int mx_linear_bwd(const void* dy, int dtype, int64_t M, int64_t N, in
                              const uint8_t* wq_codes, const uint8_t* wq_scales, uint64_t seed,
                              float* dx, float* dw, void* workspace, size_t workspace_bytes,
                              void* stream) {
-  MX_REQUIRE(dtype == MX_F32 || dtype == MX_BF16, MX_ERR_ENUM);
-  MX_REQUIRE(M >= 0 && N >= 0 && K >= 0, MX_ERR_SHAPE);
-  MX_REQUIRE(M % 32 == 0 && N % 32 == 0 && K % 32 == 0, MX_ERR_SHAPE);
-  if (M == 0 || N == 0 || K == 0) return MX_OK;
-  MX_REQUIRE(dy && xq_codes && xq_scales && wq_codes && wq_scales && dx && dw, MX_ERR_NULL);
-  MX_REQUIRE(aligned16(dy) && aligned16(xq_codes) && aligned16(wq_codes) && aligned16(dx) &&
-                 aligned16(dw), MX_ERR_ALIGN);
-  const BwdLayout L = bwd_layout(M, N, K);
-  MX_REQUIRE(workspace && workspace_bytes >= L.total, MX_ERR_WORKSPACE);
-  MX_REQUIRE(aligned16(workspace), MX_ERR_ALIGN);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const hipStream_t st = as_stream(stream);
+  return linear_bwd_impl(dy, dtype, M, N, K, xq_codes, xq_scales, wq_codes, wq_scales, seed, 0,
+                         0, dx, dw, workspace, workspace_bytes, as_stream(stream));
+}
 
-  int s = quantize_dual_impl(dy, dtype, M, N, MX_SR, seed + 3, seed + 5, ws + L.q3c, ws + L.q3s,
-                             ws + L.q5c, ws + L.q5s, st);
-  if (s != MX_OK) return s;
-  s = requantize_impl(wq_codes, wq_scales, N, K, MX_SR, seed + 4, ws + L.q4c, ws + L.q4s, st);
-  if (s != MX_OK) return s;
-  s = requantize_impl(xq_codes, xq_scales, M, K, MX_SR, seed + 6, ws + L.q6c, ws + L.q6s, st);
-  if (s != MX_OK) return s;
-  float* part = reinterpret_cast<float*>(ws + L.part);
-  s = gemm_split_impl(ws + L.q3c, ws + L.q3s, ws + L.q4c, ws + L.q4s, M, K, N, 1.0f, dx, K, L.dx,
-                      part, st);
-  if (s != MX_OK) return s;
-  return gemm_split_impl(ws + L.q5c, ws + L.q5s, ws + L.q6c, ws + L.q6s, N, K, M, 1.0f, dw, K,
-                         L.dw, part, st);
+extern "C" int mx_linear_bwd_rht(const void* dy, int dtype, int64_t M, int64_t N, int64_t K,
+                                 const uint8_t* xq_codes, const uint8_t* xq_scales,
+                                 const uint8_t* wq_codes, const uint8_t* wq_scales, uint64_t seed,
+                                 uint32_t sign_mask, float* dx, float* dw, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return linear_bwd_impl(dy, dtype, M, N, K, xq_codes, xq_scales, wq_codes, wq_scales, seed, 1,
+                         sign_mask, dx, dw, workspace, workspace_bytes, as_stream(stream));
 }
 
 extern "C" const char* mx_status_string(int status) {

@@ -114,7 +114,8 @@ __global__ __launch_bounds__(256) void k_quant_row(const T* __restrict__ x, int6
 // blocks; their codes are staged so that each output row (= input column) gets
 // 64 contiguous bytes per tile.  With ROW set (dual quantization) the chunks
 // are also quantized as 1x32 blocks straight from registers: the 32 / E lanes
-// holding one row block are adjacent, E = elements per chunk.
+// holding one row block are adjacent, E = elements per chunk.  HAD rotates both
+// block shapes (with ROW only for bf16, where a row block is one DPP quad).
 constexpr int kTileR = 128;
 constexpr int kTileRowBytes = 256;
 
@@ -217,6 +218,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(
   }
 
   // ---- row pass (1x32 blocks) from registers
+  static_assert(!(ROW && HAD) || E == 8, "rotated row pass needs one quad per block");
   if constexpr (ROW) {
 #pragma unroll
     for (int j = 0; j < NLOAD; ++j) {
@@ -228,6 +230,12 @@ __global__ __launch_bounds__(256) void k_quant_tile(
       for (int i = 0; i < E; ++i) {
         if constexpr (sizeof(T) == 2) v[i] = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
         else v[i] = __uint_as_float(w[i]);
+      }
+      if constexpr (HAD && E == 8) {
+        const int qq = lc & 3;  // lane's position in its block's quad
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = apply_sign(v[i], sign_mask, qq * 8 + i);
+        fwht32_quad(v, qq);
       }
       uint32_t m = 0;
 #pragma unroll
@@ -353,6 +361,72 @@ __global__ __launch_bounds__(256) void k_requant(const uint8_t* __restrict__ cod
   store_col_tile<kRqC, NRB>(s_codes, s_scales, rows, col0, ncols, row0, nrb, codes, scales);
 }
 
+// ============================================================== rotated double quantization
+// Input: Q_D of X rotated along cols (packed row-blocked [rows, cols], sign mask
+// s).  Each row block is decoded exactly and rotated back (s * FWHT(y) * 2^-5,
+// float32, the same quad FWHT as the rotated quantizer), the tile (128 rows x 64
+// columns) is staged in LDS as float32, and each 32x1 column block is rotated
+// along rows with the same signs and quantized (output transposed).
+constexpr int kRhtR = 128;
+constexpr int kRhtC = 64;
+
+template <int ROUND>
+__global__ __launch_bounds__(256) void k_requant_rht(const uint8_t* __restrict__ codes_in,
+                                                     const uint8_t* __restrict__ scales_in,
+                                                     int64_t rows, int64_t cols, uint64_t seed,
+                                                     uint32_t sign_mask,
+                                                     uint8_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales) {
+  constexpr int NRB = kRhtR / 32;
+  __shared__ float s_x[kRhtR * kRhtC];  // [row][col]
+  __shared__ uint4 s_codes[kRhtC * NRB];
+  __shared__ uint8_t s_scales[kRhtC * NRB];
+
+  const int64_t col0 = (int64_t)blockIdx.x * kRhtC;
+  const int64_t row0 = (int64_t)blockIdx.y * kRhtR;
+  const int ncols = (int)min<int64_t>(kRhtC, cols - col0);   // 32 or 64
+  const int nrows = (int)min<int64_t>(kRhtR, rows - row0);   // multiple of 32
+  const int nrb = nrows / 32;
+  const int64_t ld_in = cols / 2, ld_sin = cols / 32;
+  const int q = threadIdx.x & 3;
+
+  // ---- decode and undo the row rotation: quad j takes row blocks j, j + 64, ...
+  for (int blk = threadIdx.x >> 2; blk < kRhtR * (kRhtC / 32); blk += 64) {
+    const int r = blk / (kRhtC / 32), kb = blk % (kRhtC / 32);
+    if (r >= nrows || kb * 32 >= ncols) continue;  // whole quads drop out together
+    const uint32_t wcodes = *reinterpret_cast<const uint32_t*>(
+        codes_in + (row0 + r) * ld_in + (col0 + kb * 32) / 2 + q * 4);
+    const uint32_t byte = scales_in[(row0 + r) * ld_sin + (col0 / 32 + kb)];
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = e2m1_decode((wcodes >> (4 * i)) & 15u, byte);
+    fwht32_quad(v, q);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = apply_sign(v[i] * 0.03125f, sign_mask, q * 8 + i);
+    float* dst = &s_x[r * kRhtC + kb * 32 + q * 8];
+    reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  __syncthreads();
+
+  // ---- rotate and quantize the column blocks: thread (c, rb)
+  {
+    const int c = threadIdx.x % kRhtC, rb = threadIdx.x / kRhtC;
+    if (rb < nrb && c < ncols) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = apply_sign(s_x[(rb * 32 + i) * kRhtC + c], sign_mask, i);
+      fwht32_lane(v);
+      uint32_t byte;
+      const uint64_t idx0 = (uint64_t)(row0 + rb * 32) * (uint64_t)cols + (uint64_t)(col0 + c);
+      s_codes[c * NRB + rb] = quant_col32<ROUND>(v, byte, seed, idx0, (uint64_t)cols);
+      s_scales[c * NRB + rb] = (uint8_t)byte;
+    }
+  }
+  __syncthreads();
+  store_col_tile<kRhtC, NRB>(s_codes, s_scales, rows, col0, ncols, row0, nrb, codes, scales);
+}
+
 // ============================================================== dequantization
 template <typename TOut>
 __device__ __forceinline__ void store8(TOut* p, const float v[8]);
@@ -470,11 +544,12 @@ static int launch_quant_tile(const T* x, int64_t rows, int64_t cols, int round, 
   constexpr int TC = kTileRowBytes / sizeof(T);
   const dim3 grid((unsigned)cdiv(cols, TC), (unsigned)cdiv(rows, kTileR)), block(256);
 #define MX_TILE_ARGS x, rows, cols, seed_row, seed_col, mask, codes_row, scales_row, codes_col, scales_col
+  constexpr bool kHad = !ROW || sizeof(T) == 2;  // rotated row pass: bf16 only
   if (round == MX_RNE) {
-    if (had) k_quant_tile<T, MX_RNE, ROW, true><<<grid, block, 0, st>>>(MX_TILE_ARGS);
+    if (had && kHad) k_quant_tile<T, MX_RNE, ROW, kHad><<<grid, block, 0, st>>>(MX_TILE_ARGS);
     else k_quant_tile<T, MX_RNE, ROW, false><<<grid, block, 0, st>>>(MX_TILE_ARGS);
   } else {
-    if (had) k_quant_tile<T, MX_SR, ROW, true><<<grid, block, 0, st>>>(MX_TILE_ARGS);
+    if (had && kHad) k_quant_tile<T, MX_SR, ROW, kHad><<<grid, block, 0, st>>>(MX_TILE_ARGS);
     else k_quant_tile<T, MX_SR, ROW, false><<<grid, block, 0, st>>>(MX_TILE_ARGS);
   }
 #undef MX_TILE_ARGS
@@ -512,17 +587,37 @@ int requantize_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t r
 }
 
 int quantize_dual_impl(const void* x, int dtype, int64_t rows, int64_t cols, int round,
-                       uint64_t seed_row, uint64_t seed_col, uint8_t* codes_row,
-                       uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
-                       hipStream_t st) {
+                       uint64_t seed_row, uint64_t seed_col, int had, uint32_t mask,
+                       uint8_t* codes_row, uint8_t* scales_row, uint8_t* codes_col,
+                       uint8_t* scales_col, hipStream_t st) {
   if (rows == 0 || cols == 0) return MX_OK;
-  return dtype == MX_BF16
-             ? launch_quant_tile<uint16_t, true>(static_cast<const uint16_t*>(x), rows, cols, round,
-                                                 seed_row, seed_col, 0, 0, codes_row, scales_row,
-                                                 codes_col, scales_col, st)
-             : launch_quant_tile<float, true>(static_cast<const float*>(x), rows, cols, round,
-                                              seed_row, seed_col, 0, 0, codes_row, scales_row,
-                                              codes_col, scales_col, st);
+  if (dtype == MX_BF16)
+    return launch_quant_tile<uint16_t, true>(static_cast<const uint16_t*>(x), rows, cols, round,
+                                             seed_row, seed_col, had, mask, codes_row, scales_row,
+                                             codes_col, scales_col, st);
+  if (!had)
+    return launch_quant_tile<float, true>(static_cast<const float*>(x), rows, cols, round,
+                                          seed_row, seed_col, 0, 0, codes_row, scales_row,
+                                          codes_col, scales_col, st);
+  // float32 with the rotation: a row block spans 8 lanes of the tile kernel, so
+  // the two block shapes go through the row kernel and the column tile kernel
+  const int s = quantize_impl(x, dtype, rows, cols, MX_ROW, round, seed_row, 1, mask, codes_row,
+                              scales_row, st);
+  if (s != MX_OK) return s;
+  return quantize_impl(x, dtype, rows, cols, MX_COL, round, seed_col, 1, mask, codes_col,
+                       scales_col, st);
+}
+
+int requantize_rht_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
+                        int64_t cols, int round, uint64_t seed, uint32_t mask, uint8_t* codes,
+                        uint8_t* scales, hipStream_t st) {
+  if (rows == 0 || cols == 0) return MX_OK;
+  const dim3 grid((unsigned)cdiv(cols, kRhtC), (unsigned)cdiv(rows, kRhtR)), block(256);
+  if (round == MX_RNE)
+    k_requant_rht<MX_RNE><<<grid, block, 0, st>>>(codes_in, scales_in, rows, cols, seed, mask, codes, scales);
+  else
+    k_requant_rht<MX_SR><<<grid, block, 0, st>>>(codes_in, scales_in, rows, cols, seed, mask, codes, scales);
+  return launch_status();
 }
 
 }  // namespace mx
@@ -556,8 +651,22 @@ extern "C" int mx_quantize_dual(const void* x, int dtype, int64_t rows, int64_t 
   if (rows == 0 || cols == 0) return MX_OK;
   MX_REQUIRE(x && codes_row && scales_row && codes_col && scales_col, MX_ERR_NULL);
   MX_REQUIRE(aligned16(x) && aligned16(codes_row) && aligned16(codes_col), MX_ERR_ALIGN);
-  return quantize_dual_impl(x, dtype, rows, cols, round, seed_row, seed_col, codes_row, scales_row,
-                            codes_col, scales_col, as_stream(stream));
+  return quantize_dual_impl(x, dtype, rows, cols, round, seed_row, seed_col, 0, 0, codes_row,
+                            scales_row, codes_col, scales_col, as_stream(stream));
+}
+
+extern "C" int mx_quantize_dual_rht(const void* x, int dtype, int64_t rows, int64_t cols,
+                                    int round, uint64_t seed_row, uint64_t seed_col,
+                                    uint32_t sign_mask, uint8_t* codes_row, uint8_t* scales_row,
+                                    uint8_t* codes_col, uint8_t* scales_col, void* stream) {
+  MX_REQUIRE(dtype == MX_F32 || dtype == MX_BF16, MX_ERR_ENUM);
+  MX_REQUIRE(round == MX_RNE || round == MX_SR, MX_ERR_ENUM);
+  MX_REQUIRE(rows >= 0 && cols >= 0 && rows % 32 == 0 && cols % 32 == 0, MX_ERR_SHAPE);
+  if (rows == 0 || cols == 0) return MX_OK;
+  MX_REQUIRE(x && codes_row && scales_row && codes_col && scales_col, MX_ERR_NULL);
+  MX_REQUIRE(aligned16(x) && aligned16(codes_row) && aligned16(codes_col), MX_ERR_ALIGN);
+  return quantize_dual_impl(x, dtype, rows, cols, round, seed_row, seed_col, 1, sign_mask,
+                            codes_row, scales_row, codes_col, scales_col, as_stream(stream));
 }
 
 extern "C" int mx_requantize(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
@@ -570,6 +679,18 @@ extern "C" int mx_requantize(const uint8_t* codes_in, const uint8_t* scales_in, 
   MX_REQUIRE(aligned16(codes_in) && aligned16(codes_out), MX_ERR_ALIGN);
   return requantize_impl(codes_in, scales_in, rows, cols, round, seed, codes_out, scales_out,
                          as_stream(stream));
+}
+
+extern "C" int mx_requantize_rht(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
+                                 int64_t cols, int round, uint64_t seed, uint32_t sign_mask,
+                                 uint8_t* codes_out, uint8_t* scales_out, void* stream) {
+  MX_REQUIRE(round == MX_RNE || round == MX_SR, MX_ERR_ENUM);
+  MX_REQUIRE(rows >= 0 && cols >= 0 && rows % 32 == 0 && cols % 32 == 0, MX_ERR_SHAPE);
+  if (rows == 0 || cols == 0) return MX_OK;
+  MX_REQUIRE(codes_in && scales_in && codes_out && scales_out, MX_ERR_NULL);
+  MX_REQUIRE(aligned16(codes_in) && aligned16(codes_out), MX_ERR_ALIGN);
+  return requantize_rht_impl(codes_in, scales_in, rows, cols, round, seed, sign_mask, codes_out,
+                             scales_out, as_stream(stream));
 }
 
 extern "C" int mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,

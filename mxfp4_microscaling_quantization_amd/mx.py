@@ -31,12 +31,17 @@ SIGNATURES = {
     "mx_quantize": ([_P, _i32, _i64, _i64, _i32, _i32, _u64, _i32, _u32, _P, _P, _P], _i32),
     "mx_quantize_dual": ([_P, _i32, _i64, _i64, _i32, _u64, _u64, _P, _P, _P, _P, _P], _i32),
     "mx_requantize": ([_P, _P, _i64, _i64, _i32, _u64, _P, _P, _P], _i32),
+    "mx_quantize_dual_rht": ([_P, _i32, _i64, _i64, _i32, _u64, _u64, _u32, _P, _P, _P, _P, _P], _i32),
+    "mx_requantize_rht": ([_P, _P, _i64, _i64, _i32, _u64, _u32, _P, _P, _P], _i32),
     "mx_dequantize": ([_P, _P, _i64, _i64, _i32, _i32, _u32, _P, _i32, _P], _i32),
     "mx_gemm": ([_P, _P, _P, _P, _i64, _i64, _i64, _f32, _P, _i64, _P], _i32),
     "mx_gemm_grouped": ([_P, _P, _P, _P, _P, _i64, _i64, _i64, _f32, _P, _P], _i32),
     "mx_linear_fwd": ([_P, _P, _i32, _i64, _i64, _i64, _P, _P, _P, _P, _P, _P], _i32),
     "mx_linear_bwd_workspace_size": ([_i64, _i64, _i64], _sz),
     "mx_linear_bwd": ([_P, _i32, _i64, _i64, _i64, _P, _P, _P, _P, _u64, _P, _P, _P, _sz, _P], _i32),
+    "mx_linear_fwd_rht": ([_P, _P, _i32, _i64, _i64, _i64, _u32, _P, _P, _P, _P, _P, _P], _i32),
+    "mx_linear_bwd_rht": ([_P, _i32, _i64, _i64, _i64, _P, _P, _P, _P, _u64, _u32, _P, _P, _P, _sz,
+                           _P], _i32),
     "mx_deosc_init": ([_P, _i64, _i64, _P, _P, _P, _P], _i32),
     "mx_deosc_step": ([_P, _i64, _i64, _P, _P, _P, _i32, _f32, _P, _P], _i32),
     "mx_deosc_step_quantize": ([_P, _i64, _i64, _P, _P, _P, _i32, _f32, _P, _P, _P, _P], _i32),
@@ -117,6 +122,20 @@ def mx_quantize_dual(x, dtype, rows, cols, round, seed_row, seed_col, codes_row,
         _ptr(codes_col), _ptr(scales_col), _stream(stream)))
 
 
+def mx_quantize_dual_rht(x, dtype, rows, cols, round, seed_row, seed_col, sign_mask, codes_row,
+                         scales_row, codes_col, scales_col, stream=None):
+    _check("mx_quantize_dual_rht", lib().mx_quantize_dual_rht(
+        _ptr(x), dtype, rows, cols, round, seed_row, seed_col, sign_mask, _ptr(codes_row),
+        _ptr(scales_row), _ptr(codes_col), _ptr(scales_col), _stream(stream)))
+
+
+def mx_requantize_rht(codes_in, scales_in, rows, cols, round, seed, sign_mask, codes_out,
+                      scales_out, stream=None):
+    _check("mx_requantize_rht", lib().mx_requantize_rht(
+        _ptr(codes_in), _ptr(scales_in), rows, cols, round, seed, sign_mask, _ptr(codes_out),
+        _ptr(scales_out), _stream(stream)))
+
+
 def mx_requantize(codes_in, scales_in, rows, cols, round, seed, codes_out, scales_out, stream=None):
     _check("mx_requantize", lib().mx_requantize(_ptr(codes_in), _ptr(scales_in), rows, cols, round,
                                                 seed, _ptr(codes_out), _ptr(scales_out),
@@ -149,6 +168,13 @@ def mx_linear_fwd(x, w, dtype, M, N, K, y, xq_codes, xq_scales, wq_codes, wq_sca
                                                 _ptr(wq_scales), _stream(stream)))
 
 
+def mx_linear_fwd_rht(x, w, dtype, M, N, K, sign_mask, y, xq_codes, xq_scales, wq_codes,
+                      wq_scales, stream=None):
+    _check("mx_linear_fwd_rht", lib().mx_linear_fwd_rht(
+        _ptr(x), _ptr(w), dtype, M, N, K, sign_mask, _ptr(y), _ptr(xq_codes), _ptr(xq_scales),
+        _ptr(wq_codes), _ptr(wq_scales), _stream(stream)))
+
+
 def mx_linear_bwd_workspace_size(M, N, K) -> int:
     return int(lib().mx_linear_bwd_workspace_size(M, N, K))
 
@@ -158,6 +184,14 @@ def mx_linear_bwd(dy, dtype, M, N, K, xq_codes, xq_scales, wq_codes, wq_scales, 
     _check("mx_linear_bwd", lib().mx_linear_bwd(
         _ptr(dy), dtype, M, N, K, _ptr(xq_codes), _ptr(xq_scales), _ptr(wq_codes),
         _ptr(wq_scales), seed, _ptr(dx), _ptr(dw), _ptr(workspace), workspace_bytes,
+        _stream(stream)))
+
+
+def mx_linear_bwd_rht(dy, dtype, M, N, K, xq_codes, xq_scales, wq_codes, wq_scales, seed,
+                      sign_mask, dx, dw, workspace, workspace_bytes, stream=None):
+    _check("mx_linear_bwd_rht", lib().mx_linear_bwd_rht(
+        _ptr(dy), dtype, M, N, K, _ptr(xq_codes), _ptr(xq_scales), _ptr(wq_codes),
+        _ptr(wq_scales), seed, sign_mask, _ptr(dx), _ptr(dw), _ptr(workspace), workspace_bytes,
         _stream(stream)))
 
 
@@ -235,6 +269,29 @@ def linear_fwd(x: torch.Tensor, w: torch.Tensor, stream=None):
     wq = (_u8((N, K // 2), x.device), _u8((N, K // 32), x.device))
     mx_linear_fwd(x, w, dtype_code(x), M, N, K, y, xq[0], xq[1], wq[0], wq[1], stream)
     return y, xq, wq
+
+
+def linear_fwd_rht(x: torch.Tensor, w: torch.Tensor, sign_mask: int, stream=None):
+    M, K = x.shape
+    N = w.shape[0]
+    y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    xq = (_u8((M, K // 2), x.device), _u8((M, K // 32), x.device))
+    wq = (_u8((N, K // 2), x.device), _u8((N, K // 32), x.device))
+    mx_linear_fwd_rht(x, w, dtype_code(x), M, N, K, sign_mask, y, xq[0], xq[1], wq[0], wq[1],
+                      stream)
+    return y, xq, wq
+
+
+def linear_bwd_rht(dy: torch.Tensor, xq, wq, M, N, K, seed, sign_mask, workspace=None,
+                   stream=None):
+    need = mx_linear_bwd_workspace_size(M, N, K)
+    if workspace is None:
+        workspace = _u8((need,), dy.device)
+    dx = torch.empty((M, K), dtype=torch.float32, device=dy.device)
+    dw = torch.empty((N, K), dtype=torch.float32, device=dy.device)
+    mx_linear_bwd_rht(dy, dtype_code(dy), M, N, K, xq[0], xq[1], wq[0], wq[1], seed, sign_mask,
+                      dx, dw, workspace, workspace.numel(), stream)
+    return dx, dw
 
 
 def linear_bwd(dy: torch.Tensor, xq, wq, M, N, K, seed, workspace=None, stream=None):

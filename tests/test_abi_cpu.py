@@ -112,6 +112,31 @@ def test_linear_validation_and_workspace_size(L):
     assert L.mx_linear_bwd(*args, BAD, 1 << 30, None) == mx.MX_ERR_ALIGN
 
 
+def test_rotated_entry_points_validation(L):
+    d = L.mx_quantize_dual_rht
+    assert d(GOOD, 2, 32, 32, 1, 1, 2, 5, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_ENUM
+    assert d(GOOD, 1, 32, 40, 1, 1, 2, 5, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_SHAPE
+    assert d(GOOD, 1, 32, 32, 1, 1, 2, 5, GOOD, None, GOOD, GOOD, None) == mx.MX_ERR_NULL
+    assert d(BAD, 1, 32, 32, 1, 1, 2, 5, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_ALIGN
+    r = L.mx_requantize_rht
+    assert r(GOOD, GOOD, 32, 48, 1, 1, 5, GOOD, GOOD, None) == mx.MX_ERR_SHAPE
+    assert r(GOOD, GOOD, 32, 32, 3, 1, 5, GOOD, GOOD, None) == mx.MX_ERR_ENUM
+    assert r(GOOD, None, 32, 32, 1, 1, 5, GOOD, GOOD, None) == mx.MX_ERR_NULL
+    assert r(GOOD, GOOD, 32, 32, 1, 1, 5, BAD, GOOD, None) == mx.MX_ERR_ALIGN
+    f = L.mx_linear_fwd_rht
+    assert f(GOOD, GOOD, 1, 32, 32, 40, 5, GOOD, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_SHAPE
+    assert f(GOOD, GOOD, 7, 32, 32, 32, 5, GOOD, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_ENUM
+    assert f(GOOD, None, 1, 32, 32, 32, 5, GOOD, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_NULL
+    b = L.mx_linear_bwd_rht
+    need = L.mx_linear_bwd_workspace_size(32, 32, 32)
+    assert b(GOOD, 1, 32, 32, 32, GOOD, GOOD, GOOD, GOOD, 1, 5, GOOD, GOOD, GOOD, need - 1,
+             None) == mx.MX_ERR_WORKSPACE
+    assert b(GOOD, 1, 32, 32, 40, GOOD, GOOD, GOOD, GOOD, 1, 5, GOOD, GOOD, GOOD, need,
+             None) == mx.MX_ERR_SHAPE
+    assert b(GOOD, 1, 32, 32, 32, GOOD, GOOD, GOOD, GOOD, 1, 5, GOOD, None, GOOD, need,
+             None) == mx.MX_ERR_NULL
+
+
 def test_deosc_validation(L):
     assert L.mx_deosc_step(GOOD, 4, 40, GOOD, GOOD, GOOD, 0, 4.0, None, None) == mx.MX_ERR_SHAPE
     assert L.mx_deosc_step(GOOD, 4, 32, GOOD, GOOD, GOOD, 1, 4.0, None, None) == mx.MX_ERR_NULL
