@@ -60,6 +60,7 @@ __all__ = [
     "quantize", "dequantize", "requantize", "block_indices",
     "gemm", "gemm_abs", "gemm_grouped", "linear_fwd", "linear_bwd",
     "HADAMARD_ALPHA", "requantize_rht", "linear_fwd_rht", "linear_bwd_rht",
+    "quantize_segments", "grouped_linear_bwd",
     "bin_value_f32", "deosc_init", "deosc_step", "deosc_step_quantized", "qema_step",
     "bf16_bits_to_f32",
 ]
@@ -354,6 +355,66 @@ def linear_bwd(dy, xq, wq, M: int, N: int, K: int, seed: int):
     dx = gemm(q3[0], q3[1], q4[0], q4[1], M, K, N)
     dw = gemm(q5[0], q5[1], q6[0], q6[1], N, K, M)
     return dx, dw, (q3, q4, q5, q6)
+
+
+# ---------------------------------------------------------------- grouped (MoE) backward
+def quantize_segments(x, offs, rounding: int = SR, seed: int = 0):
+    """32x1 blocks along the rows of each segment [offs[g], offs[g+1]) of a [R, C]
+    float32 matrix -- the tokens routed to one expert -- with the segment's tail
+    zero-padded to a whole block.  Returns one (codes [C, P_g/2], scales
+    [C, P_g/32]) pair per segment, P_g = n_g rounded up to a multiple of 32.  The
+    stochastic-rounding index of element (r, c) is r * C + c (padding elements are
+    zeros and round to code 0 whatever their index)."""
+    x = np.asarray(x, dtype=np.float32)
+    R, C = x.shape
+    out = []
+    for g in range(len(offs) - 1):
+        r0, r1 = int(offs[g]), int(offs[g + 1])
+        n = r1 - r0
+        P = (n + BLOCK - 1) // BLOCK * BLOCK
+        v = np.zeros((C, P), dtype=np.float32)
+        v[:, :n] = x[r0:r1].T
+        rows = r0 + np.arange(P, dtype=np.int64)
+        idx = rows[None, :] * C + np.arange(C, dtype=np.int64)[:, None]
+        codes, scales = quantize_blocks(v.reshape(C, P // BLOCK, BLOCK),
+                                        idx.reshape(C, P // BLOCK, BLOCK), rounding, seed)
+        out.append((pack_codes(codes.reshape(C, P)), scales))
+    return out
+
+
+def grouped_linear_bwd(dy, xq, wq, offs, N: int, K: int, seed: int):
+    """Backward of a grouped (mixture-of-experts) linear layer whose forward is
+    `gemm_grouped` of Q_D(X) [R, K] and the stacked Q_D(W) [E*N, K] ("ALTO MXFP4
+    training -- Weight de-oscillation", news paragraph: the MoE model trained in
+    MXFP4; the group shapes and the double quantization of the TetraJet rebuttal,
+    Question 2, applied per expert):
+
+      dX[rows of e] = Q_S^(3)(dY)[rows of e] . Q_S^(4)(Q_D(W_e))   contraction over N
+      dW_e          = Q_S^(5)(dY_e)^T . Q_S^(6)(Q_D(X_e))          contraction over e's tokens
+
+    Q^(3): 1x32 along N; Q^(4): 32x1 along N of the stacked weight (blocks stay in
+    one expert since N % 32 == 0); Q^(5), Q^(6): 32x1 along the tokens of each
+    expert (`quantize_segments`).  Quantizer q uses seed + q.  Returns dx [R, K],
+    dw [E, N, K] and the operands (q3, (q4 codes, q4 scales) per expert, q5, q6).
+    """
+    offs = [int(o) for o in offs]
+    E, R = len(offs) - 1, offs[-1]
+    dy = np.asarray(dy, dtype=np.float32)
+    q3 = quantize(dy, ROW, SR, seed + 3)
+    wdeq = dequantize(wq[0], wq[1], E * N, K, ROW).astype(np.float32)
+    q4c, q4s = quantize(wdeq, COL, SR, seed + 4)              # [K, E*N/2], [K, E*N/32]
+    b_codes = np.stack([q4c[:, e * N // 2:(e + 1) * N // 2] for e in range(E)])
+    b_scales = np.stack([q4s[:, e * N // BLOCK:(e + 1) * N // BLOCK] for e in range(E)])
+    dx = gemm_grouped(q3[0], q3[1], b_codes, b_scales, offs, K, N)
+    xdeq = dequantize(xq[0], xq[1], R, K, ROW).astype(np.float32)
+    q5 = quantize_segments(dy, offs, SR, seed + 5)
+    q6 = quantize_segments(xdeq, offs, SR, seed + 6)
+    dw = np.zeros((E, N, K), dtype=np.float64)
+    for e in range(E):
+        P = q5[e][0].shape[1] * 2
+        if P:
+            dw[e] = gemm(*q5[e], *q6[e], N, K, P)
+    return dx, dw, (q3, (b_codes, b_scales), q5, q6)
 
 
 # ---------------------------------------------------------------- rotated linear layer
