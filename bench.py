@@ -281,6 +281,29 @@ def bench_moe(torch, mx, synth, dev, iters=10, deosc_steps=20):
         res[f"grouped_{key}"] = {"us": ms * 1e3,
                                  "TFLOPs": 2.0 * R * n_out * H / (ms * 1e-3) / 1e12,
                                  "frac_fp4_peak": 2.0 * R * n_out * H / (ms * 1e-3) / 1e12 / PEAK_FP4_TFLOPS}
+    # grouped backward (dX and every expert's dW): dY N(0, 1e-3) bf16 drawn on the
+    # device with a fixed seed; 4 R N K flops (dX and dW each 2 R N K)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    for key, xq_g, wq_g, n_out in (("down", xq_dn, (wq[0][E * F:], wq[1][E * F:]), H),
+                                   ("up", xq_up, (wq[0][:E * F], wq[1][:E * F]), F)):
+        dy = (torch.randn((R, n_out), generator=gen, device=dev) * 1e-3).to(torch.bfloat16)
+        dx_g = torch.empty((R, H), dtype=torch.float32, device=dev)
+        dw_g = torch.empty((E, n_out, H), dtype=torch.float32, device=dev)
+        wsz = mx.mx_grouped_linear_bwd_workspace_size(offs, E, n_out, H)
+        ws_g = torch.empty(wsz, dtype=torch.uint8, device=dev)
+        run = lambda: mx.mx_grouped_linear_bwd(dy, mx.MX_BF16, offs, E, n_out, H, *xq_g, *wq_g, 4,
+                                               dx_g, dw_g, ws_g, wsz, st)
+        run()
+        T = Timer(torch, st)
+        for _ in range(5):
+            T.run("b", run)
+        torch.cuda.synchronize()
+        ms = T.mean_ms("b")
+        fl = 4.0 * R * n_out * H
+        res[f"grouped_bwd_{key}"] = {"us": ms * 1e3, "TFLOPs": fl / (ms * 1e-3) / 1e12,
+                                     "frac_fp4_peak": fl / (ms * 1e-3) / 1e12 / PEAK_FP4_TFLOPS}
+        del dy, dx_g, dw_g, ws_g
     del c_up, c_dn, xq_up, xq_dn, x_up, x_dn, wq
     # de-oscillation: 796M fp32 master weights, synthetic optimizer step between passes
     wp, dw_, dq_ = (torch.empty_like(w) for _ in range(3))

@@ -187,6 +187,31 @@ int mx_gemm_grouped(const uint8_t* a_codes, const uint8_t* a_scales,
                     const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha,
                     float* c, void* stream);
 
+/* ------------------------------------------------------------------ token segments
+ * The 32x1 quantizers of a grouped (mixture-of-experts) layer run per token
+ * segment: segment g is rows offs[g] .. offs[g+1]-1 (offs: HOST array of
+ * groups+1 non-decreasing offsets, offs[0] == 0, offs[groups] == rows, 1 <=
+ * groups <= MX_MAX_GROUPS).  Blocks start at the segment's first row; the
+ * segment's tail is zero-padded to a multiple of 128 rows, so the transposed
+ * outputs have a padded row axis of P = mx_segments_padded_rows(offs, groups)
+ * positions, segment g's starting at the sum of the padded lengths before it.
+ * Padding blocks hold code 0 and scale byte 0.  The stochastic-rounding index
+ * of a real element is its row-major index in [rows, cols]. */
+int64_t mx_segments_padded_rows(const int64_t* offs, int64_t groups);
+
+/* mx_quantize_segments: 32x1 blocks of x [rows, cols] (`dtype`) per segment:
+ * codes [cols][P/2], scales [cols][P/32].  cols % 8 == 0. */
+int mx_quantize_segments(const void* x, int dtype, int64_t rows, int64_t cols,
+                         const int64_t* offs, int64_t groups, int round, uint64_t seed,
+                         uint8_t* codes, uint8_t* scales, void* stream);
+
+/* mx_requantize_segments: mx_requantize per segment -- the exact values of a
+ * packed MX_ROW [rows, cols] matrix quantized with 32x1 blocks per segment:
+ * codes_out [cols][P/2], scales_out [cols][P/32].  cols % 32 == 0. */
+int mx_requantize_segments(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
+                           int64_t cols, const int64_t* offs, int64_t groups, int round,
+                           uint64_t seed, uint8_t* codes_out, uint8_t* scales_out, void* stream);
+
 /* ------------------------------------------------------------------ linear layer
  * mx_linear_fwd: forward of the quantized linear layer, Y = Q_D(X) Q_D(W)^T
  * ([TJ] Question 2 (1)); X [M, K], W [N, K] (nn.Linear layout), both `dtype`;
@@ -238,6 +263,29 @@ int mx_linear_bwd_rht(const void* dy, int dtype, int64_t M, int64_t N, int64_t K
                       const uint8_t* wq_codes, const uint8_t* wq_scales,
                       uint64_t seed, uint32_t sign_mask, float* dx, float* dw,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* mx_grouped_linear_bwd: backward of a grouped (mixture-of-experts) linear
+ * layer whose forward is mx_gemm_grouped(Q_D(X), Q_D(W)) ([ALTO] news
+ * paragraph: the MoE model trained in MXFP4; the group shapes and double
+ * quantization of [TJ] Question 2, per expert):
+ *   dX[rows of e] = Q_S^(3)(dY)[rows of e] . Q_S^(4)(Q_D(W_e))  contraction over N
+ *   dW_e          = Q_S^(5)(dY_e)^T . Q_S^(6)(Q_D(X_e))        contraction over e's tokens
+ * Q^(3): 1x32 along N; Q^(4): 32x1 along N of each expert's [N, K] weight (the
+ * index is that of the stacked [groups*N, K] weight); Q^(5), Q^(6): 32x1 along
+ * the tokens of each expert (token segments, zero-padded tails).  Stochastic
+ * rounding, quantizer q uses seed + q.  dy [R][N] (`dtype`, R = offs[groups]);
+ * xq: Q_D(X) [R][K/2] + [R][K/32]; wq: the stacked Q_D(W) [groups*N][K/2] +
+ * [groups*N][K/32].  Writes dx [R][K] and dw [groups][N][K] float32 (an expert
+ * without tokens gets dW_e = 0).  N, K multiples of 32.  workspace: at least
+ * mx_grouped_linear_bwd_workspace_size(offs, groups, N, K) bytes, 16-byte
+ * aligned. */
+size_t mx_grouped_linear_bwd_workspace_size(const int64_t* offs, int64_t groups, int64_t N,
+                                            int64_t K);
+int mx_grouped_linear_bwd(const void* dy, int dtype, const int64_t* offs, int64_t groups,
+                          int64_t N, int64_t K, const uint8_t* xq_codes, const uint8_t* xq_scales,
+                          const uint8_t* wq_codes, const uint8_t* wq_scales, uint64_t seed,
+                          float* dx, float* dw, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* ------------------------------------------------------------------ de-oscillation
  * Weight de-oscillation as a post-optimizer-step pass ([ALTO] "How does ALTO

@@ -45,12 +45,14 @@ struct GemmGroups {
   int64_t row_off[MX_MAX_GROUPS + 1];       // rows of A / C per group
 };
 
-// Split-K: split s of n covers K-values [s kchunk, min((s + 1) kchunk, K)) and
-// writes its partial sums to C + s c_stride (alpha applied per split).
+// Contraction ranges: split s of n covers K-values [kbeg[s], kbeg[s+1]) (each
+// start a multiple of 128) and writes its own output at C + s c_stride, alpha
+// applied per split.  Used for split-K (partial sums added afterwards) and for
+// the experts' weight gradients (each over its own token range).
 struct GemmSplit {
   int n;
-  int64_t kchunk;    // multiple of 512
-  int64_t c_stride;  // elements between the splits' outputs
+  int64_t c_stride;                   // elements between the splits' outputs
+  int64_t kbeg[MX_MAX_GROUPS + 1];
 };
 
 constexpr int kGroupM = 4;  // tile rows walked together (L2 reuse of B tiles)
@@ -195,8 +197,8 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
 
   const int64_t ldk = K / 2;   // code bytes per row
   const int64_t lds = K / 32;  // scale bytes (32-blocks) per row
-  const int64_t k0 = split * sp.kchunk;
-  const int64_t kc_len = lmin(sp.kchunk, K - k0);  // K-values of this split
+  const int64_t k0 = sp.kbeg[split];
+  const int64_t kc_len = sp.kbeg[split + 1] - k0;  // K-values of this split
   const int64_t kc_bytes = kc_len / 2, kc_blocks = kc_len / 32;
   const int KT = (int)((kc_len + 127) / 128);
   const int tail_kb = (int)(kc_blocks - (int64_t)(KT - 1) * 4);  // valid 32-blocks in the last step
@@ -565,7 +567,16 @@ static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
                    (reinterpret_cast<uintptr_t>(sb) & 3u) == 0 && b_stride_scales % 4 == 0;
   const bool al16 = (reinterpret_cast<uintptr_t>(sa) & 15u) == 0 &&
                     (reinterpret_cast<uintptr_t>(sb) & 15u) == 0 && b_stride_scales % 16 == 0;
-  const int sc = ((K / 32) % 16 == 0 && al16) ? kScGroup : (((K / 32) % 4 == 0 && al4) ? kScDword : kScByte);
+  // scale rows of every split must start aligned as well (group mode reads 16
+  // bytes of four steps, dword mode 4 bytes of one)
+  bool k512 = true, k128 = true;
+  for (int s = 0; s < sp.n; ++s) {
+    k512 = k512 && sp.kbeg[s] % 512 == 0;
+    k128 = k128 && sp.kbeg[s] % 128 == 0;
+  }
+  const int sc = ((K / 32) % 16 == 0 && al16 && k512)
+                     ? kScGroup
+                     : (((K / 32) % 4 == 0 && al4 && k128) ? kScDword : kScByte);
   const bool big = tiles256 * sp.n >= 512;
 #define MX_GEMM_ARGS a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, sp, st
   if (big) {
@@ -582,7 +593,10 @@ static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
 int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
               const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha, float* c,
               int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, hipStream_t st) {
-  const GemmSplit one = {1, K, 0};
+  GemmSplit one{};
+  one.n = 1;
+  one.kbeg[0] = 0;
+  one.kbeg[1] = K;
   return gemm_launch(a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes,
                      b_stride_scales, one, st);
 }
@@ -596,7 +610,7 @@ SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K) {
   SplitPlan p = {1, K};
   const int64_t tiles128 = cdiv(M, 128) * cdiv(N, 128);
   if (cdiv(M, 256) * cdiv(N, 256) >= 512 || tiles128 >= 256 || K < 2048) return p;
-  int64_t n = hmin(cdiv(512, tiles128), K / 1024);
+  int64_t n = hmin(hmin(cdiv(512, tiles128), K / 1024), 64);
   if (n < 2) return p;
   const int64_t chunk = cdiv(cdiv(K, n), 512) * 512;
   n = cdiv(K, chunk);
@@ -630,13 +644,30 @@ int gemm_split_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const
                     SplitPlan plan, float* part, hipStream_t st) {
   const int64_t offs[2] = {0, M};
   if (plan.n <= 1) return gemm_impl(a, sa, b, sb, offs, 1, N, K, alpha, c, ldc, 0, 0, st);
-  const GemmSplit sp = {plan.n, plan.kchunk, M * N};
+  GemmSplit sp{};
+  sp.n = plan.n;
+  sp.c_stride = M * N;
+  for (int i = 0; i <= plan.n; ++i) sp.kbeg[i] = hmin((int64_t)i * plan.kchunk, K);
   int s = gemm_launch(a, sa, b, sb, offs, 1, N, K, 1.0f, part, N, 0, 0, sp, st);
   if (s != MX_OK) return s;
   const int64_t n4 = M * (N / 4);
   k_splitk_sum<<<dim3((unsigned)hmin(cdiv(n4, 256), 4096)), dim3(256), 0, st>>>(
       reinterpret_cast<const float4*>(part), plan.n, M, N / 4, alpha, c, ldc);
   return launch_status();
+}
+
+// C_s [M][N] = alpha * A[:, kbeg[s]:kbeg[s+1]] . B[:, kbeg[s]:kbeg[s+1]]^T for
+// s < n, written at c + s * M * N (A [M, K], B [N, K] packed along K; each kbeg
+// a multiple of 128; an empty range writes zeros).
+int gemm_ranges_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
+                     int64_t M, int64_t N, int64_t K, const int64_t* kbeg, int n, float alpha,
+                     float* c, hipStream_t st) {
+  GemmSplit sp{};
+  sp.n = n;
+  sp.c_stride = M * N;
+  for (int i = 0; i <= n; ++i) sp.kbeg[i] = kbeg[i];
+  const int64_t offs[2] = {0, M};
+  return gemm_launch(a, sa, b, sb, offs, 1, N, K, alpha, c, N, 0, 0, sp, st);
 }
 
 }  // namespace mx

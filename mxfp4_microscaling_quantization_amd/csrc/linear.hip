@@ -35,6 +35,20 @@ SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K);
 int gemm_split_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                     int64_t M, int64_t N, int64_t K, float alpha, float* c, int64_t ldc,
                     SplitPlan plan, float* part, hipStream_t st);
+int gemm_ranges_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
+                     int64_t M, int64_t N, int64_t K, const int64_t* kbeg, int n, float alpha,
+                     float* c, hipStream_t st);
+int requantize_batched_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t batch,
+                            int64_t rows, int64_t cols, int round, uint64_t seed, uint8_t* codes,
+                            uint8_t* scales, hipStream_t st);
+int quantize_segments_impl(const void* x, int dtype, int64_t rows, int64_t cols,
+                           const int64_t* offs, int64_t groups, int round, uint64_t seed,
+                           uint8_t* codes, uint8_t* scales, hipStream_t st);
+int requantize_segments_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
+                             int64_t cols, const int64_t* offs, int64_t groups, int round,
+                             uint64_t seed, uint8_t* codes, uint8_t* scales, hipStream_t st);
+int64_t segments_padded_rows(const int64_t* offs, int64_t groups);
+void segments_padded_offsets(const int64_t* offs, int64_t groups, int64_t* out);
 
 static size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -65,6 +79,38 @@ static BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K) {
   L.part = take(px > pw ? px : pw);
   L.total = o;
   return L;
+}
+
+// Grouped (mixture-of-experts) backward workspace: Q3 [R][N], the experts'
+// Q4 [E][K][N], Q5 [N][P] and Q6 [K][P] packed, P = the padded token axis.
+struct GroupedLayout {
+  size_t q3c, q3s, q4c, q4s, q5c, q5s, q6c, q6s, total;
+  int64_t P;
+};
+
+static GroupedLayout grouped_layout(const int64_t* offs, int64_t E, int64_t N, int64_t K) {
+  GroupedLayout L;
+  const int64_t R = offs[E];
+  L.P = segments_padded_rows(offs, E);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round256(bytes);
+    return at;
+  };
+  L.q3c = take((size_t)R * N / 2);      L.q3s = take((size_t)R * N / 32);
+  L.q4c = take((size_t)E * K * N / 2);  L.q4s = take((size_t)E * K * N / 32);
+  L.q5c = take((size_t)N * L.P / 2);    L.q5s = take((size_t)N * L.P / 32);
+  L.q6c = take((size_t)K * L.P / 2);    L.q6s = take((size_t)K * L.P / 32);
+  L.total = o;
+  return L;
+}
+
+static bool valid_offsets(const int64_t* offs, int64_t groups) {
+  if (!offs || groups < 1 || groups > MX_MAX_GROUPS || offs[0] != 0) return false;
+  for (int64_t g = 0; g < groups; ++g)
+    if (offs[g + 1] < offs[g]) return false;
+  return true;
 }
 
 // Two rotated operands carry a factor 32 (H H^T = 32 I): the product takes 2^-5.
@@ -174,6 +220,62 @@ extern "C" int mx_linear_bwd_rht(const void* dy, int dtype, int64_t M, int64_t N
                                  size_t workspace_bytes, void* stream) {
   return linear_bwd_impl(dy, dtype, M, N, K, xq_codes, xq_scales, wq_codes, wq_scales, seed, 1,
                          sign_mask, dx, dw, workspace, workspace_bytes, as_stream(stream));
+}
+
+extern "C" size_t mx_grouped_linear_bwd_workspace_size(const int64_t* offs, int64_t groups,
+                                                       int64_t N, int64_t K) {
+  if (!valid_offsets(offs, groups) || N < 0 || K < 0) return 0;
+  return grouped_layout(offs, groups, N, K).total;
+}
+
+// Backward of the grouped layer: dX through the grouped product with each
+// expert's double-quantized weight, dW_e over the expert's own tokens in one
+// launch of contraction ranges (the padded token axis of Q5 and Q6).
+extern "C" int mx_grouped_linear_bwd(const void* dy, int dtype, const int64_t* offs,
+                                     int64_t groups, int64_t N, int64_t K,
+                                     const uint8_t* xq_codes, const uint8_t* xq_scales,
+                                     const uint8_t* wq_codes, const uint8_t* wq_scales,
+                                     uint64_t seed, float* dx, float* dw, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  MX_REQUIRE(dtype == MX_F32 || dtype == MX_BF16, MX_ERR_ENUM);
+  MX_REQUIRE(valid_offsets(offs, groups), MX_ERR_SHAPE);
+  MX_REQUIRE(N >= 0 && K >= 0 && N % 32 == 0 && K % 32 == 0, MX_ERR_SHAPE);
+  const int64_t E = groups, R = offs[groups];
+  if (N == 0 || K == 0) return MX_OK;
+  MX_REQUIRE(dw, MX_ERR_NULL);
+  MX_REQUIRE(aligned16(dw), MX_ERR_ALIGN);
+  if (R > 0) {
+    MX_REQUIRE(dy && xq_codes && xq_scales && dx, MX_ERR_NULL);
+    MX_REQUIRE(aligned16(dy) && aligned16(xq_codes) && aligned16(dx), MX_ERR_ALIGN);
+  }
+  MX_REQUIRE(wq_codes && wq_scales, MX_ERR_NULL);
+  MX_REQUIRE(aligned16(wq_codes), MX_ERR_ALIGN);
+  const GroupedLayout L = grouped_layout(offs, E, N, K);
+  MX_REQUIRE(workspace && workspace_bytes >= L.total, MX_ERR_WORKSPACE);
+  MX_REQUIRE(aligned16(workspace), MX_ERR_ALIGN);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const hipStream_t st = as_stream(stream);
+
+  int s = requantize_batched_impl(wq_codes, wq_scales, E, N, K, MX_SR, seed + 4, ws + L.q4c,
+                                  ws + L.q4s, st);
+  if (s != MX_OK) return s;
+  if (R > 0) {
+    s = quantize_impl(dy, dtype, R, N, MX_ROW, MX_SR, seed + 3, 0, 0, ws + L.q3c, ws + L.q3s, st);
+    if (s != MX_OK) return s;
+    s = quantize_segments_impl(dy, dtype, R, N, offs, E, MX_SR, seed + 5, ws + L.q5c, ws + L.q5s,
+                               st);
+    if (s != MX_OK) return s;
+    s = requantize_segments_impl(xq_codes, xq_scales, R, K, offs, E, MX_SR, seed + 6, ws + L.q6c,
+                                 ws + L.q6s, st);
+    if (s != MX_OK) return s;
+    s = gemm_impl(ws + L.q3c, ws + L.q3s, ws + L.q4c, ws + L.q4s, offs, E, K, N, 1.0f, dx, K,
+                  K * N / 2, K * N / 32, st);
+    if (s != MX_OK) return s;
+  }
+  int64_t kbeg[MX_MAX_GROUPS + 1];
+  segments_padded_offsets(offs, E, kbeg);
+  return gemm_ranges_impl(ws + L.q5c, ws + L.q5s, ws + L.q6c, ws + L.q6s, N, K, L.P, kbeg, (int)E,
+                          1.0f, dw, st);
 }
 
 extern "C" const char* mx_status_string(int status) {

@@ -105,6 +105,50 @@ __global__ __launch_bounds__(256) void k_quant_row(const T* __restrict__ x, int6
   }
 }
 
+// ============================================================== row segments
+// The 32x1 quantizers can run per token segment of a grouped (mixture-of-
+// experts) layer: segment g is rows [row_off[g], row_off[g+1]); its blocks
+// start at the segment's first row and its tail is zero-padded to a multiple
+// of kSegPad rows, so the transposed output has a padded row axis of out_len
+// positions, segment g's starting at out_off[g].  n == 0: one plain segment.
+constexpr int kSegPad = 128;
+
+struct Segs {
+  int n;
+  int tile_start[MX_MAX_GROUPS + 1];   // first blockIdx.y of each segment
+  int64_t row_off[MX_MAX_GROUPS + 1];
+  int64_t out_off[MX_MAX_GROUPS + 1];
+  int64_t out_len;
+};
+
+// Rows of this workgroup's tile of height TR: input rows [row0, row0 + nreal),
+// output positions [out0, out0 + 32 nrb) of an axis of out_len.
+struct TileRows {
+  int64_t row0, out0, out_len;
+  int nreal, nrb;
+};
+
+__device__ __forceinline__ TileRows tile_rows(const Segs& s, int TR, int64_t rows) {
+  TileRows t;
+  if (s.n == 0) {
+    t.row0 = (int64_t)blockIdx.y * TR;
+    t.nreal = (int)min<int64_t>(TR, rows - t.row0);
+    t.out0 = t.row0;
+    t.nrb = t.nreal / 32;
+    t.out_len = rows;
+    return t;
+  }
+  int g = 0;
+  while (g + 1 < s.n && s.tile_start[g + 1] <= (int)blockIdx.y) ++g;
+  const int64_t k = (int64_t)blockIdx.y - s.tile_start[g];
+  t.row0 = s.row_off[g] + k * TR;
+  t.nreal = (int)min<int64_t>(TR, s.row_off[g + 1] - t.row0);
+  t.out0 = s.out_off[g] + k * TR;
+  t.nrb = (int)(min<int64_t>(TR, s.out_off[g + 1] - t.out0) / 32);
+  t.out_len = s.out_len;
+  return t;
+}
+
 // ============================================================== column blocks
 // A workgroup owns a tile of kTileR = 128 rows x 256 bytes of input (128 bf16
 // or 64 f32 columns).  Each thread loads 8 chunks of 16 bytes (coalesced) and
@@ -183,7 +227,7 @@ template <typename T, int ROUND, bool ROW, bool HAD>
 __global__ __launch_bounds__(256) void k_quant_tile(
     const T* __restrict__ x, int64_t rows, int64_t cols, uint64_t seed_row, uint64_t seed_col,
     uint32_t sign_mask, uint8_t* __restrict__ codes_row, uint8_t* __restrict__ scales_row,
-    uint8_t* __restrict__ codes_col, uint8_t* __restrict__ scales_col) {
+    uint8_t* __restrict__ codes_col, uint8_t* __restrict__ scales_col, const Segs segs) {
   constexpr int E = 16 / sizeof(T);               // elements per 16-byte chunk
   constexpr int TC = kTileRowBytes / sizeof(T);   // tile columns
   constexpr int CPR = kTileRowBytes / 16;         // chunks per tile row (16)
@@ -195,10 +239,11 @@ __global__ __launch_bounds__(256) void k_quant_tile(
   __shared__ uint8_t s_scales[TC * NRB];
 
   const int64_t col0 = (int64_t)blockIdx.x * TC;
-  const int64_t row0 = (int64_t)blockIdx.y * kTileR;
+  const TileRows tr = tile_rows(segs, kTileR, rows);
+  const int64_t row0 = tr.row0;
   const int ncols = (int)min<int64_t>(TC, cols - col0);
-  const int nrows = (int)min<int64_t>(kTileR, rows - row0);
-  const int nrb = nrows / 32;
+  const int nrows = tr.nreal;  // rows past it (segment padding) stay zero in LDS
+  const int nrb = tr.nrb;
   const int tid = threadIdx.x;
 
   // ---- load: chunk (r, c) = (j * 16 + tid / 16, tid % 16)
@@ -297,7 +342,8 @@ __global__ __launch_bounds__(256) void k_quant_tile(
     }
   }
   __syncthreads();
-  store_col_tile<TC, NRB>(s_codes, s_scales, rows, col0, ncols, row0, nrb, codes_col, scales_col);
+  store_col_tile<TC, NRB>(s_codes, s_scales, tr.out_len, col0, ncols, tr.out0, nrb, codes_col,
+                          scales_col);
 }
 
 // ============================================================== double quantization
@@ -308,6 +354,9 @@ __global__ __launch_bounds__(256) void k_quant_tile(
 // row) over row block rb, decodes each value exactly (E2M1 magnitude times
 // 2^(scale - 127); a 0xFF input scale makes the whole column block NaN) and
 // quantizes the four 32x1 blocks.  Codes are staged for 128-byte row stores.
+// blockIdx.z selects a matrix of a stack of equal [rows, cols] matrices (the
+// experts' weights); stochastic rounding indexes the stacked logical tensor.
+// Rows past a segment's end (segment padding) are zeros.
 constexpr int kRqR = 256;
 constexpr int kRqC = 128;
 
@@ -316,28 +365,40 @@ __global__ __launch_bounds__(256) void k_requant(const uint8_t* __restrict__ cod
                                                  const uint8_t* __restrict__ scales_in,
                                                  int64_t rows, int64_t cols, uint64_t seed,
                                                  uint8_t* __restrict__ codes,
-                                                 uint8_t* __restrict__ scales) {
+                                                 uint8_t* __restrict__ scales, const Segs segs) {
   constexpr int NRB = kRqR / 32;
   __shared__ uint4 s_codes[kRqC * NRB];
   __shared__ uint8_t s_scales[kRqC * NRB];
 
+  const int64_t z = blockIdx.z;
+  codes_in += z * rows * (cols / 2);
+  scales_in += z * rows * (cols / 32);
+  codes += z * rows * (cols / 2);
+  scales += z * rows * (cols / 32);
   const int64_t col0 = (int64_t)blockIdx.x * kRqC;
-  const int64_t row0 = (int64_t)blockIdx.y * kRqR;
+  const TileRows tr = tile_rows(segs, kRqR, rows);
+  const int64_t row0 = tr.row0;
   const int ncols = (int)min<int64_t>(kRqC, cols - col0);   // multiple of 32
-  const int nrows = (int)min<int64_t>(kRqR, rows - row0);
-  const int nrb = nrows / 32;
+  const int nrb = tr.nrb;
   const int64_t ld_in = cols / 2, ld_sin = cols / 32;
   const int o = threadIdx.x % 32, rb = threadIdx.x / 32;
 
   if (rb < nrb && o * 4 < ncols) {
     const int64_t c0 = col0 + o * 4;
-    const uint8_t* cp = codes_in + (row0 + rb * 32) * ld_in + c0 / 2;
-    const uint8_t* sp = scales_in + (row0 + rb * 32) * ld_sin + c0 / 32;
+    // rows at or past nreal are padding: load a valid row (never used) and zero it
     uint32_t cw[32], sw[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      cw[i] = *reinterpret_cast<const uint16_t*>(cp + i * ld_in);
-      sw[i] = sp[i * ld_sin];
+      const int64_t r = row0 + min(rb * 32 + i, tr.nreal - 1);
+      cw[i] = *reinterpret_cast<const uint16_t*>(codes_in + r * ld_in + c0 / 2);
+      sw[i] = scales_in[r * ld_sin + c0 / 32];
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (rb * 32 + i >= tr.nreal) {
+        cw[i] = 0;     // code +0
+        sw[i] = 127;   // any finite scale
+      }
     }
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
@@ -352,13 +413,15 @@ __global__ __launch_bounds__(256) void k_requant(const uint8_t* __restrict__ cod
       }
       uint32_t byte;
       const int c = o * 4 + cc;
-      const uint64_t idx0 = (uint64_t)(row0 + rb * 32) * (uint64_t)cols + (uint64_t)(col0 + c);
+      const uint64_t idx0 = (uint64_t)(z * rows + row0 + rb * 32) * (uint64_t)cols +
+                            (uint64_t)(col0 + c);
       s_codes[c * NRB + rb] = quant_col32<ROUND>(v, byte, seed, idx0, (uint64_t)cols);
       s_scales[c * NRB + rb] = (uint8_t)byte;
     }
   }
   __syncthreads();
-  store_col_tile<kRqC, NRB>(s_codes, s_scales, rows, col0, ncols, row0, nrb, codes, scales);
+  store_col_tile<kRqC, NRB>(s_codes, s_scales, tr.out_len, col0, ncols, tr.out0, nrb, codes,
+                            scales);
 }
 
 // ============================================================== rotated double quantization
@@ -535,15 +598,53 @@ static int launch_quant_row(const T* x, int64_t rows, int64_t cols, int round, u
   return launch_status();
 }
 
+static Segs plain_segs() {
+  Segs s{};
+  s.n = 0;
+  return s;
+}
+
+// Segments of tile height TR over the row offsets offs[0..groups] (host array).
+static Segs make_segs(const int64_t* offs, int64_t groups, int TR) {
+  Segs s{};
+  s.n = (int)groups;
+  s.tile_start[0] = 0;
+  s.out_off[0] = 0;
+  for (int64_t g = 0; g < groups; ++g) {
+    const int64_t n = offs[g + 1] - offs[g];
+    s.row_off[g] = offs[g];
+    s.tile_start[g + 1] = s.tile_start[g] + (int)cdiv(n, TR);
+    s.out_off[g + 1] = s.out_off[g] + cdiv(n, kSegPad) * kSegPad;
+  }
+  s.row_off[groups] = offs[groups];
+  s.out_len = s.out_off[groups];
+  return s;
+}
+
+// Start of each segment on the padded row axis (out[0..groups], out[groups] = total).
+void segments_padded_offsets(const int64_t* offs, int64_t groups, int64_t* out) {
+  out[0] = 0;
+  for (int64_t g = 0; g < groups; ++g)
+    out[g + 1] = out[g] + cdiv(offs[g + 1] - offs[g], kSegPad) * kSegPad;
+}
+
+int64_t segments_padded_rows(const int64_t* offs, int64_t groups) {
+  int64_t p = 0;
+  for (int64_t g = 0; g < groups; ++g) p += cdiv(offs[g + 1] - offs[g], kSegPad) * kSegPad;
+  return p;
+}
+
 // Column blocks (ROW = false) or both block shapes from one read (ROW = true).
 template <typename T, bool ROW>
 static int launch_quant_tile(const T* x, int64_t rows, int64_t cols, int round, uint64_t seed_row,
                              uint64_t seed_col, int had, uint32_t mask, uint8_t* codes_row,
                              uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
-                             hipStream_t st) {
+                             hipStream_t st, const Segs& segs = plain_segs()) {
   constexpr int TC = kTileRowBytes / sizeof(T);
-  const dim3 grid((unsigned)cdiv(cols, TC), (unsigned)cdiv(rows, kTileR)), block(256);
-#define MX_TILE_ARGS x, rows, cols, seed_row, seed_col, mask, codes_row, scales_row, codes_col, scales_col
+  const unsigned ty = segs.n ? (unsigned)segs.tile_start[segs.n] : (unsigned)cdiv(rows, kTileR);
+  if (ty == 0) return MX_OK;
+  const dim3 grid((unsigned)cdiv(cols, TC), ty), block(256);
+#define MX_TILE_ARGS x, rows, cols, seed_row, seed_col, mask, codes_row, scales_row, codes_col, scales_col, segs
   constexpr bool kHad = !ROW || sizeof(T) == 2;  // rotated row pass: bf16 only
   if (round == MX_RNE) {
     if (had && kHad) k_quant_tile<T, MX_RNE, ROW, kHad><<<grid, block, 0, st>>>(MX_TILE_ARGS);
@@ -575,15 +676,56 @@ int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, int axis
                                                seed, had, mask, nullptr, nullptr, codes, scales, st);
 }
 
+static int launch_requant(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
+                          int64_t cols, int round, uint64_t seed, uint8_t* codes, uint8_t* scales,
+                          int64_t batch, const Segs& segs, hipStream_t st) {
+  const unsigned ty = segs.n ? (unsigned)segs.tile_start[segs.n] : (unsigned)cdiv(rows, kRqR);
+  if (ty == 0 || batch == 0) return MX_OK;
+  const dim3 grid((unsigned)cdiv(cols, kRqC), ty, (unsigned)batch), block(256);
+  if (round == MX_RNE)
+    k_requant<MX_RNE><<<grid, block, 0, st>>>(codes_in, scales_in, rows, cols, seed, codes, scales, segs);
+  else
+    k_requant<MX_SR><<<grid, block, 0, st>>>(codes_in, scales_in, rows, cols, seed, codes, scales, segs);
+  return launch_status();
+}
+
 int requantize_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows, int64_t cols,
                     int round, uint64_t seed, uint8_t* codes, uint8_t* scales, hipStream_t st) {
   if (rows == 0 || cols == 0) return MX_OK;
-  const dim3 grid((unsigned)cdiv(cols, kRqC), (unsigned)cdiv(rows, kRqR)), block(256);
-  if (round == MX_RNE)
-    k_requant<MX_RNE><<<grid, block, 0, st>>>(codes_in, scales_in, rows, cols, seed, codes, scales);
-  else
-    k_requant<MX_SR><<<grid, block, 0, st>>>(codes_in, scales_in, rows, cols, seed, codes, scales);
-  return launch_status();
+  return launch_requant(codes_in, scales_in, rows, cols, round, seed, codes, scales, 1,
+                        plain_segs(), st);
+}
+
+// A stack of `batch` [rows, cols] matrices, each requantized on its own (the
+// experts' weights); stochastic rounding indexes the stacked [batch*rows, cols].
+int requantize_batched_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t batch,
+                            int64_t rows, int64_t cols, int round, uint64_t seed, uint8_t* codes,
+                            uint8_t* scales, hipStream_t st) {
+  if (rows == 0 || cols == 0) return MX_OK;
+  return launch_requant(codes_in, scales_in, rows, cols, round, seed, codes, scales, batch,
+                        plain_segs(), st);
+}
+
+// 32x1 blocks per row segment (offs: host array of groups+1 row offsets).
+int quantize_segments_impl(const void* x, int dtype, int64_t rows, int64_t cols,
+                           const int64_t* offs, int64_t groups, int round, uint64_t seed,
+                           uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  if (rows == 0 || cols == 0) return MX_OK;
+  const Segs s = make_segs(offs, groups, kTileR);
+  return dtype == MX_BF16
+             ? launch_quant_tile<uint16_t, false>(static_cast<const uint16_t*>(x), rows, cols, round,
+                                                  0, seed, 0, 0, nullptr, nullptr, codes, scales,
+                                                  st, s)
+             : launch_quant_tile<float, false>(static_cast<const float*>(x), rows, cols, round, 0,
+                                               seed, 0, 0, nullptr, nullptr, codes, scales, st, s);
+}
+
+int requantize_segments_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
+                             int64_t cols, const int64_t* offs, int64_t groups, int round,
+                             uint64_t seed, uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  if (rows == 0 || cols == 0) return MX_OK;
+  return launch_requant(codes_in, scales_in, rows, cols, round, seed, codes, scales, 1,
+                        make_segs(offs, groups, kRqR), st);
 }
 
 int quantize_dual_impl(const void* x, int dtype, int64_t rows, int64_t cols, int round,
@@ -691,6 +833,49 @@ extern "C" int mx_requantize_rht(const uint8_t* codes_in, const uint8_t* scales_
   MX_REQUIRE(aligned16(codes_in) && aligned16(codes_out), MX_ERR_ALIGN);
   return requantize_rht_impl(codes_in, scales_in, rows, cols, round, seed, sign_mask, codes_out,
                              scales_out, as_stream(stream));
+}
+
+static bool valid_offsets(const int64_t* offs, int64_t groups, int64_t rows) {
+  if (!offs || groups < 1 || groups > MX_MAX_GROUPS || offs[0] != 0 || offs[groups] != rows)
+    return false;
+  for (int64_t g = 0; g < groups; ++g)
+    if (offs[g + 1] < offs[g]) return false;
+  return true;
+}
+
+extern "C" int64_t mx_segments_padded_rows(const int64_t* offs, int64_t groups) {
+  if (!offs || groups < 1 || groups > MX_MAX_GROUPS || offs[0] != 0) return -1;
+  for (int64_t g = 0; g < groups; ++g)
+    if (offs[g + 1] < offs[g]) return -1;
+  return segments_padded_rows(offs, groups);
+}
+
+extern "C" int mx_quantize_segments(const void* x, int dtype, int64_t rows, int64_t cols,
+                                    const int64_t* offs, int64_t groups, int round, uint64_t seed,
+                                    uint8_t* codes, uint8_t* scales, void* stream) {
+  MX_REQUIRE(dtype == MX_F32 || dtype == MX_BF16, MX_ERR_ENUM);
+  MX_REQUIRE(round == MX_RNE || round == MX_SR, MX_ERR_ENUM);
+  MX_REQUIRE(rows >= 0 && cols >= 0 && cols % 8 == 0, MX_ERR_SHAPE);
+  MX_REQUIRE(valid_offsets(offs, groups, rows), MX_ERR_SHAPE);
+  if (rows == 0 || cols == 0) return MX_OK;
+  MX_REQUIRE(x && codes && scales, MX_ERR_NULL);
+  MX_REQUIRE(aligned16(x) && aligned16(codes), MX_ERR_ALIGN);
+  return quantize_segments_impl(x, dtype, rows, cols, offs, groups, round, seed, codes, scales,
+                                as_stream(stream));
+}
+
+extern "C" int mx_requantize_segments(const uint8_t* codes_in, const uint8_t* scales_in,
+                                      int64_t rows, int64_t cols, const int64_t* offs,
+                                      int64_t groups, int round, uint64_t seed,
+                                      uint8_t* codes_out, uint8_t* scales_out, void* stream) {
+  MX_REQUIRE(round == MX_RNE || round == MX_SR, MX_ERR_ENUM);
+  MX_REQUIRE(rows >= 0 && cols >= 0 && cols % 32 == 0, MX_ERR_SHAPE);
+  MX_REQUIRE(valid_offsets(offs, groups, rows), MX_ERR_SHAPE);
+  if (rows == 0 || cols == 0) return MX_OK;
+  MX_REQUIRE(codes_in && scales_in && codes_out && scales_out, MX_ERR_NULL);
+  MX_REQUIRE(aligned16(codes_in) && aligned16(codes_out), MX_ERR_ALIGN);
+  return requantize_segments_impl(codes_in, scales_in, rows, cols, offs, groups, round, seed,
+                                  codes_out, scales_out, as_stream(stream));
 }
 
 extern "C" int mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,

@@ -33,12 +33,18 @@ SIGNATURES = {
     "mx_requantize": ([_P, _P, _i64, _i64, _i32, _u64, _P, _P, _P], _i32),
     "mx_quantize_dual_rht": ([_P, _i32, _i64, _i64, _i32, _u64, _u64, _u32, _P, _P, _P, _P, _P], _i32),
     "mx_requantize_rht": ([_P, _P, _i64, _i64, _i32, _u64, _u32, _P, _P, _P], _i32),
+    "mx_segments_padded_rows": ([_P, _i64], _i64),
+    "mx_quantize_segments": ([_P, _i32, _i64, _i64, _P, _i64, _i32, _u64, _P, _P, _P], _i32),
+    "mx_requantize_segments": ([_P, _P, _i64, _i64, _P, _i64, _i32, _u64, _P, _P, _P], _i32),
     "mx_dequantize": ([_P, _P, _i64, _i64, _i32, _i32, _u32, _P, _i32, _P], _i32),
     "mx_gemm": ([_P, _P, _P, _P, _i64, _i64, _i64, _f32, _P, _i64, _P], _i32),
     "mx_gemm_grouped": ([_P, _P, _P, _P, _P, _i64, _i64, _i64, _f32, _P, _P], _i32),
     "mx_linear_fwd": ([_P, _P, _i32, _i64, _i64, _i64, _P, _P, _P, _P, _P, _P], _i32),
     "mx_linear_bwd_workspace_size": ([_i64, _i64, _i64], _sz),
     "mx_linear_bwd": ([_P, _i32, _i64, _i64, _i64, _P, _P, _P, _P, _u64, _P, _P, _P, _sz, _P], _i32),
+    "mx_grouped_linear_bwd_workspace_size": ([_P, _i64, _i64, _i64], _sz),
+    "mx_grouped_linear_bwd": ([_P, _i32, _P, _i64, _i64, _i64, _P, _P, _P, _P, _u64, _P, _P, _P, _sz,
+                               _P], _i32),
     "mx_linear_fwd_rht": ([_P, _P, _i32, _i64, _i64, _i64, _u32, _P, _P, _P, _P, _P, _P], _i32),
     "mx_linear_bwd_rht": ([_P, _i32, _i64, _i64, _i64, _P, _P, _P, _P, _u64, _u32, _P, _P, _P, _sz,
                            _P], _i32),
@@ -154,9 +160,49 @@ def mx_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, alpha, c, ldc, stream
                                     M, N, K, alpha, _ptr(c), ldc, _stream(stream)))
 
 
+def _offsets(offs):
+    """Host int64 array of the offsets (kept alive by the caller's reference)."""
+    return (ctypes.c_int64 * len(offs))(*[int(o) for o in offs])
+
+
+def mx_segments_padded_rows(offs, groups) -> int:
+    arr = _offsets(offs)
+    return int(lib().mx_segments_padded_rows(ctypes.addressof(arr), groups))
+
+
+def mx_quantize_segments(x, dtype, rows, cols, offs, groups, round, seed, codes, scales,
+                         stream=None):
+    arr = _offsets(offs)
+    _check("mx_quantize_segments", lib().mx_quantize_segments(
+        _ptr(x), dtype, rows, cols, ctypes.addressof(arr), groups, round, seed, _ptr(codes),
+        _ptr(scales), _stream(stream)))
+
+
+def mx_requantize_segments(codes_in, scales_in, rows, cols, offs, groups, round, seed, codes_out,
+                           scales_out, stream=None):
+    arr = _offsets(offs)
+    _check("mx_requantize_segments", lib().mx_requantize_segments(
+        _ptr(codes_in), _ptr(scales_in), rows, cols, ctypes.addressof(arr), groups, round, seed,
+        _ptr(codes_out), _ptr(scales_out), _stream(stream)))
+
+
+def mx_grouped_linear_bwd_workspace_size(offs, groups, N, K) -> int:
+    arr = _offsets(offs)
+    return int(lib().mx_grouped_linear_bwd_workspace_size(ctypes.addressof(arr), groups, N, K))
+
+
+def mx_grouped_linear_bwd(dy, dtype, offs, groups, N, K, xq_codes, xq_scales, wq_codes, wq_scales,
+                          seed, dx, dw, workspace, workspace_bytes, stream=None):
+    arr = _offsets(offs)
+    _check("mx_grouped_linear_bwd", lib().mx_grouped_linear_bwd(
+        _ptr(dy), dtype, ctypes.addressof(arr), groups, N, K, _ptr(xq_codes), _ptr(xq_scales),
+        _ptr(wq_codes), _ptr(wq_scales), seed, _ptr(dx), _ptr(dw), _ptr(workspace),
+        workspace_bytes, _stream(stream)))
+
+
 def mx_gemm_grouped(a_codes, a_scales, b_codes, b_scales, offs, groups, N, K, alpha, c,
                     stream=None):
-    arr = (ctypes.c_int64 * len(offs))(*[int(o) for o in offs])
+    arr = _offsets(offs)
     _check("mx_gemm_grouped", lib().mx_gemm_grouped(
         _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), ctypes.addressof(arr),
         groups, N, K, alpha, _ptr(c), _stream(stream)))
@@ -291,6 +337,20 @@ def linear_bwd_rht(dy: torch.Tensor, xq, wq, M, N, K, seed, sign_mask, workspace
     dw = torch.empty((N, K), dtype=torch.float32, device=dy.device)
     mx_linear_bwd_rht(dy, dtype_code(dy), M, N, K, xq[0], xq[1], wq[0], wq[1], seed, sign_mask,
                       dx, dw, workspace, workspace.numel(), stream)
+    return dx, dw
+
+
+def grouped_linear_bwd(dy: torch.Tensor, xq, wq, offs, N, K, seed, workspace=None, stream=None):
+    """dX [R, K] and dW [groups, N, K] of a grouped layer (offs: host offsets)."""
+    G = len(offs) - 1
+    R = int(offs[-1])
+    need = mx_grouped_linear_bwd_workspace_size(offs, G, N, K)
+    if workspace is None:
+        workspace = _u8((need,), wq[0].device)
+    dx = torch.empty((R, K), dtype=torch.float32, device=wq[0].device)
+    dw = torch.empty((G, N, K), dtype=torch.float32, device=wq[0].device)
+    mx_grouped_linear_bwd(dy, dtype_code(dy), offs, G, N, K, xq[0], xq[1], wq[0], wq[1], seed, dx,
+                          dw, workspace, workspace.numel(), stream)
     return dx, dw
 
 

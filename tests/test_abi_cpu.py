@@ -137,6 +137,35 @@ def test_rotated_entry_points_validation(L):
              None) == mx.MX_ERR_NULL
 
 
+def test_segment_entry_points_validation(L):
+    import ctypes
+    offs = (ctypes.c_int64 * 4)(0, 37, 37, 100)
+    bad = (ctypes.c_int64 * 4)(0, 37, 30, 100)       # decreasing
+    a, b = ctypes.addressof(offs), ctypes.addressof(bad)
+    assert L.mx_segments_padded_rows(a, 3) == 256
+    assert L.mx_segments_padded_rows(b, 3) == -1
+    q = L.mx_quantize_segments
+    assert q(GOOD, 1, 100, 60, a, 3, 1, 5, GOOD, GOOD, None) == mx.MX_ERR_SHAPE   # cols % 8
+    assert q(GOOD, 1, 100, 64, b, 3, 1, 5, GOOD, GOOD, None) == mx.MX_ERR_SHAPE
+    assert q(GOOD, 1, 99, 64, a, 3, 1, 5, GOOD, GOOD, None) == mx.MX_ERR_SHAPE    # offs[end] != rows
+    assert q(GOOD, 1, 100, 64, a, 3, 1, 5, GOOD, None, None) == mx.MX_ERR_NULL
+    assert q(GOOD, 1, 100, 64, a, 3, 1, 5, BAD, GOOD, None) == mx.MX_ERR_ALIGN
+    r = L.mx_requantize_segments
+    assert r(GOOD, GOOD, 100, 48, a, 3, 1, 5, GOOD, GOOD, None) == mx.MX_ERR_SHAPE  # cols % 32
+    assert r(GOOD, GOOD, 100, 64, a, 3, 4, 5, GOOD, GOOD, None) == mx.MX_ERR_ENUM
+    assert r(GOOD, GOOD, 100, 64, a, 3, 1, 5, GOOD, None, None) == mx.MX_ERR_NULL
+    g = L.mx_grouped_linear_bwd
+    need = L.mx_grouped_linear_bwd_workspace_size(a, 3, 64, 96)
+    assert need > 0 and L.mx_grouped_linear_bwd_workspace_size(b, 3, 64, 96) == 0
+    args = (GOOD, GOOD, GOOD, GOOD, 7, GOOD, GOOD, GOOD)
+    assert g(GOOD, 1, a, 3, 64, 96, *args, need - 1, None) == mx.MX_ERR_WORKSPACE
+    assert g(GOOD, 1, a, 3, 64, 80, *args, need, None) == mx.MX_ERR_SHAPE
+    assert g(GOOD, 1, b, 3, 64, 96, *args, need, None) == mx.MX_ERR_SHAPE
+    assert g(GOOD, 5, a, 3, 64, 96, *args, need, None) == mx.MX_ERR_ENUM
+    assert g(GOOD, 1, a, 3, 64, 96, GOOD, GOOD, GOOD, GOOD, 7, GOOD, None, GOOD, need,
+             None) == mx.MX_ERR_NULL
+
+
 def test_deosc_validation(L):
     assert L.mx_deosc_step(GOOD, 4, 40, GOOD, GOOD, GOOD, 0, 4.0, None, None) == mx.MX_ERR_SHAPE
     assert L.mx_deosc_step(GOOD, 4, 32, GOOD, GOOD, GOOD, 1, 4.0, None, None) == mx.MX_ERR_NULL

@@ -1,0 +1,167 @@
+"""GPU parity of the grouped (mixture-of-experts) backward: the per-segment 32x1
+quantizers bit-exact (padding blocks zero), dX and every expert's dW within the
+GEMM tolerance of the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mxfp4_microscaling_quantization_amd import mx, synth
+from tests.gpu_util import (DEV, assert_bytes_equal, assert_gemm_close, host, oracle_input,
+                            to_dev_u8, upload)
+from tests.test_gpu_quant import mixed_input
+
+pytestmark = pytest.mark.gpu
+
+OFFS = [0, 0, 37, 100, 100, 261, 400]   # empty, ragged and 32-misaligned segments
+
+
+def padded_starts(offs):
+    p = [0]
+    for g in range(len(offs) - 1):
+        p.append(p[-1] + (offs[g + 1] - offs[g] + 127) // 128 * 128)
+    return p
+
+
+def check_segments(got_c, got_s, want, offs):
+    """GPU [C][P/2] codes / [C][P/32] scales against the oracle's per-segment blocks."""
+    ps = padded_starts(offs)
+    assert got_c.shape[1] * 2 == ps[-1] and got_s.shape[1] * 32 == ps[-1]
+    for g, (wc, ws) in enumerate(want):
+        p0, p32 = ps[g], wc.shape[1] * 2
+        assert_bytes_equal(got_c[:, p0 // 2:p0 // 2 + p32 // 2], wc, f"segment {g} codes")
+        assert_bytes_equal(got_s[:, p0 // 32:p0 // 32 + p32 // 32], ws, f"segment {g} scales")
+        assert not got_c[:, (p0 + p32) // 2:ps[g + 1] // 2].any(), f"segment {g} padding codes"
+        assert not got_s[:, (p0 + p32) // 32:ps[g + 1] // 32].any(), f"segment {g} padding scales"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rnd", [mx.MX_RNE, mx.MX_SR])
+def test_quantize_segments_matches_oracle(dtype, rnd):
+    R, C = OFFS[-1], 200
+    x = mixed_input(R, C, 41, dtype)
+    P = mx.mx_segments_padded_rows(OFFS, len(OFFS) - 1)
+    codes = torch.full((C, P // 2), 0x55, dtype=torch.uint8, device=DEV)
+    scales = torch.full((C, P // 32), 0x55, dtype=torch.uint8, device=DEV)
+    d = upload(x, dtype)
+    mx.mx_quantize_segments(d, mx.dtype_code(d), R, C, OFFS, len(OFFS) - 1, rnd, 77, codes, scales)
+    want = O.quantize_segments(oracle_input(x, dtype), OFFS, rnd, 77)
+    check_segments(host(codes), host(scales), want, OFFS)
+
+
+@pytest.mark.parametrize("rnd", [mx.MX_RNE, mx.MX_SR])
+def test_requantize_segments_matches_oracle(rnd):
+    R, C = OFFS[-1], 160
+    x = mixed_input(R, C, 43, "f32")
+    xq = O.quantize(x, O.ROW, O.RNE)
+    P = mx.mx_segments_padded_rows(OFFS, len(OFFS) - 1)
+    codes = torch.full((C, P // 2), 0x55, dtype=torch.uint8, device=DEV)
+    scales = torch.full((C, P // 32), 0x55, dtype=torch.uint8, device=DEV)
+    mx.mx_requantize_segments(to_dev_u8(xq[0]), to_dev_u8(xq[1]), R, C, OFFS, len(OFFS) - 1, rnd,
+                              78, codes, scales)
+    want = O.quantize_segments(O.dequantize(*xq, R, C).astype(np.float32), OFFS, rnd, 78)
+    check_segments(host(codes), host(scales), want, OFFS)
+
+
+def check_grouped_bwd(dy, dtype, xq, wq, offs, N, K, seed, rows=None, experts=None, nrows=None):
+    E = len(offs) - 1
+    gx, gw = mx.grouped_linear_bwd(upload(dy, dtype), tuple(to_dev_u8(a) for a in xq),
+                                   tuple(to_dev_u8(a) for a in wq), offs, N, K, seed)
+    gx, gw = host(gx), host(gw)
+    odx, odw, (q3, q4, q5, q6) = O.grouped_linear_bwd(oracle_input(dy, dtype), xq, wq, offs, N, K,
+                                                      seed)
+    for e in range(E):
+        r0, r1 = offs[e], offs[e + 1]
+        if r1 > r0:
+            ab = O.gemm_abs(q3[0][r0:r1], q3[1][r0:r1], q4[0][e], q4[1][e], r1 - r0, K, N)
+            assert_gemm_close(gx[r0:r1], odx[r0:r1], ab, f"dX expert {e}")
+            P = q5[e][0].shape[1] * 2
+            ab = O.gemm_abs(*q5[e], *q6[e], N, K, P)
+            assert_gemm_close(gw[e], odw[e], ab, f"dW expert {e}")
+        else:
+            assert not gw[e].any(), f"expert {e} has no tokens"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_grouped_linear_bwd_matches_oracle(dtype):
+    rng = np.random.default_rng(44)
+    E, N, K = len(OFFS) - 1, 64, 96
+    R = OFFS[-1]
+    x = rng.standard_normal((R, K)).astype(np.float32)
+    w = (rng.standard_normal((E * N, K)) * 0.02).astype(np.float32)
+    dy = (rng.standard_normal((R, N)) * 1e-3).astype(np.float32)
+    if dtype == "bf16":
+        dy = synth.f32_to_bf16_bits(dy)
+    xq, wq = O.quantize(x, O.ROW, O.RNE), O.quantize(w, O.ROW, O.RNE)
+    check_grouped_bwd(dy, dtype, xq, wq, OFFS, N, K, seed=9)
+
+
+def test_grouped_linear_bwd_single_expert_equals_dense_backward():
+    """One expert with a 32-aligned token count is the dense layer: the same bits."""
+    rng = np.random.default_rng(45)
+    M, N, K = 256, 96, 128
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    dy = synth.f32_to_bf16_bits((rng.standard_normal((M, N)) * 1e-3).astype(np.float32))
+    y, xq, wq = mx.linear_fwd(upload(x, "f32"), upload(w, "f32"))
+    dx1, dw1 = mx.linear_bwd(upload(dy, "bf16"), xq, wq, M, N, K, 5)
+    dx2, dw2 = mx.grouped_linear_bwd(upload(dy, "bf16"), xq, wq, [0, M], N, K, 5)
+    assert torch.equal(dx1, dx2)
+    assert torch.equal(dw1, dw2[0])
+
+
+def test_grouped_linear_bwd_moe_down_projection_sampled():
+    """32 experts, top-4 routing of 16384 tokens, down projection 2880 -> 2880: dY
+    [65536, 2880] bf16 N(0, 1e-3); dX checked on sampled rows, dW on sampled rows of
+    sampled experts, each against the oracle's operands for exactly those outputs."""
+    cfg = synth.moe_config(with_weights=False)
+    E, H = cfg["E"], cfg["hidden"]
+    offs = [int(o) for o in cfg["offs"]]
+    R = offs[-1]
+    rng = np.random.default_rng(46)
+    w = (rng.standard_normal((E * H, H)) * 0.02).astype(np.float32)
+    dy = synth.f32_to_bf16_bits((rng.standard_normal((R, H)) * 1e-3).astype(np.float32))
+    xin = cfg["x_down"]
+    xq_d = mx.quantize(upload(xin, "bf16"))
+    wq_d = mx.quantize(upload(w, "f32"))
+    seed = 4
+    gx, gw = mx.grouped_linear_bwd(upload(dy, "bf16"), xq_d, wq_d, offs, H, H, seed)
+    gx, gw = host(gx), host(gw)
+    xq = (host(xq_d[0]), host(xq_d[1]))
+    dyf = O.bf16_bits_to_f32(dy)
+    for e in rng.choice(E, 4, replace=False):
+        r0, r1 = offs[e], offs[e + 1]
+        # Q4 of expert e: 32x1 along N of its [H, H] weight, stacked index
+        wdeq = O.dequantize(host(wq_d[0])[e * H:(e + 1) * H], host(wq_d[1])[e * H:(e + 1) * H],
+                            H, H).astype(np.float32)
+        idx4 = (e * H + np.arange(H))[None, :] * H + np.arange(H)[:, None]  # [k][n] -> (eH+n)H+k
+        c4, s4 = O.quantize_blocks(wdeq.T.reshape(H, H // 32, 32), idx4.reshape(H, H // 32, 32),
+                                   O.SR, seed + 4)
+        q4 = (O.pack_codes(c4.reshape(H, H)), s4)
+        rows = np.sort(rng.choice(np.arange(r0, r1), 6, replace=False))
+        idx3 = rows[:, None] * H + np.arange(H)[None, :]
+        c3, s3 = O.quantize_blocks(dyf[rows].reshape(6, H // 32, 32), idx3.reshape(6, H // 32, 32),
+                                   O.SR, seed + 3)
+        q3 = (O.pack_codes(c3.reshape(6, H)), s3)
+        assert_gemm_close(gx[rows], O.gemm(*q3, *q4, 6, H, H), O.gemm_abs(*q3, *q4, 6, H, H),
+                          f"dX expert {e}")
+        # dW_e rows n: Q5 column n of dY_e, Q6 of the expert's Q_D(X) over its tokens
+        ns = np.sort(rng.choice(H, 6, replace=False))
+        # the segment blocks of the sampled columns, with the [R, H] element indices
+        n = r1 - r0
+        P = (n + 31) // 32 * 32
+        v = np.zeros((6, P), np.float32)
+        v[:, :n] = dyf[r0:r1][:, ns].T
+        idx5 = (r0 + np.arange(P))[None, :] * H + ns[:, None]
+        c5, s5 = O.quantize_blocks(v.reshape(6, P // 32, 32), idx5.reshape(6, P // 32, 32), O.SR,
+                                   seed + 5)
+        q5 = (O.pack_codes(c5.reshape(6, P)), s5)
+        xdeq = O.dequantize(xq[0][r0:r1], xq[1][r0:r1], n, H).astype(np.float32)
+        vx = np.zeros((H, P), np.float32)
+        vx[:, :n] = xdeq.T
+        idx6 = (r0 + np.arange(P))[None, :] * H + np.arange(H)[:, None]
+        c6, s6 = O.quantize_blocks(vx.reshape(H, P // 32, 32), idx6.reshape(H, P // 32, 32), O.SR,
+                                   seed + 6)
+        q6 = (O.pack_codes(c6.reshape(H, P)), s6)
+        assert_gemm_close(gw[e][ns], O.gemm(*q5, *q6, 6, H, P), O.gemm_abs(*q5, *q6, 6, H, P),
+                          f"dW expert {e}")
