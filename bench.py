@@ -33,8 +33,8 @@ PEAK_FP4_TFLOPS = 10100.0
 # from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB copy, valid for
 # the GEMM source with this sha256 only (the per-launch table is kept with the
 # committed profiles).
-GEMM_TRAFFIC = {"sha256": "bff6c0370dc90652edd013ecd1f58efbebcbe952034ef056a1c2a574c7927b1f",
-                "bytes_per_launch": 670795827}
+GEMM_TRAFFIC = {"sha256": "c920416b2fcfda757de5d561a0240ccc61cedf928db7e3c538457d7e8ecc9386",
+                "bytes_per_launch": 670457142}
 
 
 def gemm_traffic():
