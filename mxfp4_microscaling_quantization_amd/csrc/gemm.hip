@@ -97,6 +97,12 @@ __device__ __forceinline__ void dma4(const void* g, void* lds) {
                : "s"(lds_addr(lds)), "v"(g)
                : "memory", "m0");
 }
+__device__ __forceinline__ void dma2(const void* g, void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, off"
+               :
+               : "s"(lds_addr(lds)), "v"(g)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void dma1(const void* g, void* lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ubyte %1, off"
                :
@@ -110,21 +116,23 @@ __device__ __forceinline__ void dma1(const void* g, void* lds) {
 // reading chunk c of 16 consecutive rows hit 16 different bank groups.  One
 // direct-to-LDS load moves 16 rows (4 lanes per row, 64 contiguous bytes of
 // global memory).
-// Scales: a dword DMA puts lane i's 4 bytes at [4i, 4i+4) and a byte DMA puts
-// lane i's byte in the low byte of dword i.  With 4-byte aligned scale rows
+// Scales: a dword DMA puts lane i's 4 bytes at [4i, 4i+4); a ushort (byte) DMA
+// puts lane i's 2 bytes (byte) zero-extended in dword i.  With 4-byte aligned scale rows
 // (K/32 % 4 == 0) one dword per row carries the step's four scale bytes:
 // layout [rows][4] bytes.  Otherwise one byte per dword: layout [4][rows] dwords.
 // Scale modes: kScGroup -- K/32 % 16 == 0: one 16-byte load per row brings the
 // scales of four K-steps into a separate double buffer [rows][16 B] once per
 // four steps (a quarter of the cache lines a per-step load touches);
 // kScDword -- K/32 % 4 == 0: one dword per row and step, layout [rows][4];
+// kScShort -- K/32 % 2 == 0: two 2-byte loads per row and step, layout [2][rows]
+// dwords (bytes 0-1 and 2-3 of the step);
 // kScByte -- otherwise: one byte per row and step, layout [4][rows] dwords.
-enum { kScGroup = 0, kScDword = 1, kScByte = 2 };
+enum { kScGroup = 0, kScDword = 1, kScByte = 2, kScShort = 3 };
 
 template <int ROWS, int SC>
 struct TileLds {
   uint4 codes[ROWS * 4];
-  uint32_t scales[SC == kScGroup ? 1 : (SC == kScDword ? ROWS : ROWS * 4)];
+  uint32_t scales[SC == kScGroup ? 1 : (SC == kScDword ? ROWS : (SC == kScShort ? ROWS * 2 : ROWS * 4))];
 };
 
 template <int BM, int BN, int SC>
@@ -150,10 +158,11 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
   constexpr int LA = BM / 16 / NW;  // code DMAs per wave per step, A (16 rows each)
   constexpr int LB = BN / 16 / NW;
   constexpr int QG = (BM + BN) / 64;                 // 64-row groups of both operands
-  constexpr int QW = (SC == kScByte ? 4 * QG : QG) / NW;  // scale DMAs per wave per step (or group)
+  constexpr int QJ = SC == kScByte ? 4 * QG : (SC == kScShort ? 2 * QG : QG);  // scale jobs
+  constexpr int QW = QJ / NW;  // scale DMAs per wave per step (or group)
   constexpr int LC = LA + LB + (SC == kScGroup ? 0 : QW);  // per-step vector-memory instructions
   static_assert(LA * NW * 16 == BM && LB * NW * 16 == BN, "tile/wave mismatch");
-  static_assert(QW * NW == (SC == kScByte ? 4 * QG : QG) && BM % 64 == 0 && BN % 64 == 0, "scale jobs");
+  static_assert(QW * NW == QJ && BM % 64 == 0 && BN % 64 == 0, "scale jobs");
   static_assert(STAGES == 4 && 2 * LC + QW < 64, "pipeline depth");
 
   // The LDS ring (contiguous, reused by the epilogue); every access uses a
@@ -229,19 +238,21 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
     b_src[j] = Bg + row * ldk + k0 / 2 + dc * 16;
   }
   // scale jobs: job q covers 64 rows (lane = row) of A (q % QG < BM/64) or B,
-  // for all 32-blocks of a step (dword), of four steps (group) or for 32-block
-  // q / QG (byte mode)
+  // for all 32-blocks of a step (dword), of four steps (group), for 32-blocks
+  // 2 (q / QG) and 2 (q / QG) + 1 (short mode) or for 32-block q / QG (byte mode)
   const uint8_t* s_src[QW];
   int s_dst[QW];  // dword / uint4 offset in the A or B scale area, B marked by +2^20
 #pragma unroll
   for (int j = 0; j < QW; ++j) {
     const int q = wave * QW + j;
-    const int grp = q % QG, kb = SC == kScByte ? q / QG : 0;
+    const int grp = q % QG, part = (SC == kScByte || SC == kScShort) ? q / QG : 0;
+    const int kb = SC == kScShort ? 2 * part : part;  // first 32-block the job loads
     const bool isA = grp < BM / 64;
     const int r0 = (isA ? grp : grp - BM / 64) * 64;
     const int64_t row = isA ? lmin(m0 + r0 + lane, a_last) : lmin(n0 + r0 + lane, N - 1);
     s_src[j] = (isA ? SA : SBg) + row * lds + k0 / 32 + kb;
-    s_dst[j] = (SC == kScByte ? kb * (isA ? BM : BN) + r0 : r0) + (isA ? 0 : (1 << 20));
+    s_dst[j] = ((SC == kScByte || SC == kScShort) ? part * (isA ? BM : BN) + r0 : r0) +
+               (isA ? 0 : (1 << 20));
   }
 
   auto issue = [&](int kt, auto S) {
@@ -262,6 +273,10 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
         uint32_t* dst = isB ? &tb.scales[s_dst[j] - (1 << 20)] : &ta.scales[s_dst[j]];
         if (SC == kScDword) {
           dma4(s_src[j] + (int64_t)kt * 4, dst);
+        } else if (SC == kScShort) {
+          // bytes [4 kt + kb, 4 kt + kb + 2), clamped into the row (kc_blocks >= 2)
+          const int kb = 2 * ((wave * QW + j) / QG);
+          dma2(s_src[j] + lmin((int64_t)kt * 4, kc_blocks - 2 - kb), dst);
         } else {
           const int kb = (wave * QW + j) / QG;
           dma1(s_src[j] + lmin((int64_t)kt * 4, kc_blocks - 1 - kb), dst);
@@ -316,6 +331,9 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
       const int row = wm_off + t * 32 + lr;
       if constexpr (SC == kScByte) {
         sa[t] = (uint32_t)sab[4 * (lh * BM + row)] | ((uint32_t)sab[4 * ((2 + lh) * BM + row)] << 16);
+      } else if constexpr (SC == kScShort) {
+        const uint32_t* s32 = reinterpret_cast<const uint32_t*>(sab);
+        sa[t] = (s32[row] | (s32[BM + row] << 16)) >> (8 * lh);
       } else {
         const uint32_t w = *reinterpret_cast<const uint32_t*>(
             sab + (SC == kScGroup ? row * 16 + P * 4 : row * 4));
@@ -327,6 +345,9 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
       const int row = wn_off + t * 32 + lr;
       if constexpr (SC == kScByte) {
         sb[t] = (uint32_t)sbb[4 * (lh * BN + row)] | ((uint32_t)sbb[4 * ((2 + lh) * BN + row)] << 16);
+      } else if constexpr (SC == kScShort) {
+        const uint32_t* s32 = reinterpret_cast<const uint32_t*>(sbb);
+        sb[t] = (s32[row] | (s32[BN + row] << 16)) >> (8 * lh);
       } else {
         const uint32_t w = *reinterpret_cast<const uint32_t*>(
             sbb + (SC == kScGroup ? row * 16 + P * 4 : row * 4));
@@ -567,8 +588,11 @@ static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
                    (reinterpret_cast<uintptr_t>(sb) & 3u) == 0 && b_stride_scales % 4 == 0;
   const bool al16 = (reinterpret_cast<uintptr_t>(sa) & 15u) == 0 &&
                     (reinterpret_cast<uintptr_t>(sb) & 15u) == 0 && b_stride_scales % 16 == 0;
+  const bool al2 = (reinterpret_cast<uintptr_t>(sa) & 1u) == 0 &&
+                   (reinterpret_cast<uintptr_t>(sb) & 1u) == 0 && b_stride_scales % 2 == 0;
   // scale rows of every split must start aligned as well (group mode reads 16
-  // bytes of four steps, dword mode 4 bytes of one)
+  // bytes of four steps, dword mode 4 bytes of one; every split starts at a
+  // multiple of 128 K-values, i.e. 4 scale bytes)
   bool k512 = true, k128 = true;
   for (int s = 0; s < sp.n; ++s) {
     k512 = k512 && sp.kbeg[s] % 512 == 0;
@@ -576,16 +600,20 @@ static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
   }
   const int sc = ((K / 32) % 16 == 0 && al16 && k512)
                      ? kScGroup
-                     : (((K / 32) % 4 == 0 && al4 && k128) ? kScDword : kScByte);
+                     : (((K / 32) % 4 == 0 && al4 && k128)
+                            ? kScDword
+                            : (((K / 32) % 2 == 0 && al2 && k128) ? kScShort : kScByte));
   const bool big = tiles256 * sp.n >= 512;
 #define MX_GEMM_ARGS a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, sp, st
   if (big) {
     if (sc == kScGroup) return launch_gemm<256, 256, 2, 2, kScGroup>(MX_GEMM_ARGS);
     if (sc == kScDword) return launch_gemm<256, 256, 2, 2, kScDword>(MX_GEMM_ARGS);
+    if (sc == kScShort) return launch_gemm<256, 256, 2, 2, kScShort>(MX_GEMM_ARGS);
     return launch_gemm<256, 256, 2, 2, kScByte>(MX_GEMM_ARGS);
   }
   if (sc == kScGroup) return launch_gemm<128, 128, 2, 2, kScGroup>(MX_GEMM_ARGS);
   if (sc == kScDword) return launch_gemm<128, 128, 2, 2, kScDword>(MX_GEMM_ARGS);
+  if (sc == kScShort) return launch_gemm<128, 128, 2, 2, kScShort>(MX_GEMM_ARGS);
   return launch_gemm<128, 128, 2, 2, kScByte>(MX_GEMM_ARGS);
 #undef MX_GEMM_ARGS
 }
