@@ -83,11 +83,18 @@ __device__ __forceinline__ uint32_t sm64_top24(uint64_t z) {
   return h >> 8;
 }
 
-__device__ __forceinline__ uint64_t sm64_full(uint64_t z) {
+// Stochastic rounding draws one output per adjacent pair (2i, 2i+1) of a block,
+// keyed by element 2i's index: element 2i takes bits 40..63 of the output, element
+// 2i+1 bits 8..31.  In the final z ^ (z >> 31), bits 8..31 of the shifted term are
+// bits 39..62 of z, i.e. bits 7..30 of the high word: (hi << 1) at bits 8..31.
+__device__ __forceinline__ void sm64_pair24(uint64_t z, uint32_t& r_even, uint32_t& r_odd) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  return z ^ (z >> 31);
+  const uint32_t lo = (uint32_t)z, hi = (uint32_t)(z >> 32);
+  r_even = hi >> 8;
+  r_odd = (lo ^ (hi << 1)) >> 8;
 }
+
 
 // ---------------------------------------------------------------- cross-lane
 // DPP quad permutations: lane i of each group of 4 reads lane perm[i].

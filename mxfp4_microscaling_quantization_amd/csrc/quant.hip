@@ -38,30 +38,49 @@ __device__ __forceinline__ void load8<float>(const float* p, float v[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// Quantize the 8 values a lane holds, given the block's scale byte; returns the
-// 8 packed codes (element i in nibble i).  idx0 = logical index of v[0].
+// Codes of the adjacent block elements 2i (bits 0..3) and 2i+1 (bits 4..7) at
+// inverse scale inv; z is the generator state of the pair's key (element 2i's
+// index), whose one output gives both stochastic rounding decisions.
 template <int ROUND>
-__device__ __forceinline__ uint32_t quant8(const float v[8], uint32_t byte, uint64_t seed,
-                                           uint64_t idx0) {
+__device__ __forceinline__ uint32_t code_pair(float v0, float v1, float inv, uint64_t z) {
+  const float a0 = fabsf(v0) * inv, a1 = fabsf(v1) * inv;
+  uint32_t c0, c1;
+  if (ROUND == MX_SR) {
+    uint32_t r0, r1;
+    sm64_pair24(z, r0, r1);
+    c0 = e2m1_sr(a0, r0);
+    c1 = e2m1_sr(a1, r1);
+  } else {
+    c0 = e2m1_rne(a0);
+    c1 = e2m1_rne(a1);
+  }
+  c0 |= (__float_as_uint(v0) >> 28) & 8u;
+  c1 |= (__float_as_uint(v1) >> 28) & 8u;
+  return c0 | (c1 << 4);
+}
+
+// Quantize N consecutive values of a row block a lane holds (N even, v[0] at an
+// even position in its block), given the block's scale byte; returns the packed
+// codes (element i in nibble i).  idx0 = logical index of v[0].
+template <int ROUND, int N>
+__device__ __forceinline__ uint32_t quant_run(const float v[N], uint32_t byte, uint64_t seed,
+                                              uint64_t idx0) {
   if (byte == 255u) return 0u;
   const float inv = inv_scale_of(byte);
   uint32_t packed = 0;
-  uint64_t z = 0;
-  if (ROUND == MX_SR) z = sm64_state(seed, idx0);
+  uint64_t z = ROUND == MX_SR ? sm64_state(seed, idx0) : 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float a = fabsf(v[i]) * inv;
-    uint32_t c;
-    if (ROUND == MX_SR) {
-      c = e2m1_sr(a, sm64_top24(z));
-      z += kGamma;
-    } else {
-      c = e2m1_rne(a);
-    }
-    c |= (__float_as_uint(v[i]) >> 28) & 8u;
-    packed |= c << (4 * i);
+  for (int i = 0; i < N; i += 2) {
+    packed |= code_pair<ROUND>(v[i], v[i + 1], inv, z) << (4 * i);
+    z += 2 * kGamma;
   }
   return packed;
+}
+
+template <int ROUND>
+__device__ __forceinline__ uint32_t quant8(const float v[8], uint32_t byte, uint64_t seed,
+                                           uint64_t idx0) {
+  return quant_run<ROUND, 8>(v, byte, seed, idx0);
 }
 
 // A workgroup takes 64 x kRowU consecutive blocks per iteration; its quad j
@@ -178,20 +197,12 @@ __device__ __forceinline__ uint4 quant_col32(float v[32], uint32_t& byte_out, ui
     uint64_t z = 0, dz = 0;
     if (ROUND == MX_SR) {
       z = sm64_state(seed, idx0);
-      dz = idx_step * kGamma;
+      dz = 2 * idx_step * kGamma;   // next pair's key: two elements further down
     }
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float a = fabsf(v[i]) * inv;
-      uint32_t c;
-      if (ROUND == MX_SR) {
-        c = e2m1_sr(a, sm64_top24(z));
-        z += dz;
-      } else {
-        c = e2m1_rne(a);
-      }
-      c |= (__float_as_uint(v[i]) >> 28) & 8u;
-      w[i >> 3] |= c << (4 * (i & 7));
+    for (int i = 0; i < 32; i += 2) {
+      w[i >> 3] |= code_pair<ROUND>(v[i], v[i + 1], inv, z) << (4 * (i & 7));
+      z += dz;
     }
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
@@ -288,24 +299,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(
       m = rowblock_max_u32<E>(m);
       const uint32_t byte = scale_byte_of(m);
       const uint64_t idx0 = (uint64_t)(row0 + r) * (uint64_t)cols + (uint64_t)(col0 + lc * E);
-      uint32_t packed = 0;
-      if (byte != 255u) {
-        const float inv = inv_scale_of(byte);
-        uint64_t z = ROUND == MX_SR ? sm64_state(seed_row, idx0) : 0;
-#pragma unroll
-        for (int i = 0; i < E; ++i) {
-          const float a = fabsf(v[i]) * inv;
-          uint32_t c;
-          if (ROUND == MX_SR) {
-            c = e2m1_sr(a, sm64_top24(z));
-            z += kGamma;
-          } else {
-            c = e2m1_rne(a);
-          }
-          c |= (__float_as_uint(v[i]) >> 28) & 8u;
-          packed |= c << (4 * i);
-        }
-      }
+      const uint32_t packed = quant_run<ROUND, E>(v, byte, seed_row, idx0);
       if constexpr (E == 8) reinterpret_cast<uint32_t*>(codes_row)[idx0 / 8] = packed;
       else reinterpret_cast<uint16_t*>(codes_row)[idx0 / 4] = (uint16_t)packed;
       if (lc % (32 / E) == 0) scales_row[idx0 / 32] = (uint8_t)byte;

@@ -33,9 +33,11 @@ Readings taken where the pages are silent (each is also listed in the design
 notes): ties round to the even code; values above 6 saturate to 6; the sign bit
 always copies the input's sign bit; an all-zero block has scale byte 0; a
 non-finite block gets scale byte 0xFF and zero codes; stochastic rounding rounds
-up iff r24 < floor(t) with t the 2^24-scaled distance to the lower neighbour and
-r24 the top 24 bits of SplitMix64(seed, idx) (Steele, Lea & Flood, OOPSLA 2014);
-idx is the row-major index in the logical input tensor; codes pack element 2j
+up iff r24 < floor(t) with t the 2^24-scaled distance to the lower neighbour;
+the adjacent elements 2i, 2i+1 of a block share one output of SplitMix64(seed,
+idx) (Steele, Lea & Flood, OOPSLA 2014), idx the even element's row-major index
+in the logical input tensor: the even element takes bits 40..63 as r24, the odd
+one bits 8..31; codes pack element 2j
 in the low nibble of byte j; 32x1 outputs are stored transposed; the Hadamard
 is the unnormalised Sylvester H32 after a sign flip by a 32-bit mask, computed
 in float32 with stages h = 1, 2, 4, 8, 16.
@@ -98,8 +100,19 @@ def splitmix64(seed: int, idx) -> np.ndarray:
 
 
 def sr_bits24(seed: int, idx) -> np.ndarray:
-    """The 24 random bits one stochastic rounding decision uses: the top 24 bits."""
-    return (splitmix64(seed, idx) >> np.uint64(40)).astype(np.int64)
+    """The 24 random bits of each stochastic rounding decision in blocks of 32.
+
+    idx: [..., 32] logical indices of the blocks' elements.  Elements 2i and 2i+1
+    of a block share the output keyed by element 2i's index: element 2i takes its
+    bits 40..63, element 2i+1 its bits 8..31 (disjoint bits of one output).
+    """
+    i = np.asarray(idx)
+    assert i.shape[-1] == BLOCK
+    z = splitmix64(seed, i[..., 0::2])
+    r = np.empty(i.shape, dtype=np.int64)
+    r[..., 0::2] = (z >> np.uint64(40)).astype(np.int64)
+    r[..., 1::2] = ((z >> np.uint64(8)) & np.uint64(0xFFFFFF)).astype(np.int64)
+    return r
 
 
 # ---------------------------------------------------------------- Hadamard

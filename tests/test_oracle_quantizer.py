@@ -68,7 +68,8 @@ def exact_block_quantize(values, rounding, seed=0, idx=None):
             else:
                 k = max(i for i, g in enumerate(GRID) if g <= a)
                 t = math.floor((a - GRID[k]) / (GRID[k + 1] - GRID[k]) * (1 << 24))
-                r24 = int(O.splitmix64(seed, idx[j])) >> 40
+                z = int(O.splitmix64(seed, idx[j - (j & 1)]))   # pair (2i, 2i+1)
+                r24 = z >> 40 if j % 2 == 0 else (z >> 8) & 0xFFFFFF
                 k = k + (1 if r24 < t else 0)
         sign = 1 if math.copysign(1.0, v) < 0 else 0
         codes.append((sign << 3) | k)
@@ -198,6 +199,27 @@ def test_splitmix64_known_answers(golden_dir):
         if line.strip() and not line.startswith("#"):
             n, hexv = line.split()
             assert int(O.splitmix64(0, int(n) - 1)) == int(hexv, 16)
+
+
+def test_sr_decisions_use_the_published_output_bits(golden_dir):
+    """Seed 0, block indices 0..31: the pair (0, 1) draws output 1, the pair (2, 3)
+    output 3 of the published sequence.  Element 2i rounds up iff its bits 40..63,
+    element 2i+1 iff its bits 8..31, are below t; each value puts t one above or
+    exactly at those bits (a = t * 2^-25 in [0, 0.5) with scale 1)."""
+    known = {}
+    for line in open(os.path.join(golden_dir, "splitmix64_seed0.txt")):
+        if line.strip() and not line.startswith("#"):
+            n, hexv = line.split()
+            known[int(n)] = int(hexv, 16)
+    r = [known[1] >> 40, (known[1] >> 8) & 0xFFFFFF, known[3] >> 40, (known[3] >> 8) & 0xFFFFFF]
+    for bump in (0, 1):
+        blk = np.zeros(32, np.float32)
+        blk[31] = 6.0                       # amax 6: scale byte 127
+        for j in range(4):
+            blk[j] = np.float32((r[j] + bump) * 2.0 ** -25)
+        codes, scales = O.quantize_blocks(blk, np.arange(32, dtype=np.int64), O.SR, seed=0)
+        assert scales == 127
+        assert codes[:4].tolist() == [bump] * 4, (bump, codes[:4])
 
 
 def test_sr_matches_exact_rationals_on_random_blocks():
