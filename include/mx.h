@@ -30,12 +30,13 @@
  *  - MX_COL quantizes 32x1 blocks along the rows and stores the result
  *    transposed: codes [cols][rows/2], scales [cols][rows/32].  So every GEMM
  *    operand is contiguous along its contraction axis.
- *  - Stochastic rounding rounds an element up iff r24 < floor(t * 2^24), with
- *    t in [0, 1) the relative distance to the lower neighbour.  The elements
- *    2i and 2i+1 of a block share output idx+1 of SplitMix64 started from
- *    `seed` (Steele, Lea & Flood, OOPSLA 2014), idx the logical row-major index
- *    of element 2i in the input: element 2i takes bits 40..63 as r24, element
- *    2i+1 bits 8..31.  The result does not depend on tiling or launch shape.
+ *  - Stochastic rounding rounds an element up iff floor(t * 2^22) + r22 >= 2^22,
+ *    with t in [0, 1) the relative distance to the lower neighbour.  The
+ *    elements 2i and 2i+1 of a block share output idx+1 of SplitMix64 started
+ *    from `seed` (Steele, Lea & Flood, OOPSLA 2014), idx the logical row-major
+ *    index of element 2i in the input: element 2i takes bits 42..63 as r22,
+ *    element 2i+1 bits 9..30.  The result does not depend on tiling or launch
+ *    shape.
  *
  * Ownership and execution
  *  - Every pointer argument is a DEVICE pointer owned by the caller, except

@@ -29,6 +29,11 @@ __device__ __forceinline__ float inv_scale_of(uint32_t byte) {
   return __uint_as_float((254u - byte) << 23);
 }
 
+// 2^e for scale byte b = e + 127, b <= 252 (b = 0 gives the float32 subnormal 2^-127).
+__device__ __forceinline__ float scale_of(uint32_t byte) {
+  return __uint_as_float(byte ? byte << 23 : 0x00400000u);
+}
+
 // ---------------------------------------------------------------- rounding
 // Nearest E2M1 magnitude index for a in [0, 8), ties to the even index.
 //  a < 1: the grid is the multiples of 0.5; adding 2^22 (ulp 0.5) rounds to
@@ -44,23 +49,24 @@ __device__ __forceinline__ uint32_t e2m1_rne(float a) {
   return a < 1.0f ? sub : nrm;
 }
 
-// Stochastic E2M1 rounding of a in [0, 8): the lower neighbour's index plus 1
-// iff r24 < floor(t * 2^24), t = (a - lo) / (hi - lo); a >= 6 gives 6.  Both
-// ranges are written as "add a complement of the random bits below the kept
-// precision and let the carry decide":
-//  a >= 1: the 22 dropped mantissa bits d equal t * 2^22, and r24 < 4d exactly
-//          when floor(r24 / 4) < d, i.e. when d + (2^22 - 1 - floor(r24 / 4))
-//          carries into the kept bit; the carry may run into the exponent (next
-//          binade), and the index is (bits >> 22) - 252 as for nearest rounding.
-//  a < 1:  F = a * 2^25 is exact and F mod 2^24 = t * 2^24 (spacing 0.5), so
-//          the index is (F + 2^24 - 1 - r24) >> 24.
-__device__ __forceinline__ uint32_t e2m1_sr(float a, uint32_t r24) {
-  const uint32_t b = __float_as_uint(a);
-  const uint32_t nrm = (b + (0x3FFFFFu - (r24 >> 2)) - 0x3F000000u) >> 22;
-  const uint32_t F = (uint32_t)(a * 33554432.0f);
-  const uint32_t sub = (F + (0xFFFFFFu - r24)) >> 24;
-  const uint32_t c = a < 1.0f ? sub : nrm;
-  return c < 7u ? c : 7u;
+// gfx950 conversions of a pair of float32 values to E2M1 codes after division by
+// a power-of-two scale (exact).  Only the low byte of the result is defined: the
+// code of v0 in bits 0..3, of v1 in bits 4..7; the sign bit always copies the
+// input's, magnitudes at or above 6 give 6 (as do NaN and Inf, which the callers
+// never pass: such blocks take the NaN scale byte and zero codes).
+//  cvt_rne_pair: nearest magnitude, ties to the even code.
+//  cvt_sr_pair:  with a = |v| / scale between neighbours lo <= a < hi and
+//                t = floor((a - lo) / (hi - lo) * 2^22), v0 takes hi iff
+//                t + (seed >> 10) >= 2^22 and v1 iff t + ((seed >> 9) & (2^22 - 1))
+//                >= 2^22 -- 22 random bits added below the kept precision.
+__device__ __forceinline__ uint32_t cvt_rne_pair(float v0, float v1, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v0, v1, scale, 0);
+}
+
+__device__ __forceinline__ uint32_t cvt_sr_pair(float v0, float v1, uint32_t seed, float scale) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  const v2f v = {v0, v1};
+  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, v, seed, scale, 0);
 }
 
 // ---------------------------------------------------------------- SplitMix64
@@ -84,17 +90,16 @@ __device__ __forceinline__ uint32_t sm64_top24(uint64_t z) {
 }
 
 // Stochastic rounding draws one output per adjacent pair (2i, 2i+1) of a block,
-// keyed by element 2i's index: element 2i takes bits 40..63 of the output, element
-// 2i+1 bits 8..31.  In the final z ^ (z >> 31), bits 8..31 of the shifted term are
-// bits 39..62 of z, i.e. bits 7..30 of the high word: (hi << 1) at bits 8..31.
-__device__ __forceinline__ void sm64_pair24(uint64_t z, uint32_t& r_even, uint32_t& r_odd) {
+// keyed by element 2i's index: element 2i reads bits 42..63 of the output,
+// element 2i+1 bits 9..30.  Returns words whose bits 10..31 (hi) and 9..30 (lo)
+// are those output bits: the final z ^ (z >> 31) leaves bits 33..63 unchanged,
+// and its low word's bits 9..30 are z's xor bits 39..60 = (hi << 1) at 9..30.
+__device__ __forceinline__ void sm64_words(uint64_t z, uint32_t& hi, uint32_t& lo) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  const uint32_t lo = (uint32_t)z, hi = (uint32_t)(z >> 32);
-  r_even = hi >> 8;
-  r_odd = (lo ^ (hi << 1)) >> 8;
+  hi = (uint32_t)(z >> 32);
+  lo = (uint32_t)z ^ (hi << 1);
 }
-
 
 // ---------------------------------------------------------------- cross-lane
 // DPP quad permutations: lane i of each group of 4 reads lane perm[i].

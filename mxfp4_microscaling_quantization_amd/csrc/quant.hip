@@ -39,24 +39,19 @@ __device__ __forceinline__ void load8<float>(const float* p, float v[8]) {
 }
 
 // Codes of the adjacent block elements 2i (bits 0..3) and 2i+1 (bits 4..7) at
-// inverse scale inv; z is the generator state of the pair's key (element 2i's
-// index), whose one output gives both stochastic rounding decisions.
+// block scale `scale`; z is the generator state of the pair's key (element 2i's
+// index), whose one output gives both stochastic rounding decisions.  Each
+// element gets a conversion of its own, so the two decisions read disjoint bits.
 template <int ROUND>
-__device__ __forceinline__ uint32_t code_pair(float v0, float v1, float inv, uint64_t z) {
-  const float a0 = fabsf(v0) * inv, a1 = fabsf(v1) * inv;
-  uint32_t c0, c1;
+__device__ __forceinline__ uint32_t code_pair(float v0, float v1, float scale, uint64_t z) {
   if (ROUND == MX_SR) {
-    uint32_t r0, r1;
-    sm64_pair24(z, r0, r1);
-    c0 = e2m1_sr(a0, r0);
-    c1 = e2m1_sr(a1, r1);
-  } else {
-    c0 = e2m1_rne(a0);
-    c1 = e2m1_rne(a1);
+    uint32_t hi, lo;
+    sm64_words(z, hi, lo);
+    const uint32_t b0 = cvt_sr_pair(v0, v1, hi, scale);  // v0 reads hi bits 10..31
+    const uint32_t b1 = cvt_sr_pair(v0, v1, lo, scale);  // v1 reads lo bits 9..30
+    return (b0 & 0x0Fu) | (b1 & 0xF0u);
   }
-  c0 |= (__float_as_uint(v0) >> 28) & 8u;
-  c1 |= (__float_as_uint(v1) >> 28) & 8u;
-  return c0 | (c1 << 4);
+  return cvt_rne_pair(v0, v1, scale) & 0xFFu;
 }
 
 // Quantize N consecutive values of a row block a lane holds (N even, v[0] at an
@@ -66,12 +61,12 @@ template <int ROUND, int N>
 __device__ __forceinline__ uint32_t quant_run(const float v[N], uint32_t byte, uint64_t seed,
                                               uint64_t idx0) {
   if (byte == 255u) return 0u;
-  const float inv = inv_scale_of(byte);
+  const float sc = scale_of(byte);
   uint32_t packed = 0;
   uint64_t z = ROUND == MX_SR ? sm64_state(seed, idx0) : 0;
 #pragma unroll
   for (int i = 0; i < N; i += 2) {
-    packed |= code_pair<ROUND>(v[i], v[i + 1], inv, z) << (4 * i);
+    packed |= code_pair<ROUND>(v[i], v[i + 1], sc, z) << (4 * i);
     z += 2 * kGamma;
   }
   return packed;
@@ -193,7 +188,7 @@ __device__ __forceinline__ uint4 quant_col32(float v[32], uint32_t& byte_out, ui
   byte_out = byte;
   uint32_t w[4] = {0, 0, 0, 0};
   if (byte != 255u) {
-    const float inv = inv_scale_of(byte);
+    const float sc = scale_of(byte);
     uint64_t z = 0, dz = 0;
     if (ROUND == MX_SR) {
       z = sm64_state(seed, idx0);
@@ -201,7 +196,7 @@ __device__ __forceinline__ uint4 quant_col32(float v[32], uint32_t& byte_out, ui
     }
 #pragma unroll
     for (int i = 0; i < 32; i += 2) {
-      w[i >> 3] |= code_pair<ROUND>(v[i], v[i + 1], inv, z) << (4 * (i & 7));
+      w[i >> 3] |= code_pair<ROUND>(v[i], v[i + 1], sc, z) << (4 * (i & 7));
       z += dz;
     }
   }

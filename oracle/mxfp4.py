@@ -33,11 +33,12 @@ Readings taken where the pages are silent (each is also listed in the design
 notes): ties round to the even code; values above 6 saturate to 6; the sign bit
 always copies the input's sign bit; an all-zero block has scale byte 0; a
 non-finite block gets scale byte 0xFF and zero codes; stochastic rounding rounds
-up iff r24 < floor(t) with t the 2^24-scaled distance to the lower neighbour;
-the adjacent elements 2i, 2i+1 of a block share one output of SplitMix64(seed,
-idx) (Steele, Lea & Flood, OOPSLA 2014), idx the even element's row-major index
-in the logical input tensor: the even element takes bits 40..63 as r24, the odd
-one bits 8..31; codes pack element 2j
+up iff floor(t * 2^22) + r22 >= 2^22 with t in [0, 1) the relative distance to
+the lower neighbour (22 random bits added below the kept precision, the carry
+decides); the adjacent elements 2i, 2i+1 of a block share one output of
+SplitMix64(seed, idx) (Steele, Lea & Flood, OOPSLA 2014), idx the even element's
+row-major index in the logical input tensor: the even element takes bits 42..63
+as r22, the odd one bits 9..30; codes pack element 2j
 in the low nibble of byte j; 32x1 outputs are stored transposed; the Hadamard
 is the unnormalised Sylvester H32 after a sign flip by a 32-bit mask, computed
 in float32 with stages h = 1, 2, 4, 8, 16.
@@ -57,7 +58,7 @@ import numpy as np
 
 __all__ = [
     "E2M1_MAGNITUDES", "ROW", "COL", "RNE", "SR", "BLOCK", "SCALE_NAN",
-    "splitmix64", "sr_bits24", "hadamard_matrix32", "fwht32_f32", "sign_vector",
+    "splitmix64", "sr_bits22", "hadamard_matrix32", "fwht32_f32", "sign_vector",
     "shared_exponent", "quantize_blocks", "pack_codes", "unpack_codes",
     "quantize", "dequantize", "requantize", "block_indices",
     "gemm", "gemm_abs", "gemm_grouped", "linear_fwd", "linear_bwd",
@@ -99,19 +100,19 @@ def splitmix64(seed: int, idx) -> np.ndarray:
     return z
 
 
-def sr_bits24(seed: int, idx) -> np.ndarray:
-    """The 24 random bits of each stochastic rounding decision in blocks of 32.
+def sr_bits22(seed: int, idx) -> np.ndarray:
+    """The 22 random bits of each stochastic rounding decision in blocks of 32.
 
     idx: [..., 32] logical indices of the blocks' elements.  Elements 2i and 2i+1
     of a block share the output keyed by element 2i's index: element 2i takes its
-    bits 40..63, element 2i+1 its bits 8..31 (disjoint bits of one output).
+    bits 42..63, element 2i+1 its bits 9..30 (disjoint bits of one output).
     """
     i = np.asarray(idx)
     assert i.shape[-1] == BLOCK
     z = splitmix64(seed, i[..., 0::2])
     r = np.empty(i.shape, dtype=np.int64)
-    r[..., 0::2] = (z >> np.uint64(40)).astype(np.int64)
-    r[..., 1::2] = ((z >> np.uint64(8)) & np.uint64(0xFFFFFF)).astype(np.int64)
+    r[..., 0::2] = (z >> np.uint64(42)).astype(np.int64)
+    r[..., 1::2] = ((z >> np.uint64(9)) & np.uint64(0x3FFFFF)).astype(np.int64)
     return r
 
 
@@ -179,12 +180,13 @@ def _round_nearest_even(a: np.ndarray) -> np.ndarray:
     return np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1)).astype(np.int64)
 
 
-def _round_stochastic(a: np.ndarray, r24: np.ndarray) -> np.ndarray:
+def _round_stochastic(a: np.ndarray, r22: np.ndarray) -> np.ndarray:
     """Stochastic rounding of a >= 0 to E2M1 magnitudes.
 
     a >= 6 saturates to 6.  Otherwise lo <= a < hi are neighbours in the set,
-    t = floor((a - lo) / (hi - lo) * 2^24) and the result is hi iff r24 < t,
-    so P(hi) = floor(t) / 2^24 -- the odds follow the distance to each neighbour.
+    t = floor((a - lo) / (hi - lo) * 2^22) and the result is hi iff
+    t + r22 >= 2^22, so P(hi) = t / 2^22 -- the odds follow the distance to each
+    neighbour.
     """
     sat = a >= 6.0
     a_in = np.where(sat, 0.0, a)
@@ -192,8 +194,8 @@ def _round_stochastic(a: np.ndarray, r24: np.ndarray) -> np.ndarray:
     k = np.clip(k, 0, 6)
     lo = E2M1_MAGNITUDES[k]
     hi = E2M1_MAGNITUDES[k + 1]
-    t = np.floor((a_in - lo) / (hi - lo) * float(1 << 24))
-    up = r24.astype(np.float64) < t
+    t = np.floor((a_in - lo) / (hi - lo) * float(1 << 22))
+    up = t + r22.astype(np.float64) >= float(1 << 22)
     return np.where(sat, 7, k + up.astype(np.int64)).astype(np.int64)
 
 
@@ -217,7 +219,7 @@ def quantize_blocks(v, idx, rounding: int = RNE, seed: int = 0,
     if rounding == RNE:
         mag = _round_nearest_even(a)
     elif rounding == SR:
-        mag = _round_stochastic(a, sr_bits24(seed, idx))
+        mag = _round_stochastic(a, sr_bits22(seed, idx))
     else:
         raise ValueError("rounding must be RNE or SR")
     sign = np.signbit(v).astype(np.int64)

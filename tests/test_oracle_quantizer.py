@@ -67,10 +67,10 @@ def exact_block_quantize(values, rounding, seed=0, idx=None):
                 k = 7
             else:
                 k = max(i for i, g in enumerate(GRID) if g <= a)
-                t = math.floor((a - GRID[k]) / (GRID[k + 1] - GRID[k]) * (1 << 24))
+                t = math.floor((a - GRID[k]) / (GRID[k + 1] - GRID[k]) * (1 << 22))
                 z = int(O.splitmix64(seed, idx[j - (j & 1)]))   # pair (2i, 2i+1)
-                r24 = z >> 40 if j % 2 == 0 else (z >> 8) & 0xFFFFFF
-                k = k + (1 if r24 < t else 0)
+                r22 = z >> 42 if j % 2 == 0 else (z >> 9) & 0x3FFFFF
+                k = k + (1 if t + r22 >= 1 << 22 else 0)
         sign = 1 if math.copysign(1.0, v) < 0 else 0
         codes.append((sign << 3) | k)
     return codes, e + 127
@@ -203,20 +203,20 @@ def test_splitmix64_known_answers(golden_dir):
 
 def test_sr_decisions_use_the_published_output_bits(golden_dir):
     """Seed 0, block indices 0..31: the pair (0, 1) draws output 1, the pair (2, 3)
-    output 3 of the published sequence.  Element 2i rounds up iff its bits 40..63,
-    element 2i+1 iff its bits 8..31, are below t; each value puts t one above or
-    exactly at those bits (a = t * 2^-25 in [0, 0.5) with scale 1)."""
+    output 3 of the published sequence.  Element 2i takes bits 42..63, element
+    2i+1 bits 9..30 as r, and rounds up iff t + r >= 2^22; each value puts t one
+    below or exactly at 2^22 - r (a = t * 2^-23 in [0, 0.5) with scale 1)."""
     known = {}
     for line in open(os.path.join(golden_dir, "splitmix64_seed0.txt")):
         if line.strip() and not line.startswith("#"):
             n, hexv = line.split()
             known[int(n)] = int(hexv, 16)
-    r = [known[1] >> 40, (known[1] >> 8) & 0xFFFFFF, known[3] >> 40, (known[3] >> 8) & 0xFFFFFF]
+    r = [known[1] >> 42, (known[1] >> 9) & 0x3FFFFF, known[3] >> 42, (known[3] >> 9) & 0x3FFFFF]
     for bump in (0, 1):
         blk = np.zeros(32, np.float32)
         blk[31] = 6.0                       # amax 6: scale byte 127
         for j in range(4):
-            blk[j] = np.float32((r[j] + bump) * 2.0 ** -25)
+            blk[j] = np.float32(((1 << 22) - r[j] - 1 + bump) * 2.0 ** -23)
         codes, scales = O.quantize_blocks(blk, np.arange(32, dtype=np.int64), O.SR, seed=0)
         assert scales == 127
         assert codes[:4].tolist() == [bump] * 4, (bump, codes[:4])
