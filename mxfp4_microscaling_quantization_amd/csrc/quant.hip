@@ -39,9 +39,10 @@ __device__ __forceinline__ void load8<float>(const float* p, float v[8]) {
 }
 
 // Codes of the adjacent block elements 2i (bits 0..3) and 2i+1 (bits 4..7) at
-// block scale `scale`; z is the generator state of the pair's key (element 2i's
-// index), whose one output gives both stochastic rounding decisions.  Each
-// element gets a conversion of its own, so the two decisions read disjoint bits.
+// block scale `scale`, in the low byte of the result (the bits above are
+// undefined); z is the generator state of the pair's key (element 2i's index),
+// whose one output gives both stochastic rounding decisions.  Each element gets
+// a conversion of its own, so the two decisions read disjoint bits.
 template <int ROUND>
 __device__ __forceinline__ uint32_t code_pair(float v0, float v1, float scale, uint64_t z) {
   if (ROUND == MX_SR) {
@@ -49,27 +50,37 @@ __device__ __forceinline__ uint32_t code_pair(float v0, float v1, float scale, u
     sm64_words(z, hi, lo);
     const uint32_t b0 = cvt_sr_pair(v0, v1, hi, scale);  // v0 reads hi bits 10..31
     const uint32_t b1 = cvt_sr_pair(v0, v1, lo, scale);  // v1 reads lo bits 9..30
-    return (b0 & 0x0Fu) | (b1 & 0xF0u);
+    return (b0 & 0x0Fu) | (b1 & ~0x0Fu);
   }
-  return cvt_rne_pair(v0, v1, scale) & 0xFFu;
+  return cvt_rne_pair(v0, v1, scale);
 }
 
-// Quantize N consecutive values of a row block a lane holds (N even, v[0] at an
+// The low bytes of b0..b3 as one word, b0 in bits 0..7 (byte permutes; the
+// bytes above each low byte are ignored).
+__device__ __forceinline__ uint32_t low_bytes4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  const uint32_t l = __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u);  // [b0, b1, 0, 0]
+  const uint32_t h = __builtin_amdgcn_perm(b3, b2, 0x0C0C0400u);  // [b2, b3, 0, 0]
+  return __builtin_amdgcn_perm(h, l, 0x05040100u);
+}
+
+// Quantize N = 4 or 8 consecutive values of a row block a lane holds (v[0] at an
 // even position in its block), given the block's scale byte; returns the packed
 // codes (element i in nibble i).  idx0 = logical index of v[0].
 template <int ROUND, int N>
 __device__ __forceinline__ uint32_t quant_run(const float v[N], uint32_t byte, uint64_t seed,
                                               uint64_t idx0) {
+  static_assert(N == 4 || N == 8, "runs of 4 or 8 values");
   if (byte == 255u) return 0u;
   const float sc = scale_of(byte);
-  uint32_t packed = 0;
+  uint32_t b[N / 2];
   uint64_t z = ROUND == MX_SR ? sm64_state(seed, idx0) : 0;
 #pragma unroll
-  for (int i = 0; i < N; i += 2) {
-    packed |= code_pair<ROUND>(v[i], v[i + 1], sc, z) << (4 * i);
+  for (int p = 0; p < N / 2; ++p) {
+    b[p] = code_pair<ROUND>(v[2 * p], v[2 * p + 1], sc, z);
     z += 2 * kGamma;
   }
-  return packed;
+  if constexpr (N == 8) return low_bytes4(b[0], b[1], b[2], b[3]);
+  else return __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);
 }
 
 template <int ROUND>
@@ -194,11 +205,14 @@ __device__ __forceinline__ uint4 quant_col32(float v[32], uint32_t& byte_out, ui
       z = sm64_state(seed, idx0);
       dz = 2 * idx_step * kGamma;   // next pair's key: two elements further down
     }
+    uint32_t b[16];
 #pragma unroll
-    for (int i = 0; i < 32; i += 2) {
-      w[i >> 3] |= code_pair<ROUND>(v[i], v[i + 1], sc, z) << (4 * (i & 7));
+    for (int p = 0; p < 16; ++p) {
+      b[p] = code_pair<ROUND>(v[2 * p], v[2 * p + 1], sc, z);
       z += dz;
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = low_bytes4(b[4 * q], b[4 * q + 1], b[4 * q + 2], b[4 * q + 3]);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
@@ -241,8 +255,11 @@ __global__ __launch_bounds__(256) void k_quant_tile(
   constexpr int NRB = kTileR / 32;                // row blocks per tile (4)
   constexpr int NLOAD = kTileR * CPR / 256;       // chunks per thread (8)
   __shared__ uint32_t s_in[kTileR * kTileRowBytes / 4];
-  __shared__ uint4 s_codes[TC * NRB];
   __shared__ uint8_t s_scales[TC * NRB];
+  // Once the column pass holds its values in registers the tile is no longer
+  // read; its first TC * NRB * 16 bytes then stage the column-block codes.
+  static_assert(TC * NRB * 16 <= kTileR * kTileRowBytes, "code staging fits the tile");
+  uint4* const s_codes = reinterpret_cast<uint4*>(s_in);
 
   const int64_t col0 = (int64_t)blockIdx.x * TC;
   const TileRows tr = tile_rows(segs, kTileR, rows);
@@ -305,10 +322,14 @@ __global__ __launch_bounds__(256) void k_quant_tile(
   // ---- column pass (32x1 blocks) from LDS
   {
     const int p = tid % 64, rb = tid / 64;
-    if (rb < nrb && p * CPT < ncols) {
-      uint32_t raw[32];
+    const bool active = rb < nrb && p * CPT < ncols;
+    uint32_t raw[32];
+    if (active) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) raw[i] = s_in[(rb * 32 + i) * (kTileRowBytes / 4) + p];
+    }
+    __syncthreads();  // every thread has read the tile: s_codes may overwrite it
+    if (active) {
 #pragma unroll
       for (int cc = 0; cc < CPT; ++cc) {
         float v[32];
