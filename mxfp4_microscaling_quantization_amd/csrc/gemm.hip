@@ -51,9 +51,25 @@ struct GemmGroups {
 // the experts' weight gradients (each over its own token range).
 struct GemmSplit {
   int n;
+  int stream_c;                       // 1: final outputs, stored non-temporally
   int64_t c_stride;                   // elements between the splits' outputs
   int64_t kbeg[MX_MAX_GROUPS + 1];
 };
+
+// 16-byte store of C.  Final outputs are written with non-temporal stores: the
+// next kernel does not read them, and a GEMM's output (up to several hundred MB)
+// left dirty in the Infinity Cache would otherwise be written back during the
+// next kernel, slowing it (measured 1.6x on an HBM-bound quantizer after a
+// 235 MB output).  Split-K partials, read back at once, use ordinary stores.
+__device__ __forceinline__ void store_c4(float* p, float4 v, bool stream) {
+  if (stream) {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    const v4f w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<v4f*>(p));
+  } else {
+    *reinterpret_cast<float4*>(p) = v;
+  }
+}
 
 constexpr int kGroupM = 4;  // tile rows walked together (L2 reuse of B tiles)
 
@@ -518,7 +534,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
         if (mrow < rows_valid) {
           float* crow = C + (m0 + mrow) * ldc + n0;
           if (ncol + 3 < cols_valid) {
-            *reinterpret_cast<float4*>(crow + ncol) = v;
+            store_c4(crow + ncol, v, sp.stream_c != 0);
           } else {
             if (ncol + 0 < cols_valid) crow[ncol + 0] = v.x;
             if (ncol + 1 < cols_valid) crow[ncol + 1] = v.y;
@@ -541,7 +557,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
           const float v0 = acc[a][b][4 * gq] * alpha, v1 = acc[a][b][4 * gq + 1] * alpha;
           const float v2 = acc[a][b][4 * gq + 2] * alpha, v3 = acc[a][b][4 * gq + 3] * alpha;
           if (ncol + 3 < cols_valid) {
-            *reinterpret_cast<float4*>(crow + ncol) = make_float4(v0, v1, v2, v3);
+            store_c4(crow + ncol, make_float4(v0, v1, v2, v3), sp.stream_c != 0);
           } else {
             if (ncol + 0 < cols_valid) crow[ncol + 0] = v0;
             if (ncol + 1 < cols_valid) crow[ncol + 1] = v1;
@@ -623,6 +639,7 @@ int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8
               int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, hipStream_t st) {
   GemmSplit one{};
   one.n = 1;
+  one.stream_c = 1;
   one.kbeg[0] = 0;
   one.kbeg[1] = K;
   return gemm_launch(a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes,
@@ -660,8 +677,8 @@ __global__ __launch_bounds__(256) void k_splitk_sum(const float4* __restrict__ p
       s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }
     const int64_t r = i / cols4, q = i % cols4;
-    *reinterpret_cast<float4*>(c + r * ldc + q * 4) =
-        make_float4(s.x * alpha, s.y * alpha, s.z * alpha, s.w * alpha);
+    store_c4(c + r * ldc + q * 4, make_float4(s.x * alpha, s.y * alpha, s.z * alpha, s.w * alpha),
+             true);
   }
 }
 
@@ -674,6 +691,7 @@ int gemm_split_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const
   if (plan.n <= 1) return gemm_impl(a, sa, b, sb, offs, 1, N, K, alpha, c, ldc, 0, 0, st);
   GemmSplit sp{};
   sp.n = plan.n;
+  sp.stream_c = 0;  // partial sums, read back by k_splitk_sum
   sp.c_stride = M * N;
   for (int i = 0; i <= plan.n; ++i) sp.kbeg[i] = hmin((int64_t)i * plan.kchunk, K);
   int s = gemm_launch(a, sa, b, sb, offs, 1, N, K, 1.0f, part, N, 0, 0, sp, st);
@@ -692,6 +710,7 @@ int gemm_ranges_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, cons
                      float* c, hipStream_t st) {
   GemmSplit sp{};
   sp.n = n;
+  sp.stream_c = 1;
   sp.c_stride = M * N;
   for (int i = 0; i <= n; ++i) sp.kbeg[i] = kbeg[i];
   const int64_t offs[2] = {0, M};
