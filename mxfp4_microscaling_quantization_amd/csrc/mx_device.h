@@ -29,9 +29,29 @@ __device__ __forceinline__ float inv_scale_of(uint32_t byte) {
   return __uint_as_float((254u - byte) << 23);
 }
 
-// 2^e for scale byte b = e + 127, b <= 252 (b = 0 gives the float32 subnormal 2^-127).
+// 2^e for scale byte b = e + 127 (b = 0 gives the float32 subnormal 2^-127,
+// b = 0xFF gives +Inf, which makes every scaled decode below NaN).
 __device__ __forceinline__ float scale_of(uint32_t byte) {
   return __uint_as_float(byte ? byte << 23 : 0x00400000u);
+}
+
+// Decode of packed codes with gfx950's scaled FP4 -> float32 conversion, which
+// is exact: code * 2^(byte - 127) (subnormal results kept, values beyond the
+// float32 range +-Inf), NaN for every code under scale byte 0xFF.  `sel` picks
+// the byte of w; the low nibble gives .x.
+typedef float mx_v2f __attribute__((ext_vector_type(2)));
+template <int SEL>
+__device__ __forceinline__ mx_v2f decode_byte(uint32_t w, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, SEL);
+}
+
+// The 8 codes of w (element i in nibble i) under scale byte `byte`.
+__device__ __forceinline__ void decode8(uint32_t w, uint32_t byte, float v[8]) {
+  const float s = scale_of(byte);
+  const mx_v2f r0 = decode_byte<0>(w, s), r1 = decode_byte<1>(w, s);
+  const mx_v2f r2 = decode_byte<2>(w, s), r3 = decode_byte<3>(w, s);
+  v[0] = r0.x; v[1] = r0.y; v[2] = r1.x; v[3] = r1.y;
+  v[4] = r2.x; v[5] = r2.y; v[6] = r3.x; v[7] = r3.y;
 }
 
 // ---------------------------------------------------------------- rounding

@@ -411,15 +411,13 @@ __global__ __launch_bounds__(256) void k_requant(const uint8_t* __restrict__ cod
       }
     }
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
+    for (int cc = 0; cc < 4; ++cc) {  // column 4o + cc: code byte cc / 2 of each row
       float v[32];
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        const uint32_t code = (cw[i] >> (4 * cc)) & 15u;
-        const uint32_t twice = (0xC8643210u >> ((code & 7u) * 4u)) & 0xFu;  // 2 |value|
-        const float mag = __builtin_amdgcn_ldexpf((float)twice, (int)sw[i] - 128);
-        const float sv = __uint_as_float(__float_as_uint(mag) | ((code & 8u) << 28));
-        v[i] = sw[i] == 255u ? __uint_as_float(0x7FC00000u) : sv;
+        const float s = scale_of(sw[i]);
+        const mx_v2f r = cc < 2 ? decode_byte<0>(cw[i], s) : decode_byte<1>(cw[i], s);
+        v[i] = (cc & 1) ? r.y : r.x;
       }
       uint32_t byte;
       const int c = o * 4 + cc;
@@ -471,8 +469,7 @@ __global__ __launch_bounds__(256) void k_requant_rht(const uint8_t* __restrict__
         codes_in + (row0 + r) * ld_in + (col0 + kb * 32) / 2 + q * 4);
     const uint32_t byte = scales_in[(row0 + r) * ld_sin + (col0 / 32 + kb)];
     float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = e2m1_decode((wcodes >> (4 * i)) & 15u, byte);
+    decode8(wcodes, byte, v);
     fwht32_quad(v, q);
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = apply_sign(v[i] * 0.03125f, sign_mask, q * 8 + i);
@@ -541,8 +538,7 @@ __global__ __launch_bounds__(256) void k_dequant_row(const uint32_t* __restrict_
     const uint32_t w = codes[b * 4 + q];
     const uint32_t byte = scales[b];
     float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = e2m1_decode((w >> (4 * i)) & 15u, byte);
+    decode8(w, byte, v);
     if (HAD) {
       fwht32_quad(v, q);
 #pragma unroll
@@ -569,7 +565,7 @@ __global__ __launch_bounds__(256) void k_dequant_col(const uint8_t* __restrict__
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
     float v[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = e2m1_decode((ws[i >> 3] >> (4 * (i & 7))) & 15u, byte);
+    for (int q = 0; q < 4; ++q) decode8(ws[q], byte, v + 8 * q);
     if (HAD) {
       fwht32_lane(v);
 #pragma unroll
