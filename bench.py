@@ -33,8 +33,8 @@ PEAK_FP4_TFLOPS = 10100.0
 # from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB copy, valid for
 # the GEMM source with this sha256 only (the per-launch table is kept with the
 # committed profiles).
-GEMM_TRAFFIC = {"sha256": "c920416b2fcfda757de5d561a0240ccc61cedf928db7e3c538457d7e8ecc9386",
-                "bytes_per_launch": 670457142}
+GEMM_TRAFFIC = {"sha256": "a2762481055143c1bc3cc025008b3327719f0dd23d1fe5f2b6c59e574a59e2ba",
+                "bytes_per_launch": 668290033}
 
 
 def gemm_traffic():

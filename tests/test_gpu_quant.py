@@ -67,6 +67,19 @@ def test_every_bf16_value_under_a_fixed_scale(rnd, e):
     assert_bytes_equal(host(codes), wc, "codes")
 
 
+@pytest.mark.parametrize("axis", [mx.MX_ROW, mx.MX_COL])
+def test_sr_decisions_one_step_either_side_of_the_carry(axis):
+    """Each value sits one 2^-22 step below or exactly at the carry point of its
+    own random bits, in every interval of the grid, under random block scales:
+    the GPU codes are the expected neighbours, as the oracle's are."""
+    from tests.sr_cases import carry_boundary_case
+    seed = 0xC0FFEE
+    x, codes, scales = carry_boundary_case(160, 224, axis, seed, np.random.default_rng(8))
+    c, s = mx.quantize(upload(x, "f32"), axis, mx.MX_SR, seed)
+    assert_bytes_equal(host(s), scales, "scales")
+    assert_bytes_equal(host(c), O.pack_codes(codes), "codes")
+
+
 def test_random_f32_bit_patterns():
     rng = np.random.default_rng(3)
     u = rng.integers(0, 0x7F800000, (256, 256), dtype=np.uint32)

@@ -222,6 +222,17 @@ def test_sr_decisions_use_the_published_output_bits(golden_dir):
         assert codes[:4].tolist() == [bump] * 4, (bump, codes[:4])
 
 
+@pytest.mark.parametrize("axis", [O.ROW, O.COL])
+def test_sr_decisions_one_step_either_side_of_the_carry(axis):
+    """Values one 2^-22 step below or exactly at their own carry point, in every
+    interval of the grid: the oracle picks the lower or the upper neighbour."""
+    from tests.sr_cases import carry_boundary_case
+    x, codes, scales = carry_boundary_case(64, 96, axis, 0xC0FFEE, np.random.default_rng(7))
+    c, s = O.quantize(x, axis, O.SR, 0xC0FFEE)
+    assert np.array_equal(s, scales)
+    assert np.array_equal(c, O.pack_codes(codes))
+
+
 def test_sr_matches_exact_rationals_on_random_blocks():
     rng = np.random.default_rng(5)
     x = (rng.standard_normal((40, 32)) * np.exp2(rng.integers(-30, 30, (40, 1)))).astype(np.float32)
