@@ -92,15 +92,16 @@ __device__ __forceinline__ uint32_t cvt_sr_pair(float v0, float v1, uint32_t see
 // ---------------------------------------------------------------- SplitMix64
 // Steele, Lea & Flood, "Fast splittable pseudorandom number generators"
 // (OOPSLA 2014): output number idx+1 from state `seed` is the variant-13
-// finalizer applied to seed + (idx+1) * 0x9E3779B97F4A7C15.  Only the top 24
-// bits are used; the last xor-shift (by 31) leaves bits 33..63 unchanged, and
-// only the high word of the last product is needed.
+// finalizer applied to seed + (idx+1) * 0x9E3779B97F4A7C15.
 constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
 
 __device__ __forceinline__ uint64_t sm64_state(uint64_t seed, uint64_t idx) {
   return seed + (idx + 1ull) * kGamma;
 }
 
+// Top 24 bits of the output for state z (the synthetic update generator's
+// uniforms): the last xor-shift (by 31) leaves bits 33..63 unchanged, so only
+// the high word of the last product is needed.
 __device__ __forceinline__ uint32_t sm64_top24(uint64_t z) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z ^= z >> 27;
@@ -113,7 +114,8 @@ __device__ __forceinline__ uint32_t sm64_top24(uint64_t z) {
 // keyed by element 2i's index: element 2i reads bits 42..63 of the output,
 // element 2i+1 bits 9..30.  Returns words whose bits 10..31 (hi) and 9..30 (lo)
 // are those output bits: the final z ^ (z >> 31) leaves bits 33..63 unchanged,
-// and its low word's bits 9..30 are z's xor bits 39..60 = (hi << 1) at 9..30.
+// and in its low word bits 9..30 of z are xored with z's bits 40..61, which are
+// bits 8..29 of the high word: (hi << 1) at bits 9..30.
 __device__ __forceinline__ void sm64_words(uint64_t z, uint32_t& hi, uint32_t& lo) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
