@@ -41,9 +41,10 @@ int gemm_ranges_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, cons
 int requantize_batched_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t batch,
                             int64_t rows, int64_t cols, int round, uint64_t seed, uint8_t* codes,
                             uint8_t* scales, hipStream_t st);
-int quantize_segments_impl(const void* x, int dtype, int64_t rows, int64_t cols,
-                           const int64_t* offs, int64_t groups, int round, uint64_t seed,
-                           uint8_t* codes, uint8_t* scales, hipStream_t st);
+int quantize_dual_segments_impl(const void* x, int dtype, int64_t rows, int64_t cols,
+                                const int64_t* offs, int64_t groups, int round, uint64_t seed_row,
+                                uint64_t seed_col, uint8_t* codes_row, uint8_t* scales_row,
+                                uint8_t* codes_col, uint8_t* scales_col, hipStream_t st);
 int requantize_segments_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
                              int64_t cols, const int64_t* offs, int64_t groups, int round,
                              uint64_t seed, uint8_t* codes, uint8_t* scales, hipStream_t st);
@@ -260,10 +261,10 @@ extern "C" int mx_grouped_linear_bwd(const void* dy, int dtype, const int64_t* o
                                   ws + L.q4s, st);
   if (s != MX_OK) return s;
   if (R > 0) {
-    s = quantize_impl(dy, dtype, R, N, MX_ROW, MX_SR, seed + 3, 0, 0, ws + L.q3c, ws + L.q3s, st);
-    if (s != MX_OK) return s;
-    s = quantize_segments_impl(dy, dtype, R, N, offs, E, MX_SR, seed + 5, ws + L.q5c, ws + L.q5s,
-                               st);
+    // Q3 (1x32 along N, every token) and Q5 (32x1 along each expert's tokens)
+    // from one read of dY
+    s = quantize_dual_segments_impl(dy, dtype, R, N, offs, E, MX_SR, seed + 3, seed + 5,
+                                    ws + L.q3c, ws + L.q3s, ws + L.q5c, ws + L.q5s, st);
     if (s != MX_OK) return s;
     s = requantize_segments_impl(xq_codes, xq_scales, R, K, offs, E, MX_SR, seed + 6, ws + L.q6c,
                                  ws + L.q6s, st);

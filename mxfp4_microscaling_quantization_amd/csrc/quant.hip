@@ -726,6 +726,25 @@ int quantize_segments_impl(const void* x, int dtype, int64_t rows, int64_t cols,
                                                seed, 0, 0, nullptr, nullptr, codes, scales, st, s);
 }
 
+// Row (1x32) quantization of every row plus the per-segment column (32x1)
+// quantization, from one read of x: the row pass of the tile kernel covers the
+// segment's real rows only and writes them at their own rows, so the row output
+// is the plain row quantization.
+int quantize_dual_segments_impl(const void* x, int dtype, int64_t rows, int64_t cols,
+                                const int64_t* offs, int64_t groups, int round, uint64_t seed_row,
+                                uint64_t seed_col, uint8_t* codes_row, uint8_t* scales_row,
+                                uint8_t* codes_col, uint8_t* scales_col, hipStream_t st) {
+  if (rows == 0 || cols == 0) return MX_OK;
+  const Segs s = make_segs(offs, groups, kTileR);
+  return dtype == MX_BF16
+             ? launch_quant_tile<uint16_t, true>(static_cast<const uint16_t*>(x), rows, cols, round,
+                                                 seed_row, seed_col, 0, 0, codes_row, scales_row,
+                                                 codes_col, scales_col, st, s)
+             : launch_quant_tile<float, true>(static_cast<const float*>(x), rows, cols, round,
+                                              seed_row, seed_col, 0, 0, codes_row, scales_row,
+                                              codes_col, scales_col, st, s);
+}
+
 int requantize_segments_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
                              int64_t cols, const int64_t* offs, int64_t groups, int round,
                              uint64_t seed, uint8_t* codes, uint8_t* scales, hipStream_t st) {
