@@ -4,9 +4,9 @@ Step = one MXFP4 linear forward + backward of the Llama-3-8B MLP up-projection
 (M = 8192 tokens, K = 4096, N = 14336, bf16 activations with 1% outlier
 channels x30, weights N(0, 0.02), dY N(0, 1e-3)):
 
-  quantize X (1x32 RNE), quantize W (1x32 RNE), GEMM Y = Q(X) Q(W)^T,
-  dual-quantize dY (1x32 SR + 32x1 SR), requantize Q(W) and Q(X) (32x1 SR),
-  GEMM dX, GEMM dW
+  quantize X and W (1x32 RNE, one launch), GEMM Y = Q(X) Q(W)^T,
+  dual-quantize dY (1x32 SR + 32x1 SR), requantize Q(W) and Q(X) (32x1 SR,
+  one launch), GEMM dX, GEMM dW
 
 -- the kernels mx_linear_fwd / mx_linear_bwd launch, issued one entry point at
 a time so that every kernel is bracketed by events on the stream it runs on.
@@ -115,13 +115,13 @@ def bench_linear(torch, mx, synth, dev, steps, warmup, seed=3):
         (an event record between kernels costs a few microseconds)."""
         def run(name, fn):
             (timer.run(name, fn) if name in timed else fn())
-        run("quant_x", lambda: mx.mx_quantize(x, BF, M, K, mx.MX_ROW, mx.MX_RNE, 0, 0, 0, *xq, st))
-        run("quant_w", lambda: mx.mx_quantize(w, BF, N, K, mx.MX_ROW, mx.MX_RNE, 0, 0, 0, *wq, st))
+        run("quant_xw", lambda: mx.mx_quantize_pair(x, M, w, N, K, BF, mx.MX_RNE, 0, 0, 0, 0,
+                                                   *xq, *wq, st))
         run("gemm", lambda: mx.mx_gemm(*xq, *wq, M, N, K, 1.0, y, N, st))
         run("dual_dy", lambda: mx.mx_quantize_dual(dy, BF, M, N, mx.MX_SR, seed + 3, seed + 5,
                                                   *q3, *q5, st))
-        run("requant_w", lambda: mx.mx_requantize(*wq, N, K, mx.MX_SR, seed + 4, *q4, st))
-        run("requant_x", lambda: mx.mx_requantize(*xq, M, K, mx.MX_SR, seed + 6, *q6, st))
+        run("requant_wx", lambda: mx.mx_requantize_pair(*wq, N, *xq, M, K, mx.MX_SR, seed + 4,
+                                                       seed + 6, *q4, *q6, st))
         run("gemm", lambda: mx.mx_gemm(*q3, *q4, M, K, N, 1.0, dx, K, st))
         run("gemm", lambda: mx.mx_gemm(*q5, *q6, N, K, M, 1.0, dw, K, st))
 
@@ -151,16 +151,15 @@ def bench_linear(torch, mx, synth, dev, steps, warmup, seed=3):
     # per-kernel breakdown of the quantizers: a separate pass with every kernel timed
     B = Timer(torch, st)
     for _ in range(5):
-        step(B, timed=("quant_x", "quant_w", "dual_dy", "requant_w", "requant_x", "gemm"))
+        step(B, timed=("quant_xw", "dual_dy", "requant_wx", "gemm"))
     torch.cuda.synchronize()
     kern = {k: B.mean_ms(k) for k in B.pairs}
     kern["gemm"] = T.mean_ms("gemm")  # the GEMM launches of the timed region itself
     gemm_ms = kern["gemm"]
     gemm_tf = 2.0 * M * N * K / (gemm_ms * 1e-3) / 1e12
     bytes_q = {
-        "quant_x": M * K * (2 + 0.53125), "quant_w": N * K * (2 + 0.53125),
-        "dual_dy": M * N * (2 + 2 * 0.53125), "requant_w": N * K * 2 * 0.53125,
-        "requant_x": M * K * 2 * 0.53125,
+        "quant_xw": (M + N) * K * (2 + 0.53125), "dual_dy": M * N * (2 + 2 * 0.53125),
+        "requant_wx": (N + M) * K * 2 * 0.53125,
     }
     quant = {k: {"us": kern[k] * 1e3, "GBps": bytes_q[k] / (kern[k] * 1e-3) / 1e9,
                  "frac_hbm": bytes_q[k] / (kern[k] * 1e-3) / 1e9 / PEAK_HBM_GBPS} for k in bytes_q}

@@ -120,6 +120,19 @@ int mx_quantize_dual(const void* x, int dtype, int64_t rows, int64_t cols, int r
                      uint8_t* codes_row, uint8_t* scales_row,
                      uint8_t* codes_col, uint8_t* scales_col, void* stream);
 
+/* mx_quantize_pair: two MX_ROW quantizations in one launch -- the forward
+ * layer's two operands Q_D(X) and Q_D(W) ([TJ] Question 2 (1): both 1x32 along
+ * the contraction axis).  x0 [rows0, cols] and x1 [rows1, cols] (same dtype,
+ * rounding, rotation and sign_mask) are quantized exactly as two mx_quantize
+ * calls with axis MX_ROW and seeds seed0 / seed1 would (each tensor's
+ * stochastic-rounding index starts at 0), writing codes0 [rows0][cols/2],
+ * scales0 [rows0][cols/32] and codes1 / scales1 likewise.  cols % 32 == 0; a
+ * tensor with 0 rows is skipped (its pointers may then be NULL). */
+int mx_quantize_pair(const void* x0, int64_t rows0, const void* x1, int64_t rows1, int64_t cols,
+                     int dtype, int round, uint64_t seed0, uint64_t seed1, int hadamard,
+                     uint32_t sign_mask, uint8_t* codes0, uint8_t* scales0,
+                     uint8_t* codes1, uint8_t* scales1, void* stream);
+
 /* mx_quantize_dual_rht: mx_quantize_dual with the random-sign block Hadamard
  * ([ALTO] Jargon "Randomized Hadamard transform"; the "MXFP4 + RHT +
  * stochastic rounding" rows of its steps table) on both outputs: each row
@@ -142,6 +155,19 @@ int mx_quantize_dual_rht(const void* x, int dtype, int64_t rows, int64_t cols, i
  * mx_quantize(dequantized input, MX_COL, ...).  rows % 32 == 0, cols % 32 == 0. */
 int mx_requantize(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows, int64_t cols,
                   int round, uint64_t seed, uint8_t* codes_out, uint8_t* scales_out, void* stream);
+
+/* mx_requantize_pair: two double quantizations in one launch -- the backward
+ * layer's Q_S^(4)(Q_D(W)) and Q_S^(6)(Q_D(X)) ([TJ] Question 2 (2)).  The
+ * packed MX_ROW inputs [rows0, cols] and [rows1, cols] are requantized exactly
+ * as two mx_requantize calls with seeds seed0 / seed1 would, outputs transposed
+ * (codes_out0 [cols][rows0/2], scales_out0 [cols][rows0/32], and likewise for
+ * input 1).  rows0, rows1, cols multiples of 32; an input with 0 rows is skipped
+ * (its pointers may then be NULL). */
+int mx_requantize_pair(const uint8_t* codes_in0, const uint8_t* scales_in0, int64_t rows0,
+                       const uint8_t* codes_in1, const uint8_t* scales_in1, int64_t rows1,
+                       int64_t cols, int round, uint64_t seed0, uint64_t seed1,
+                       uint8_t* codes_out0, uint8_t* scales_out0,
+                       uint8_t* codes_out1, uint8_t* scales_out1, void* stream);
 
 /* mx_requantize_rht: double quantization of an operand kept in the rotated
  * domain (the rotated layer's saved Q_D(H X), rotated along cols with

@@ -23,8 +23,15 @@ int quantize_dual_impl(const void* x, int dtype, int64_t rows, int64_t cols, int
                        uint64_t seed_row, uint64_t seed_col, int had, uint32_t mask,
                        uint8_t* codes_row, uint8_t* scales_row, uint8_t* codes_col,
                        uint8_t* scales_col, hipStream_t st);
-int requantize_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows, int64_t cols,
-                    int round, uint64_t seed, uint8_t* codes, uint8_t* scales, hipStream_t st);
+int quantize_rows2_impl(const void* x0, int64_t rows0, int64_t cols0, uint8_t* codes0,
+                        uint8_t* scales0, uint64_t seed0, const void* x1, int64_t rows1,
+                        int64_t cols1, uint8_t* codes1, uint8_t* scales1, uint64_t seed1,
+                        int dtype, int round, int had, uint32_t mask, hipStream_t st);
+int requantize_pair_impl(const uint8_t* codes_in0, const uint8_t* scales_in0, int64_t rows0,
+                         const uint8_t* codes_in1, const uint8_t* scales_in1, int64_t rows1,
+                         int64_t cols, int round, uint64_t seed0, uint64_t seed1,
+                         uint8_t* codes0, uint8_t* scales0, uint8_t* codes1, uint8_t* scales1,
+                         hipStream_t st);
 int requantize_rht_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
                         int64_t cols, int round, uint64_t seed, uint32_t mask, uint8_t* codes,
                         uint8_t* scales, hipStream_t st);
@@ -131,9 +138,9 @@ static int linear_fwd_impl(const void* x, const void* w, int dtype, int64_t M, i
   MX_REQUIRE(x && w && y && xq_codes && xq_scales && wq_codes && wq_scales, MX_ERR_NULL);
   MX_REQUIRE(aligned16(x) && aligned16(w) && aligned16(y) && aligned16(xq_codes) &&
                  aligned16(wq_codes), MX_ERR_ALIGN);
-  int s = quantize_impl(x, dtype, M, K, MX_ROW, MX_RNE, 0, had, mask, xq_codes, xq_scales, st);
-  if (s != MX_OK) return s;
-  s = quantize_impl(w, dtype, N, K, MX_ROW, MX_RNE, 0, had, mask, wq_codes, wq_scales, st);
+  // Q_D(X) and Q_D(W) (1x32 along K, nearest) in one launch
+  int s = quantize_rows2_impl(x, M, K, xq_codes, xq_scales, 0, w, N, K, wq_codes, wq_scales, 0,
+                              dtype, MX_RNE, had, mask, st);
   if (s != MX_OK) return s;
   const int64_t offs[2] = {0, M};
   return gemm_impl(xq_codes, xq_scales, wq_codes, wq_scales, offs, 1, N, K,
@@ -166,10 +173,9 @@ static int linear_bwd_impl(const void* dy, int dtype, int64_t M, int64_t N, int6
     if (s != MX_OK) return s;
     s = requantize_rht_impl(xq_codes, xq_scales, M, K, MX_SR, seed + 6, mask, ws + L.q6c,
                             ws + L.q6s, st);
-  } else {
-    s = requantize_impl(wq_codes, wq_scales, N, K, MX_SR, seed + 4, ws + L.q4c, ws + L.q4s, st);
-    if (s != MX_OK) return s;
-    s = requantize_impl(xq_codes, xq_scales, M, K, MX_SR, seed + 6, ws + L.q6c, ws + L.q6s, st);
+  } else {  // Q4 = Q_S(Q_D(W)) and Q6 = Q_S(Q_D(X)) in one launch
+    s = requantize_pair_impl(wq_codes, wq_scales, N, xq_codes, xq_scales, M, K, MX_SR, seed + 4,
+                             seed + 6, ws + L.q4c, ws + L.q4s, ws + L.q6c, ws + L.q6s, st);
   }
   if (s != MX_OK) return s;
   const float alpha = had ? kHadamardAlpha : 1.0f;

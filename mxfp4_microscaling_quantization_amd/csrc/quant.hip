@@ -94,13 +94,24 @@ __device__ __forceinline__ uint32_t quant8(const float v[8], uint32_t byte, uint
 // any of them is quantized (more bytes in flight per lane).
 constexpr int kRowU = 4;
 
+// Up to two tensors quantized by one launch (the forward layer's X and W):
+// blocks [0, n0) belong to tensor 0, [n0, nblk) to tensor 1, each indexed from
+// its own first block.
+template <typename T>
+struct RowJobs {
+  const T* x[2];
+  uint32_t* codes[2];
+  uint8_t* scales[2];
+  uint64_t seed[2];
+  int64_t n0;
+  int64_t nblk;
+};
+
 template <typename T, int ROUND, bool HAD>
-__global__ __launch_bounds__(256) void k_quant_row(const T* __restrict__ x, int64_t nblk,
-                                                   uint64_t seed, uint32_t sign_mask,
-                                                   uint32_t* __restrict__ codes,
-                                                   uint8_t* __restrict__ scales) {
+__global__ __launch_bounds__(256) void k_quant_row(const RowJobs<T> jobs, uint32_t sign_mask) {
   const int q = threadIdx.x & 3;
   const int j = threadIdx.x >> 2;
+  const int64_t nblk = jobs.nblk, n0 = jobs.n0;
   for (int64_t base = (int64_t)blockIdx.x * 64 * kRowU; base < nblk;
        base += (int64_t)gridDim.x * 64 * kRowU) {
     float v[kRowU][8];
@@ -108,12 +119,15 @@ __global__ __launch_bounds__(256) void k_quant_row(const T* __restrict__ x, int6
     for (int u = 0; u < kRowU; ++u) {
       // unconditional (clamped) loads, so that all of them are in flight at once
       const int64_t b = min(base + u * 64 + j, nblk - 1);
-      load8<T>(x + b * 32 + q * 8, v[u]);
+      const bool t1 = b >= n0;
+      load8<T>((t1 ? jobs.x[1] + (b - n0) * 32 : jobs.x[0] + b * 32) + q * 8, v[u]);
     }
 #pragma unroll
     for (int u = 0; u < kRowU; ++u) {
       const int64_t b = base + u * 64 + j;
       if (b >= nblk) break;  // quads past the end: whole quads, so the DPP partners agree
+      const bool t1 = b >= n0;
+      const int64_t lb = t1 ? b - n0 : b;  // block index within its tensor
       if (HAD) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[u][i] = apply_sign(v[u][i], sign_mask, q * 8 + i);
@@ -124,8 +138,9 @@ __global__ __launch_bounds__(256) void k_quant_row(const T* __restrict__ x, int6
       for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[u][i]) & 0x7FFFFFFFu);
       m = quad_max_u32(m);
       const uint32_t byte = scale_byte_of(m);
-      codes[b * 4 + q] = quant8<ROUND>(v[u], byte, seed, (uint64_t)b * 32 + q * 8);
-      if (q == 0) scales[b] = (uint8_t)byte;
+      (t1 ? jobs.codes[1] : jobs.codes[0])[lb * 4 + q] =
+          quant8<ROUND>(v[u], byte, t1 ? jobs.seed[1] : jobs.seed[0], (uint64_t)lb * 32 + q * 8);
+      if (q == 0) (t1 ? jobs.scales[1] : jobs.scales[0])[lb] = (uint8_t)byte;
     }
   }
 }
@@ -153,10 +168,10 @@ struct TileRows {
   int nreal, nrb;
 };
 
-__device__ __forceinline__ TileRows tile_rows(const Segs& s, int TR, int64_t rows) {
+__device__ __forceinline__ TileRows tile_rows(const Segs& s, int TR, int64_t rows, int y) {
   TileRows t;
   if (s.n == 0) {
-    t.row0 = (int64_t)blockIdx.y * TR;
+    t.row0 = (int64_t)y * TR;
     t.nreal = (int)min<int64_t>(TR, rows - t.row0);
     t.out0 = t.row0;
     t.nrb = t.nreal / 32;
@@ -164,8 +179,8 @@ __device__ __forceinline__ TileRows tile_rows(const Segs& s, int TR, int64_t row
     return t;
   }
   int g = 0;
-  while (g + 1 < s.n && s.tile_start[g + 1] <= (int)blockIdx.y) ++g;
-  const int64_t k = (int64_t)blockIdx.y - s.tile_start[g];
+  while (g + 1 < s.n && s.tile_start[g + 1] <= y) ++g;
+  const int64_t k = (int64_t)y - s.tile_start[g];
   t.row0 = s.row_off[g] + k * TR;
   t.nreal = (int)min<int64_t>(TR, s.row_off[g + 1] - t.row0);
   t.out0 = s.out_off[g] + k * TR;
@@ -262,7 +277,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(
   uint4* const s_codes = reinterpret_cast<uint4*>(s_in);
 
   const int64_t col0 = (int64_t)blockIdx.x * TC;
-  const TileRows tr = tile_rows(segs, kTileR, rows);
+  const TileRows tr = tile_rows(segs, kTileR, rows, (int)blockIdx.y);
   const int64_t row0 = tr.row0;
   const int ncols = (int)min<int64_t>(TC, cols - col0);
   const int nrows = tr.nreal;  // rows past it (segment padding) stay zero in LDS
@@ -370,23 +385,37 @@ __global__ __launch_bounds__(256) void k_quant_tile(
 constexpr int kRqR = 256;
 constexpr int kRqC = 128;
 
+// One launch can requantize two matrices with the same cols (the backward
+// layer's Q_D(W) and Q_D(X)): tile rows [0, ty0) of the grid belong to job 0,
+// the rest to job 1.
+struct RqJob {
+  const uint8_t* codes_in;
+  const uint8_t* scales_in;
+  int64_t rows;
+  uint64_t seed;
+  uint8_t* codes;
+  uint8_t* scales;
+};
+
 template <int ROUND>
-__global__ __launch_bounds__(256) void k_requant(const uint8_t* __restrict__ codes_in,
-                                                 const uint8_t* __restrict__ scales_in,
-                                                 int64_t rows, int64_t cols, uint64_t seed,
-                                                 uint8_t* __restrict__ codes,
-                                                 uint8_t* __restrict__ scales, const Segs segs) {
+__global__ __launch_bounds__(256) void k_requant(const RqJob j0, const RqJob j1, int ty0,
+                                                 int64_t cols, const Segs segs) {
   constexpr int NRB = kRqR / 32;
   __shared__ uint4 s_codes[kRqC * NRB];
   __shared__ uint8_t s_scales[kRqC * NRB];
 
+  const bool second = (int)blockIdx.y >= ty0;   // uniform over the workgroup
+  const RqJob& job = second ? j1 : j0;
+  const int ty = (int)blockIdx.y - (second ? ty0 : 0);
+  const int64_t rows = job.rows;
+  const uint64_t seed = job.seed;
   const int64_t z = blockIdx.z;
-  codes_in += z * rows * (cols / 2);
-  scales_in += z * rows * (cols / 32);
-  codes += z * rows * (cols / 2);
-  scales += z * rows * (cols / 32);
+  const uint8_t* __restrict__ codes_in = job.codes_in + z * rows * (cols / 2);
+  const uint8_t* __restrict__ scales_in = job.scales_in + z * rows * (cols / 32);
+  uint8_t* __restrict__ codes = job.codes + z * rows * (cols / 2);
+  uint8_t* __restrict__ scales = job.scales + z * rows * (cols / 32);
   const int64_t col0 = (int64_t)blockIdx.x * kRqC;
-  const TileRows tr = tile_rows(segs, kRqR, rows);
+  const TileRows tr = tile_rows(segs, kRqR, rows, ty);
   const int64_t row0 = tr.row0;
   const int ncols = (int)min<int64_t>(kRqC, cols - col0);   // multiple of 32
   const int nrb = tr.nrb;
@@ -588,20 +617,30 @@ static int grid_for_blocks(int64_t nblk) {
 }
 
 template <typename T>
+static int launch_quant_row_jobs(const RowJobs<T>& jobs, int round, int had, uint32_t mask,
+                                 hipStream_t st) {
+  const dim3 grid(grid_for_row(jobs.nblk)), block(256);
+  if (round == MX_RNE) {
+    if (had) k_quant_row<T, MX_RNE, true><<<grid, block, 0, st>>>(jobs, mask);
+    else k_quant_row<T, MX_RNE, false><<<grid, block, 0, st>>>(jobs, mask);
+  } else {
+    if (had) k_quant_row<T, MX_SR, true><<<grid, block, 0, st>>>(jobs, mask);
+    else k_quant_row<T, MX_SR, false><<<grid, block, 0, st>>>(jobs, mask);
+  }
+  return launch_status();
+}
+
+template <typename T>
 static int launch_quant_row(const T* x, int64_t rows, int64_t cols, int round, uint64_t seed,
                             int had, uint32_t mask, uint8_t* codes, uint8_t* scales,
                             hipStream_t st) {
-  const int64_t nblk = rows * cols / 32;
-  const dim3 grid(grid_for_row(nblk)), block(256);
-  uint32_t* c32 = reinterpret_cast<uint32_t*>(codes);
-  if (round == MX_RNE) {
-    if (had) k_quant_row<T, MX_RNE, true><<<grid, block, 0, st>>>(x, nblk, seed, mask, c32, scales);
-    else k_quant_row<T, MX_RNE, false><<<grid, block, 0, st>>>(x, nblk, seed, mask, c32, scales);
-  } else {
-    if (had) k_quant_row<T, MX_SR, true><<<grid, block, 0, st>>>(x, nblk, seed, mask, c32, scales);
-    else k_quant_row<T, MX_SR, false><<<grid, block, 0, st>>>(x, nblk, seed, mask, c32, scales);
-  }
-  return launch_status();
+  RowJobs<T> jobs{};
+  jobs.x[0] = jobs.x[1] = x;
+  jobs.codes[0] = jobs.codes[1] = reinterpret_cast<uint32_t*>(codes);
+  jobs.scales[0] = jobs.scales[1] = scales;
+  jobs.seed[0] = jobs.seed[1] = seed;
+  jobs.nblk = jobs.n0 = rows * cols / 32;
+  return launch_quant_row_jobs(jobs, round, had, mask, st);
 }
 
 static Segs plain_segs() {
@@ -682,17 +721,21 @@ int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, int axis
                                                seed, had, mask, nullptr, nullptr, codes, scales, st);
 }
 
+static int launch_requant_jobs(const RqJob& j0, const RqJob& j1, int ty0, int ty1, int64_t cols,
+                               int round, int64_t batch, const Segs& segs, hipStream_t st) {
+  if (ty0 + ty1 == 0 || batch == 0) return MX_OK;
+  const dim3 grid((unsigned)cdiv(cols, kRqC), (unsigned)(ty0 + ty1), (unsigned)batch), block(256);
+  if (round == MX_RNE) k_requant<MX_RNE><<<grid, block, 0, st>>>(j0, j1, ty0, cols, segs);
+  else k_requant<MX_SR><<<grid, block, 0, st>>>(j0, j1, ty0, cols, segs);
+  return launch_status();
+}
+
 static int launch_requant(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
                           int64_t cols, int round, uint64_t seed, uint8_t* codes, uint8_t* scales,
                           int64_t batch, const Segs& segs, hipStream_t st) {
-  const unsigned ty = segs.n ? (unsigned)segs.tile_start[segs.n] : (unsigned)cdiv(rows, kRqR);
-  if (ty == 0 || batch == 0) return MX_OK;
-  const dim3 grid((unsigned)cdiv(cols, kRqC), ty, (unsigned)batch), block(256);
-  if (round == MX_RNE)
-    k_requant<MX_RNE><<<grid, block, 0, st>>>(codes_in, scales_in, rows, cols, seed, codes, scales, segs);
-  else
-    k_requant<MX_SR><<<grid, block, 0, st>>>(codes_in, scales_in, rows, cols, seed, codes, scales, segs);
-  return launch_status();
+  const int ty = segs.n ? segs.tile_start[segs.n] : (int)cdiv(rows, kRqR);
+  const RqJob j{codes_in, scales_in, rows, seed, codes, scales};
+  return launch_requant_jobs(j, j, ty, 0, cols, round, batch, segs, st);
 }
 
 int requantize_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows, int64_t cols,
@@ -700,6 +743,20 @@ int requantize_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t r
   if (rows == 0 || cols == 0) return MX_OK;
   return launch_requant(codes_in, scales_in, rows, cols, round, seed, codes, scales, 1,
                         plain_segs(), st);
+}
+
+// Two packed row-blocked matrices [rows0, cols] and [rows1, cols] requantized
+// (32x1, transposed outputs) by one launch, each with its own seed.
+int requantize_pair_impl(const uint8_t* codes_in0, const uint8_t* scales_in0, int64_t rows0,
+                         const uint8_t* codes_in1, const uint8_t* scales_in1, int64_t rows1,
+                         int64_t cols, int round, uint64_t seed0, uint64_t seed1,
+                         uint8_t* codes0, uint8_t* scales0, uint8_t* codes1, uint8_t* scales1,
+                         hipStream_t st) {
+  if (cols == 0) return MX_OK;
+  const RqJob j0{codes_in0, scales_in0, rows0, seed0, codes0, scales0};
+  const RqJob j1{codes_in1, scales_in1, rows1, seed1, codes1, scales1};
+  return launch_requant_jobs(j0, j1, (int)cdiv(rows0, kRqR), (int)cdiv(rows1, kRqR), cols, round,
+                             1, plain_segs(), st);
 }
 
 // A stack of `batch` [rows, cols] matrices, each requantized on its own (the
@@ -710,6 +767,41 @@ int requantize_batched_impl(const uint8_t* codes_in, const uint8_t* scales_in, i
   if (rows == 0 || cols == 0) return MX_OK;
   return launch_requant(codes_in, scales_in, rows, cols, round, seed, codes, scales, batch,
                         plain_segs(), st);
+}
+
+template <typename T>
+static int launch_quant_rows2(const void* x0, int64_t n0, uint8_t* codes0, uint8_t* scales0,
+                              uint64_t seed0, const void* x1, int64_t n1, uint8_t* codes1,
+                              uint8_t* scales1, uint64_t seed1, int round, int had,
+                              uint32_t mask, hipStream_t st) {
+  RowJobs<T> jobs{};
+  jobs.x[0] = static_cast<const T*>(x0);
+  jobs.x[1] = static_cast<const T*>(x1);
+  jobs.codes[0] = reinterpret_cast<uint32_t*>(codes0);
+  jobs.codes[1] = reinterpret_cast<uint32_t*>(codes1);
+  jobs.scales[0] = scales0;
+  jobs.scales[1] = scales1;
+  jobs.seed[0] = seed0;
+  jobs.seed[1] = seed1;
+  jobs.n0 = n0;
+  jobs.nblk = n0 + n1;
+  return launch_quant_row_jobs(jobs, round, had, mask, st);
+}
+
+// Row (1x32) quantization of two tensors of the same type and rounding in one
+// launch: x0 [rows0, cols0] and x1 [rows1, cols1], each with its own outputs
+// and seed (the logical indices of each start at 0).
+int quantize_rows2_impl(const void* x0, int64_t rows0, int64_t cols0, uint8_t* codes0,
+                        uint8_t* scales0, uint64_t seed0, const void* x1, int64_t rows1,
+                        int64_t cols1, uint8_t* codes1, uint8_t* scales1, uint64_t seed1,
+                        int dtype, int round, int had, uint32_t mask, hipStream_t st) {
+  const int64_t n0 = rows0 * cols0 / 32, n1 = rows1 * cols1 / 32;
+  if (n0 + n1 == 0) return MX_OK;
+  return dtype == MX_BF16
+             ? launch_quant_rows2<uint16_t>(x0, n0, codes0, scales0, seed0, x1, n1, codes1,
+                                            scales1, seed1, round, had, mask, st)
+             : launch_quant_rows2<float>(x0, n0, codes0, scales0, seed0, x1, n1, codes1, scales1,
+                                         seed1, round, had, mask, st);
 }
 
 // 32x1 blocks per row segment (offs: host array of groups+1 row offsets).
@@ -808,6 +900,28 @@ extern "C" int mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols,
                        as_stream(stream));
 }
 
+extern "C" int mx_quantize_pair(const void* x0, int64_t rows0, const void* x1, int64_t rows1,
+                                int64_t cols, int dtype, int round, uint64_t seed0,
+                                uint64_t seed1, int hadamard, uint32_t sign_mask,
+                                uint8_t* codes0, uint8_t* scales0, uint8_t* codes1,
+                                uint8_t* scales1, void* stream) {
+  MX_REQUIRE(dtype == MX_F32 || dtype == MX_BF16, MX_ERR_ENUM);
+  MX_REQUIRE(round == MX_RNE || round == MX_SR, MX_ERR_ENUM);
+  MX_REQUIRE(hadamard == 0 || hadamard == 1, MX_ERR_ENUM);
+  MX_REQUIRE(rows0 >= 0 && rows1 >= 0 && cols >= 0 && cols % 32 == 0, MX_ERR_SHAPE);
+  if (cols == 0 || rows0 + rows1 == 0) return MX_OK;
+  if (rows0 > 0) {
+    MX_REQUIRE(x0 && codes0 && scales0, MX_ERR_NULL);
+    MX_REQUIRE(aligned16(x0) && aligned16(codes0), MX_ERR_ALIGN);
+  }
+  if (rows1 > 0) {
+    MX_REQUIRE(x1 && codes1 && scales1, MX_ERR_NULL);
+    MX_REQUIRE(aligned16(x1) && aligned16(codes1), MX_ERR_ALIGN);
+  }
+  return quantize_rows2_impl(x0, rows0, cols, codes0, scales0, seed0, x1, rows1, cols, codes1,
+                             scales1, seed1, dtype, round, hadamard, sign_mask, as_stream(stream));
+}
+
 extern "C" int mx_quantize_dual(const void* x, int dtype, int64_t rows, int64_t cols, int round,
                                 uint64_t seed_row, uint64_t seed_col, uint8_t* codes_row,
                                 uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
@@ -846,6 +960,29 @@ extern "C" int mx_requantize(const uint8_t* codes_in, const uint8_t* scales_in, 
   MX_REQUIRE(aligned16(codes_in) && aligned16(codes_out), MX_ERR_ALIGN);
   return requantize_impl(codes_in, scales_in, rows, cols, round, seed, codes_out, scales_out,
                          as_stream(stream));
+}
+
+extern "C" int mx_requantize_pair(const uint8_t* codes_in0, const uint8_t* scales_in0,
+                                  int64_t rows0, const uint8_t* codes_in1,
+                                  const uint8_t* scales_in1, int64_t rows1, int64_t cols,
+                                  int round, uint64_t seed0, uint64_t seed1, uint8_t* codes_out0,
+                                  uint8_t* scales_out0, uint8_t* codes_out1, uint8_t* scales_out1,
+                                  void* stream) {
+  MX_REQUIRE(round == MX_RNE || round == MX_SR, MX_ERR_ENUM);
+  MX_REQUIRE(rows0 >= 0 && rows1 >= 0 && cols >= 0, MX_ERR_SHAPE);
+  MX_REQUIRE(rows0 % 32 == 0 && rows1 % 32 == 0 && cols % 32 == 0, MX_ERR_SHAPE);
+  if (cols == 0 || rows0 + rows1 == 0) return MX_OK;
+  if (rows0 > 0) {
+    MX_REQUIRE(codes_in0 && scales_in0 && codes_out0 && scales_out0, MX_ERR_NULL);
+    MX_REQUIRE(aligned16(codes_in0) && aligned16(codes_out0), MX_ERR_ALIGN);
+  }
+  if (rows1 > 0) {
+    MX_REQUIRE(codes_in1 && scales_in1 && codes_out1 && scales_out1, MX_ERR_NULL);
+    MX_REQUIRE(aligned16(codes_in1) && aligned16(codes_out1), MX_ERR_ALIGN);
+  }
+  return requantize_pair_impl(codes_in0, scales_in0, rows0, codes_in1, scales_in1, rows1, cols,
+                              round, seed0, seed1, codes_out0, scales_out0, codes_out1,
+                              scales_out1, as_stream(stream));
 }
 
 extern "C" int mx_requantize_rht(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,

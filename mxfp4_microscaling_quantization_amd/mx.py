@@ -31,6 +31,10 @@ SIGNATURES = {
     "mx_quantize": ([_P, _i32, _i64, _i64, _i32, _i32, _u64, _i32, _u32, _P, _P, _P], _i32),
     "mx_quantize_dual": ([_P, _i32, _i64, _i64, _i32, _u64, _u64, _P, _P, _P, _P, _P], _i32),
     "mx_requantize": ([_P, _P, _i64, _i64, _i32, _u64, _P, _P, _P], _i32),
+    "mx_quantize_pair": ([_P, _i64, _P, _i64, _i64, _i32, _i32, _u64, _u64, _i32, _u32,
+                          _P, _P, _P, _P, _P], _i32),
+    "mx_requantize_pair": ([_P, _P, _i64, _P, _P, _i64, _i64, _i32, _u64, _u64,
+                            _P, _P, _P, _P, _P], _i32),
     "mx_quantize_dual_rht": ([_P, _i32, _i64, _i64, _i32, _u64, _u64, _u32, _P, _P, _P, _P, _P], _i32),
     "mx_requantize_rht": ([_P, _P, _i64, _i64, _i32, _u64, _u32, _P, _P, _P], _i32),
     "mx_segments_padded_rows": ([_P, _i64], _i64),
@@ -146,6 +150,22 @@ def mx_requantize(codes_in, scales_in, rows, cols, round, seed, codes_out, scale
     _check("mx_requantize", lib().mx_requantize(_ptr(codes_in), _ptr(scales_in), rows, cols, round,
                                                 seed, _ptr(codes_out), _ptr(scales_out),
                                                 _stream(stream)))
+
+
+def mx_quantize_pair(x0, rows0, x1, rows1, cols, dtype, round, seed0, seed1, hadamard, sign_mask,
+                     codes0, scales0, codes1, scales1, stream=None):
+    _check("mx_quantize_pair", lib().mx_quantize_pair(
+        _ptr(x0), rows0, _ptr(x1), rows1, cols, dtype, round, seed0, seed1, hadamard, sign_mask,
+        _ptr(codes0), _ptr(scales0), _ptr(codes1), _ptr(scales1), _stream(stream)))
+
+
+def mx_requantize_pair(codes_in0, scales_in0, rows0, codes_in1, scales_in1, rows1, cols, round,
+                       seed0, seed1, codes_out0, scales_out0, codes_out1, scales_out1,
+                       stream=None):
+    _check("mx_requantize_pair", lib().mx_requantize_pair(
+        _ptr(codes_in0), _ptr(scales_in0), rows0, _ptr(codes_in1), _ptr(scales_in1), rows1, cols,
+        round, seed0, seed1, _ptr(codes_out0), _ptr(scales_out0), _ptr(codes_out1),
+        _ptr(scales_out1), _stream(stream)))
 
 
 def mx_dequantize(codes, scales, rows, cols, axis, hadamard, sign_mask, out, out_dtype,

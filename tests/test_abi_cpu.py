@@ -75,6 +75,27 @@ def test_other_quantizer_validation(L):
     assert L.mx_dequantize(GOOD, None, 32, 32, 0, 0, 0, GOOD, 0, None) == mx.MX_ERR_NULL
 
 
+def test_pair_entry_points_validation(L):
+    qp, rp = L.mx_quantize_pair, L.mx_requantize_pair
+    # x0, rows0, x1, rows1, cols, dtype, round, seed0, seed1, had, mask, c0, s0, c1, s1, stream
+    assert qp(GOOD, 32, GOOD, 64, 48, 0, 0, 0, 0, 0, 0, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_SHAPE
+    assert qp(GOOD, -32, GOOD, 64, 64, 0, 0, 0, 0, 0, 0, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_SHAPE
+    assert qp(GOOD, 32, GOOD, 64, 64, 3, 0, 0, 0, 0, 0, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_ENUM
+    assert qp(GOOD, 32, GOOD, 64, 64, 0, 2, 0, 0, 0, 0, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_ENUM
+    assert qp(GOOD, 32, GOOD, 64, 64, 0, 0, 0, 0, 2, 0, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_ENUM
+    assert qp(GOOD, 32, None, 64, 64, 0, 0, 0, 0, 0, 0, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_NULL
+    assert qp(GOOD, 32, GOOD, 64, 64, 0, 0, 0, 0, 0, 0, BAD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_ALIGN
+    # a tensor with no rows is skipped and may be NULL; both empty is a no-op
+    assert qp(None, 0, None, 0, 64, 0, 0, 0, 0, 0, 0, None, None, None, None, None) == mx.MX_OK
+    # codes_in0, scales_in0, rows0, codes_in1, scales_in1, rows1, cols, round, seed0, seed1, outs, stream
+    assert rp(GOOD, GOOD, 32, GOOD, GOOD, 48, 64, 1, 0, 0, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_SHAPE
+    assert rp(GOOD, GOOD, 32, GOOD, GOOD, 64, 40, 1, 0, 0, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_SHAPE
+    assert rp(GOOD, GOOD, 32, GOOD, GOOD, 64, 64, 4, 0, 0, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_ENUM
+    assert rp(GOOD, GOOD, 32, GOOD, None, 64, 64, 1, 0, 0, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_NULL
+    assert rp(GOOD, GOOD, 32, GOOD, GOOD, 64, 64, 1, 0, 0, GOOD, GOOD, BAD, GOOD, None) == mx.MX_ERR_ALIGN
+    assert rp(None, None, 0, None, None, 0, 64, 1, 0, 0, None, None, None, None, None) == mx.MX_OK
+
+
 def test_gemm_validation(L):
     g = L.mx_gemm
     assert g(GOOD, GOOD, GOOD, GOOD, 4, 4, 48, 1.0, GOOD, 4, None) == mx.MX_ERR_SHAPE   # K % 32

@@ -198,6 +198,46 @@ def test_quantize_sweep_size_sampled_blocks():
                 assert_bytes_equal(got, O.pack_codes(wc), "sampled codes")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rnd,had", [(mx.MX_RNE, 0), (mx.MX_SR, 0), (mx.MX_RNE, 1), (mx.MX_SR, 1)])
+@pytest.mark.parametrize("rows0,rows1", [(37, 300), (0, 96), (64, 0), (1, 1)])
+def test_quantize_pair_equals_two_quantizations(dtype, rnd, had, rows0, rows1):
+    cols, mask = 224, 0x1357_9BDF
+    x0 = mixed_input(max(rows0, 1), cols, 51, dtype)[:rows0]
+    x1 = mixed_input(max(rows1, 1), cols, 52, dtype)[:rows1]
+    d0, d1 = upload(x0, dtype), upload(x1, dtype)
+    u8 = lambda *sh: torch.full(sh, 0x55, dtype=torch.uint8, device=DEV)
+    c0, s0, c1, s1 = u8(rows0, cols // 2), u8(rows0, cols // 32), u8(rows1, cols // 2), u8(rows1, cols // 32)
+    mx.mx_quantize_pair(d0, rows0, d1, rows1, cols, mx.dtype_code(d0), rnd, 11, 12, had, mask,
+                        c0, s0, c1, s1)
+    for d, rows, c, s, seed in ((d0, rows0, c0, s0, 11), (d1, rows1, c1, s1, 12)):
+        if rows == 0:
+            continue
+        wc, ws = mx.quantize(d, mx.MX_ROW, rnd, seed, had, mask)
+        assert torch.equal(c, wc) and torch.equal(s, ws), (rows, seed)
+
+
+@pytest.mark.parametrize("rows0,rows1,cols", [(96, 544, 160), (0, 64, 96), (288, 0, 64), (32, 32, 32)])
+@pytest.mark.parametrize("rnd", [mx.MX_RNE, mx.MX_SR])
+def test_requantize_pair_equals_two_requantizations(rows0, rows1, cols, rnd):
+    def packed(rows, seed):
+        x = mixed_input(max(rows, 32), cols, seed, "f32")[:rows]
+        return O.quantize(x, O.ROW, O.RNE) if rows else (np.zeros((0, cols // 2), np.uint8),
+                                                         np.zeros((0, cols // 32), np.uint8))
+    a, b = packed(rows0, 61), packed(rows1, 62)
+    u8 = lambda *sh: torch.full(sh, 0x55, dtype=torch.uint8, device=DEV)
+    outs = (u8(cols, rows0 // 2), u8(cols, rows0 // 32), u8(cols, rows1 // 2), u8(cols, rows1 // 32))
+    ins = [to_dev_u8(z) for z in (*a, *b)]
+    mx.mx_requantize_pair(ins[0], ins[1], rows0, ins[2], ins[3], rows1, cols, rnd, 21, 22, *outs)
+    for (ci, si), rows, c, s, seed in (((ins[0], ins[1]), rows0, outs[0], outs[1], 21),
+                                       ((ins[2], ins[3]), rows1, outs[2], outs[3], 22)):
+        if rows == 0:
+            continue
+        wc, ws = u8(cols, rows // 2), u8(cols, rows // 32)
+        mx.mx_requantize(ci, si, rows, cols, rnd, seed, wc, ws)
+        assert torch.equal(c, wc) and torch.equal(s, ws), (rows, seed)
+
+
 def test_quantize_is_deterministic():
     x = mixed_input(544, 200, 4, "bf16")
     d = upload(x, "bf16")
