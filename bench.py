@@ -352,12 +352,13 @@ def bench_moe(torch, mx, synth, dev, iters=10, deosc_steps=20):
 # ---------------------------------------------------------------- CPU oracle baseline
 def cpu_baseline(synth):
     """The oracle's linear fwd + bwd on a bounded slice of the same workload
-    (first 512 tokens, first 1024 output features, full K = 4096), one core."""
+    (first 2048 tokens, first 4096 output features, full K = 4096; about 15 s of
+    one core), one core."""
     import oracle as O
     from threadpoolctl import threadpool_limits
 
     cfg = synth.llama_config()
-    Ms, Ns, K = 512, 1024, cfg["K"]
+    Ms, Ns, K = 2048, 4096, cfg["K"]
     x = O.bf16_bits_to_f32(cfg["x"][:Ms])
     w = O.bf16_bits_to_f32(cfg["w"][:Ns])
     dy = O.bf16_bits_to_f32(cfg["dy"][:Ms, :Ns])
