@@ -94,40 +94,47 @@ __device__ __forceinline__ uint32_t quant8(const float v[8], uint32_t byte, uint
 // any of them is quantized (more bytes in flight per lane).
 constexpr int kRowU = 4;
 
-// Up to two tensors quantized by one launch (the forward layer's X and W):
-// blocks [0, n0) belong to tensor 0, [n0, nblk) to tensor 1, each indexed from
-// its own first block.
+// Up to two tensors quantized by one launch (the forward layer's X and W).  The
+// grid strides over windows of 64 kRowU consecutive blocks; windows [0, w0)
+// cover tensor 0 (n0 blocks), the rest tensor 1 (n1 blocks), so the tensor is
+// uniform over a workgroup's window and each is indexed from its own block 0.
 template <typename T>
-struct RowJobs {
-  const T* x[2];
-  uint32_t* codes[2];
-  uint8_t* scales[2];
-  uint64_t seed[2];
-  int64_t n0;
-  int64_t nblk;
+struct RowJobs {  // named fields: selected with ternaries, never indexed at run time
+  const T* x0;
+  const T* x1;
+  uint32_t* codes0;
+  uint32_t* codes1;
+  uint8_t* scales0;
+  uint8_t* scales1;
+  uint64_t seed0, seed1;
+  int64_t n0, n1;
+  int64_t w0;  // windows of tensor 0
+  int64_t nwin;
 };
 
-template <typename T, int ROUND, bool HAD>
+template <typename T, int ROUND, bool HAD, bool PAIR>
 __global__ __launch_bounds__(256) void k_quant_row(const RowJobs<T> jobs, uint32_t sign_mask) {
   const int q = threadIdx.x & 3;
   const int j = threadIdx.x >> 2;
-  const int64_t nblk = jobs.nblk, n0 = jobs.n0;
-  for (int64_t base = (int64_t)blockIdx.x * 64 * kRowU; base < nblk;
-       base += (int64_t)gridDim.x * 64 * kRowU) {
+  for (int64_t win = blockIdx.x; win < jobs.nwin; win += gridDim.x) {
+    const bool t = PAIR && win >= jobs.w0;  // uniform over the workgroup
+    const T* __restrict__ x = t ? jobs.x1 : jobs.x0;
+    uint32_t* __restrict__ codes = t ? jobs.codes1 : jobs.codes0;
+    uint8_t* __restrict__ scales = t ? jobs.scales1 : jobs.scales0;
+    const uint64_t seed = t ? jobs.seed1 : jobs.seed0;
+    const int64_t nblk = t ? jobs.n1 : jobs.n0;
+    const int64_t base = (win - (t ? jobs.w0 : 0)) * 64 * kRowU;
     float v[kRowU][8];
 #pragma unroll
     for (int u = 0; u < kRowU; ++u) {
       // unconditional (clamped) loads, so that all of them are in flight at once
       const int64_t b = min(base + u * 64 + j, nblk - 1);
-      const bool t1 = b >= n0;
-      load8<T>((t1 ? jobs.x[1] + (b - n0) * 32 : jobs.x[0] + b * 32) + q * 8, v[u]);
+      load8<T>(x + b * 32 + q * 8, v[u]);
     }
 #pragma unroll
     for (int u = 0; u < kRowU; ++u) {
       const int64_t b = base + u * 64 + j;
       if (b >= nblk) break;  // quads past the end: whole quads, so the DPP partners agree
-      const bool t1 = b >= n0;
-      const int64_t lb = t1 ? b - n0 : b;  // block index within its tensor
       if (HAD) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[u][i] = apply_sign(v[u][i], sign_mask, q * 8 + i);
@@ -138,9 +145,8 @@ __global__ __launch_bounds__(256) void k_quant_row(const RowJobs<T> jobs, uint32
       for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[u][i]) & 0x7FFFFFFFu);
       m = quad_max_u32(m);
       const uint32_t byte = scale_byte_of(m);
-      (t1 ? jobs.codes[1] : jobs.codes[0])[lb * 4 + q] =
-          quant8<ROUND>(v[u], byte, t1 ? jobs.seed[1] : jobs.seed[0], (uint64_t)lb * 32 + q * 8);
-      if (q == 0) (t1 ? jobs.scales[1] : jobs.scales[0])[lb] = (uint8_t)byte;
+      codes[b * 4 + q] = quant8<ROUND>(v[u], byte, seed, (uint64_t)b * 32 + q * 8);
+      if (q == 0) scales[b] = (uint8_t)byte;
     }
   }
 }
@@ -617,15 +623,29 @@ static int grid_for_blocks(int64_t nblk) {
 }
 
 template <typename T>
-static int launch_quant_row_jobs(const RowJobs<T>& jobs, int round, int had, uint32_t mask,
+static int launch_quant_row_jobs(RowJobs<T> jobs, int round, int had, uint32_t mask,
                                  hipStream_t st) {
-  const dim3 grid(grid_for_row(jobs.nblk)), block(256);
-  if (round == MX_RNE) {
-    if (had) k_quant_row<T, MX_RNE, true><<<grid, block, 0, st>>>(jobs, mask);
-    else k_quant_row<T, MX_RNE, false><<<grid, block, 0, st>>>(jobs, mask);
-  } else {
-    if (had) k_quant_row<T, MX_SR, true><<<grid, block, 0, st>>>(jobs, mask);
-    else k_quant_row<T, MX_SR, false><<<grid, block, 0, st>>>(jobs, mask);
+  const int64_t per = 64 * kRowU;  // blocks per window
+  jobs.w0 = cdiv(jobs.n0, per);
+  jobs.nwin = jobs.w0 + cdiv(jobs.n1, per);
+  if (jobs.nwin == 0) return MX_OK;
+  const dim3 grid(grid_for_row(jobs.nwin * per)), block(256);
+  if (jobs.n1 > 0) {
+    if (round == MX_RNE) {
+      if (had) k_quant_row<T, MX_RNE, true, true><<<grid, block, 0, st>>>(jobs, mask);
+      else k_quant_row<T, MX_RNE, false, true><<<grid, block, 0, st>>>(jobs, mask);
+    } else {
+      if (had) k_quant_row<T, MX_SR, true, true><<<grid, block, 0, st>>>(jobs, mask);
+      else k_quant_row<T, MX_SR, false, true><<<grid, block, 0, st>>>(jobs, mask);
+    }
+  } else {  // one tensor: the selection compiles away
+    if (round == MX_RNE) {
+      if (had) k_quant_row<T, MX_RNE, true, false><<<grid, block, 0, st>>>(jobs, mask);
+      else k_quant_row<T, MX_RNE, false, false><<<grid, block, 0, st>>>(jobs, mask);
+    } else {
+      if (had) k_quant_row<T, MX_SR, true, false><<<grid, block, 0, st>>>(jobs, mask);
+      else k_quant_row<T, MX_SR, false, false><<<grid, block, 0, st>>>(jobs, mask);
+    }
   }
   return launch_status();
 }
@@ -635,11 +655,12 @@ static int launch_quant_row(const T* x, int64_t rows, int64_t cols, int round, u
                             int had, uint32_t mask, uint8_t* codes, uint8_t* scales,
                             hipStream_t st) {
   RowJobs<T> jobs{};
-  jobs.x[0] = jobs.x[1] = x;
-  jobs.codes[0] = jobs.codes[1] = reinterpret_cast<uint32_t*>(codes);
-  jobs.scales[0] = jobs.scales[1] = scales;
-  jobs.seed[0] = jobs.seed[1] = seed;
-  jobs.nblk = jobs.n0 = rows * cols / 32;
+  jobs.x0 = jobs.x1 = x;
+  jobs.codes0 = jobs.codes1 = reinterpret_cast<uint32_t*>(codes);
+  jobs.scales0 = jobs.scales1 = scales;
+  jobs.seed0 = jobs.seed1 = seed;
+  jobs.n0 = rows * cols / 32;
+  jobs.n1 = 0;
   return launch_quant_row_jobs(jobs, round, had, mask, st);
 }
 
@@ -775,16 +796,16 @@ static int launch_quant_rows2(const void* x0, int64_t n0, uint8_t* codes0, uint8
                               uint8_t* scales1, uint64_t seed1, int round, int had,
                               uint32_t mask, hipStream_t st) {
   RowJobs<T> jobs{};
-  jobs.x[0] = static_cast<const T*>(x0);
-  jobs.x[1] = static_cast<const T*>(x1);
-  jobs.codes[0] = reinterpret_cast<uint32_t*>(codes0);
-  jobs.codes[1] = reinterpret_cast<uint32_t*>(codes1);
-  jobs.scales[0] = scales0;
-  jobs.scales[1] = scales1;
-  jobs.seed[0] = seed0;
-  jobs.seed[1] = seed1;
+  jobs.x0 = static_cast<const T*>(x0);
+  jobs.x1 = static_cast<const T*>(x1);
+  jobs.codes0 = reinterpret_cast<uint32_t*>(codes0);
+  jobs.codes1 = reinterpret_cast<uint32_t*>(codes1);
+  jobs.scales0 = scales0;
+  jobs.scales1 = scales1;
+  jobs.seed0 = seed0;
+  jobs.seed1 = seed1;
   jobs.n0 = n0;
-  jobs.nblk = n0 + n1;
+  jobs.n1 = n1;
   return launch_quant_row_jobs(jobs, round, had, mask, st);
 }
 
