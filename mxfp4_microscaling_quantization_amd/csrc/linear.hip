@@ -32,9 +32,11 @@ int requantize_pair_impl(const uint8_t* codes_in0, const uint8_t* scales_in0, in
                          int64_t cols, int round, uint64_t seed0, uint64_t seed1,
                          uint8_t* codes0, uint8_t* scales0, uint8_t* codes1, uint8_t* scales1,
                          hipStream_t st);
-int requantize_rht_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
-                        int64_t cols, int round, uint64_t seed, uint32_t mask, uint8_t* codes,
-                        uint8_t* scales, hipStream_t st);
+int requantize_rht_pair_impl(const uint8_t* codes_in0, const uint8_t* scales_in0, int64_t rows0,
+                             const uint8_t* codes_in1, const uint8_t* scales_in1, int64_t rows1,
+                             int64_t cols, int round, uint64_t seed0, uint64_t seed1,
+                             uint32_t mask, uint8_t* codes0, uint8_t* scales0, uint8_t* codes1,
+                             uint8_t* scales1, hipStream_t st);
 int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
               const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha, float* c,
               int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, hipStream_t st);
@@ -167,12 +169,10 @@ static int linear_bwd_impl(const void* dy, int dtype, int64_t M, int64_t N, int6
   int s = quantize_dual_impl(dy, dtype, M, N, MX_SR, seed + 3, seed + 5, had, mask, ws + L.q3c,
                              ws + L.q3s, ws + L.q5c, ws + L.q5s, st);
   if (s != MX_OK) return s;
-  if (had) {
-    s = requantize_rht_impl(wq_codes, wq_scales, N, K, MX_SR, seed + 4, mask, ws + L.q4c,
-                            ws + L.q4s, st);
-    if (s != MX_OK) return s;
-    s = requantize_rht_impl(xq_codes, xq_scales, M, K, MX_SR, seed + 6, mask, ws + L.q6c,
-                            ws + L.q6s, st);
+  if (had) {  // the rotated Q4 and Q6 in one launch
+    s = requantize_rht_pair_impl(wq_codes, wq_scales, N, xq_codes, xq_scales, M, K, MX_SR,
+                                 seed + 4, seed + 6, mask, ws + L.q4c, ws + L.q4s, ws + L.q6c,
+                                 ws + L.q6s, st);
   } else {  // Q4 = Q_S(Q_D(W)) and Q6 = Q_S(Q_D(X)) in one launch
     s = requantize_pair_impl(wq_codes, wq_scales, N, xq_codes, xq_scales, M, K, MX_SR, seed + 4,
                              seed + 6, ws + L.q4c, ws + L.q4s, ws + L.q6c, ws + L.q6s, st);

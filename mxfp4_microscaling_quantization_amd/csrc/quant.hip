@@ -476,20 +476,40 @@ __global__ __launch_bounds__(256) void k_requant(const RqJob j0, const RqJob j1,
 constexpr int kRhtR = 128;
 constexpr int kRhtC = 64;
 
+// One launch can take two matrices with the same cols and sign mask (the
+// rotated backward's Q_D(H W) and Q_D(H X)): tile rows [0, ty0) of the grid
+// belong to matrix 0.  Named fields, selected per workgroup.
+struct RhtJobs {
+  const uint8_t* codes_in0;
+  const uint8_t* codes_in1;
+  const uint8_t* scales_in0;
+  const uint8_t* scales_in1;
+  int64_t rows0, rows1;
+  uint64_t seed0, seed1;
+  uint8_t* codes0;
+  uint8_t* codes1;
+  uint8_t* scales0;
+  uint8_t* scales1;
+  int ty0;
+};
+
 template <int ROUND>
-__global__ __launch_bounds__(256) void k_requant_rht(const uint8_t* __restrict__ codes_in,
-                                                     const uint8_t* __restrict__ scales_in,
-                                                     int64_t rows, int64_t cols, uint64_t seed,
-                                                     uint32_t sign_mask,
-                                                     uint8_t* __restrict__ codes,
-                                                     uint8_t* __restrict__ scales) {
+__global__ __launch_bounds__(256) void k_requant_rht(const RhtJobs jobs, int64_t cols,
+                                                     uint32_t sign_mask) {
   constexpr int NRB = kRhtR / 32;
   __shared__ float s_x[kRhtR * kRhtC];  // [row][col]
   __shared__ uint4 s_codes[kRhtC * NRB];
   __shared__ uint8_t s_scales[kRhtC * NRB];
 
+  const bool t = (int)blockIdx.y >= jobs.ty0;  // uniform over the workgroup
+  const uint8_t* __restrict__ codes_in = t ? jobs.codes_in1 : jobs.codes_in0;
+  const uint8_t* __restrict__ scales_in = t ? jobs.scales_in1 : jobs.scales_in0;
+  const int64_t rows = t ? jobs.rows1 : jobs.rows0;
+  const uint64_t seed = t ? jobs.seed1 : jobs.seed0;
+  uint8_t* __restrict__ codes = t ? jobs.codes1 : jobs.codes0;
+  uint8_t* __restrict__ scales = t ? jobs.scales1 : jobs.scales0;
   const int64_t col0 = (int64_t)blockIdx.x * kRhtC;
-  const int64_t row0 = (int64_t)blockIdx.y * kRhtR;
+  const int64_t row0 = (int64_t)((int)blockIdx.y - (t ? jobs.ty0 : 0)) * kRhtR;
   const int ncols = (int)min<int64_t>(kRhtC, cols - col0);   // 32 or 64
   const int nrows = (int)min<int64_t>(kRhtR, rows - row0);   // multiple of 32
   const int nrb = nrows / 32;
@@ -497,6 +517,10 @@ __global__ __launch_bounds__(256) void k_requant_rht(const uint8_t* __restrict__
   const int q = threadIdx.x & 3;
 
   // ---- decode and undo the row rotation: quad j takes row blocks j, j + 64, ...
+  // The factor 2^-5 and the sign of element q*8+i are one exact multiply.
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = apply_sign(0.03125f, sign_mask, q * 8 + i);
   for (int blk = threadIdx.x >> 2; blk < kRhtR * (kRhtC / 32); blk += 64) {
     const int r = blk / (kRhtC / 32), kb = blk % (kRhtC / 32);
     if (r >= nrows || kb * 32 >= ncols) continue;  // whole quads drop out together
@@ -507,7 +531,7 @@ __global__ __launch_bounds__(256) void k_requant_rht(const uint8_t* __restrict__
     decode8(wcodes, byte, v);
     fwht32_quad(v, q);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = apply_sign(v[i] * 0.03125f, sign_mask, q * 8 + i);
+    for (int i = 0; i < 8; ++i) v[i] *= f[i];
     float* dst = &s_x[r * kRhtC + kb * 32 + q * 8];
     reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
     reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
@@ -888,16 +912,33 @@ int quantize_dual_impl(const void* x, int dtype, int64_t rows, int64_t cols, int
                        scales_col, st);
 }
 
+static int launch_requant_rht(const RhtJobs& jobs, int ty1, int64_t cols, int round,
+                              uint32_t mask, hipStream_t st) {
+  if (jobs.ty0 + ty1 == 0 || cols == 0) return MX_OK;
+  const dim3 grid((unsigned)cdiv(cols, kRhtC), (unsigned)(jobs.ty0 + ty1)), block(256);
+  if (round == MX_RNE) k_requant_rht<MX_RNE><<<grid, block, 0, st>>>(jobs, cols, mask);
+  else k_requant_rht<MX_SR><<<grid, block, 0, st>>>(jobs, cols, mask);
+  return launch_status();
+}
+
 int requantize_rht_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
                         int64_t cols, int round, uint64_t seed, uint32_t mask, uint8_t* codes,
                         uint8_t* scales, hipStream_t st) {
   if (rows == 0 || cols == 0) return MX_OK;
-  const dim3 grid((unsigned)cdiv(cols, kRhtC), (unsigned)cdiv(rows, kRhtR)), block(256);
-  if (round == MX_RNE)
-    k_requant_rht<MX_RNE><<<grid, block, 0, st>>>(codes_in, scales_in, rows, cols, seed, mask, codes, scales);
-  else
-    k_requant_rht<MX_SR><<<grid, block, 0, st>>>(codes_in, scales_in, rows, cols, seed, mask, codes, scales);
-  return launch_status();
+  const RhtJobs j{codes_in, codes_in, scales_in, scales_in, rows, rows, seed, seed,
+                  codes, codes, scales, scales, (int)cdiv(rows, kRhtR)};
+  return launch_requant_rht(j, 0, cols, round, mask, st);
+}
+
+// Two rotated double quantizations (same cols and sign mask) in one launch.
+int requantize_rht_pair_impl(const uint8_t* codes_in0, const uint8_t* scales_in0, int64_t rows0,
+                             const uint8_t* codes_in1, const uint8_t* scales_in1, int64_t rows1,
+                             int64_t cols, int round, uint64_t seed0, uint64_t seed1,
+                             uint32_t mask, uint8_t* codes0, uint8_t* scales0, uint8_t* codes1,
+                             uint8_t* scales1, hipStream_t st) {
+  const RhtJobs j{codes_in0, codes_in1, scales_in0, scales_in1, rows0, rows1, seed0, seed1,
+                  codes0, codes1, scales0, scales1, (int)cdiv(rows0, kRhtR)};
+  return launch_requant_rht(j, (int)cdiv(rows1, kRhtR), cols, round, mask, st);
 }
 
 }  // namespace mx
