@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parts", action="store_true", help="skip the quantizer sweep / MoE rows")
-    p.add_argument("--only", default=None, help="run one part only: linear|rht|sweep|moe|deosc")
+    p.add_argument("--only", default=None, help="run one part only: linear|deit|rht|sweep|moe|deosc")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (known HBM bytes) for counter scaling")
     return p.parse_args()
@@ -202,6 +202,87 @@ def bench_linear_rht(torch, mx, synth, dev, steps=10, seed=3, mask=0x9E3779B9):
     fl = 2.0 * M * N * K
     return {"fwd_us": f * 1e3, "bwd_us": b * 1e3, "fwd_bwd_ms": f + b,
             "TFLOPs": 3 * fl / ((f + b) * 1e-3) / 1e12, "sign_mask": mask}
+
+
+# ---------------------------------------------------------------- DeiT-S fc1 layer
+def bench_linear_deit(torch, mx, synth, dev, steps=50, seed=1):
+    """The DeiT-S MLP fc1 layer (M = 12608 tokens, K = 384, N = 1536) through the
+    library's own entry points mx_linear_fwd + mx_linear_bwd.  Its six kernels
+    take tens of microseconds each, so eager launches from Python leave the GPU
+    idle between them; the layer is also captured once in a HIP graph and
+    replayed (every replay checked bit for bit against the eager outputs before
+    the timed replays).  The GEMMs are bound by their fp32 output writes
+    (K = 384): the attainable time is the sum over the six kernels of
+    max(flops / FP4 peak, algorithmic bytes / HBM peak)."""
+    cfg = synth.deit_config()
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    x = bf16_dev(torch, cfg["x"], dev)
+    w = bf16_dev(torch, cfg["w"], dev)
+    dy = bf16_dev(torch, cfg["dy"], dev)
+    del cfg
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)
+    y, dx, dw = (torch.empty(s, dtype=torch.float32, device=dev) for s in ((M, N), (M, K), (N, K)))
+    xq, wq = (u8(M, K // 2), u8(M, K // 32)), (u8(N, K // 2), u8(N, K // 32))
+    ws = u8(mx.mx_linear_bwd_workspace_size(M, N, K))
+    BF = mx.MX_BF16
+
+    def layer(st):
+        mx.mx_linear_fwd(x, w, BF, M, N, K, y, *xq, *wq, st)
+        mx.mx_linear_bwd(dy, BF, M, N, K, *xq, *wq, seed, dx, dw, ws, ws.numel(), st)
+
+    st = torch.cuda.current_stream()
+    for _ in range(3):
+        layer(st)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (y, dx, dw, *xq, *wq)]
+
+    def eager_ms():
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(steps):
+            layer(st)
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    eager = eager_ms()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    replays_equal = True
+    for _ in range(3):  # eager fills between replays, every replay checked
+        for t in (y, dx, dw, *xq, *wq):
+            t.fill_(0x5A if t.dtype == torch.uint8 else float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        replays_equal &= all(torch.equal(a, b) for a, b in zip((y, dx, dw, *xq, *wq), want))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for _ in range(steps):
+        g.replay()
+    b.record(st)
+    torch.cuda.synchronize()
+    graph = a.elapsed_time(b) / steps
+    del g
+    fl = 2.0 * M * N * K
+    pk = 0.53125  # packed bytes per element (codes + scales)
+    kernels = [  # (flops, algorithmic bytes)
+        (0, (M + N) * K * (2 + pk)),                       # quantize X and W
+        (fl, (M + N) * K * pk + 4 * M * N),                 # Y
+        (0, M * N * (2 + 2 * pk)),                          # dual quantize dY
+        (0, (N + M) * K * 2 * pk),                          # double quantize W and X
+        (fl, (M + N) * N * pk + 4 * M * K),                 # dX
+        (fl, (N + K) * M * pk + 4 * N * K),                 # dW
+    ]
+    ideal_ms = sum(max(a / (PEAK_FP4_TFLOPS * 1e12), c / (PEAK_HBM_GBPS * 1e9))
+                   for a, c in kernels) * 1e3
+    return {"M": M, "N": N, "K": K, "eager_ms": eager, "graph_ms": graph,
+            "graph_replays_equal_eager": bool(replays_equal),
+            "TFLOPs_graph": 3 * fl / (graph * 1e-3) / 1e12,
+            "TFLOPs_eager": 3 * fl / (eager * 1e-3) / 1e12, "attainable_ms": ideal_ms,
+            "frac_attainable_graph": ideal_ms / graph}
 
 
 # ---------------------------------------------------------------- quantizer sweep
@@ -401,6 +482,10 @@ def main():
     if args.only in (None, "linear"):
         log("linear fwd+bwd (Llama-3-8B up-projection)")
         lin = bench_linear(torch, mx, synth, dev, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+    if not args.no_parts and args.only in (None, "deit"):
+        log("DeiT-S fc1 linear fwd+bwd")
+        parts["linear_deit_s_fc1"] = bench_linear_deit(torch, mx, synth, dev)
         torch.cuda.empty_cache()
     if not args.no_parts and args.only in (None, "rht"):
         log("rotated linear fwd+bwd (Llama-3-8B up-projection)")

@@ -499,17 +499,22 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
   }
 
   // ---- epilogue: lane holds D[n = 8 g + 4 lh + v][m = lr], g, v = 0..3, of each 32x32 tile
-  if constexpr (TM == 4 && TN == 4) {
-    // The LDS ring is idle now: each wave stages its 128 x 128 sub-tile there
-    // in two passes of 64 rows (32 KB per wave; row pitch 512 B, 16-byte chunk
-    // index XORed with row & 15, so the 16-row writes and the row reads are
-    // free of bank conflicts) and reads it back so that every store
-    // instruction writes two whole 512-byte row segments of C.
-    static_assert(sizeof(ring) >= 4 * 32768, "staging space");
+  // The LDS ring is idle now: each wave stages its sub-tile there, 64 rows per
+  // pass (row pitch CH 16-byte chunks, chunk index XORed with row & 15, so the
+  // 16-row writes and the row reads are free of bank conflicts), and reads it
+  // back so that every store instruction writes whole row segments of C
+  // (two rows of 512 bytes for 256 x 256 tiles, four of 256 for 128 x 128)
+  // instead of 32-byte pieces of 32 rows.
+  {
+    constexpr int CH = TN * 8;      // 16-byte chunks per staged row
+    constexpr int RB = CH * 16;     // bytes per staged row
+    constexpr int RPI = 64 / CH;    // rows per read (one chunk per lane)
+    static_assert(TM % 2 == 0 && CH >= 16 && 64 % CH == 0, "staging shape");
+    static_assert(sizeof(ring) >= NW * 64 * RB, "staging space");
     __syncthreads();  // every wave is done reading the ring
-    char* stg = reinterpret_cast<char*>(ring) + wave * 32768;
+    char* stg = reinterpret_cast<char*>(ring) + wave * 64 * RB;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < TM / 2; ++p) {
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb) {
         const int b = 2 * p + bb;
@@ -519,16 +524,16 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
 #pragma unroll
           for (int gq = 0; gq < 4; ++gq) {
             const int ch = a * 8 + gq * 2 + lh;
-            *reinterpret_cast<float4*>(stg + rl * 512 + ((ch ^ (rl & 15)) * 16)) =
+            *reinterpret_cast<float4*>(stg + rl * RB + ((ch ^ (rl & 15)) * 16)) =
                 make_float4(acc[a][b][4 * gq] * alpha, acc[a][b][4 * gq + 1] * alpha,
                             acc[a][b][4 * gq + 2] * alpha, acc[a][b][4 * gq + 3] * alpha);
           }
       }
 #pragma unroll 4
-      for (int it = 0; it < 32; ++it) {
-        const int rl = it * 2 + (lane >> 5), ch = lane & 31;
+      for (int it = 0; it < 64 / RPI; ++it) {
+        const int rl = it * RPI + lane / CH, ch = lane % CH;
         const float4 v =
-            *reinterpret_cast<const float4*>(stg + rl * 512 + ((ch ^ (rl & 15)) * 16));
+            *reinterpret_cast<const float4*>(stg + rl * RB + ((ch ^ (rl & 15)) * 16));
         const int mrow = wm_off + p * 64 + rl;
         const int ncol = wn_off + ch * 4;
         if (mrow < rows_valid) {
@@ -539,29 +544,6 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
             if (ncol + 0 < cols_valid) crow[ncol + 0] = v.x;
             if (ncol + 1 < cols_valid) crow[ncol + 1] = v.y;
             if (ncol + 2 < cols_valid) crow[ncol + 2] = v.z;
-          }
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int b = 0; b < TM; ++b) {
-      const int mrow = wm_off + b * 32 + lr;
-      if (mrow >= rows_valid) continue;
-      float* crow = C + (m0 + mrow) * ldc + n0;
-#pragma unroll
-      for (int a = 0; a < TN; ++a) {
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int ncol = wn_off + a * 32 + gq * 8 + lh * 4;
-          const float v0 = acc[a][b][4 * gq] * alpha, v1 = acc[a][b][4 * gq + 1] * alpha;
-          const float v2 = acc[a][b][4 * gq + 2] * alpha, v3 = acc[a][b][4 * gq + 3] * alpha;
-          if (ncol + 3 < cols_valid) {
-            store_c4(crow + ncol, make_float4(v0, v1, v2, v3), sp.stream_c != 0);
-          } else {
-            if (ncol + 0 < cols_valid) crow[ncol + 0] = v0;
-            if (ncol + 1 < cols_valid) crow[ncol + 1] = v1;
-            if (ncol + 2 < cols_valid) crow[ncol + 2] = v2;
           }
         }
       }
