@@ -56,6 +56,23 @@ struct GemmSplit {
   int64_t kbeg[MX_MAX_GROUPS + 1];
 };
 
+// A second, plain problem in the same launch (one group, the whole contraction,
+// a final output): workgroups past the first problem's take its tiles.  Two
+// small products that each fill one partial round of the CUs (the backward
+// layer's dX and dW at a few thousand tokens) then overlap instead of running
+// one after the other.
+struct GemmPlain {
+  const uint8_t* A;
+  const uint8_t* SA;
+  const uint8_t* B;
+  const uint8_t* SB;
+  int64_t M, N, K;
+  float alpha;
+  float* C;
+  int64_t ldc;
+  int tiles, tiles_n;
+};
+
 // 16-byte store of C.  Final outputs are written with non-temporal stores: the
 // next kernel does not read them, and a GEMM's output (up to several hundred MB)
 // left dirty in the Infinity Cache would otherwise be written back during the
@@ -163,11 +180,12 @@ struct ScaleGroupLds {
   uint4 b[BN];
 };
 
-template <int BM, int BN, int WM, int WN, int STAGES, int SC>
+template <int BM, int BN, int WM, int WN, int STAGES, int SC, bool PAIR>
 __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
-    const uint8_t* __restrict__ SB, int64_t N, int64_t K, float alpha, float* __restrict__ C,
-    int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, GemmGroups gg, GemmSplit sp) {
+    const uint8_t* __restrict__ A0, const uint8_t* __restrict__ SA0, const uint8_t* __restrict__ B0,
+    const uint8_t* __restrict__ SB0, int64_t N0, int64_t K0, float alpha0, float* __restrict__ C0,
+    int64_t ldc0, int64_t b_stride_codes, int64_t b_stride_scales, GemmGroups gg, GemmSplit sp,
+    const GemmPlain p1) {
   constexpr int NW = WM * WN;
   constexpr int TM = BM / WM / 32;  // 32-row MFMA tiles per wave along m
   constexpr int TN = BN / WN / 32;  // along n
@@ -189,24 +207,46 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
   auto bufA = [&](auto S) -> TileLds<BM, SC>& { return stage(S).a; };
   auto bufB = [&](auto S) -> TileLds<BN, SC>& { return stage(S).b; };
 
-  // ---- which tile: spread consecutive logical tiles over one XCD (workgroups
-  // are dealt round-robin to the 8 XCDs), then walk kGroupM tile rows at a time.
-  const int tiles = gg.tile_start[gg.ngroups];
-  const int total = tiles * sp.n;
-  int id = blockIdx.x;
+  // ---- which problem and tile: the first problem's workgroups come first in
+  // dispatch order.  Within a problem, consecutive logical tiles are spread
+  // over one XCD (workgroups are dealt round-robin to the 8 XCDs), then tile
+  // rows are walked kGroupM at a time.
+  const int tiles0 = gg.tile_start[gg.ngroups];
+  const int total0 = tiles0 * sp.n;
+  const bool second = PAIR && (int)blockIdx.x >= total0;  // uniform over the workgroup
+  const int total = second ? p1.tiles : total0;
+  int id = (int)blockIdx.x - (second ? total0 : 0);
   {
     const int q = total / 8, r = total % 8, x = id % 8;
     id = x * q + min(x, r) + id / 8;
   }
-  const int split = id / tiles;
-  id -= split * tiles;
-  int g = 0;
-  while (g + 1 < gg.ngroups && gg.tile_start[g + 1] <= id) ++g;
-  const int lt = id - gg.tile_start[g];
-  const int64_t grow0 = gg.row_off[g];
-  const int64_t grows = gg.row_off[g + 1] - grow0;
+  int split = 0, g = 0, tiles_n = p1.tiles_n;
+  int64_t grow0 = 0, grows = p1.M, a_last = p1.M - 1, k0 = 0, k1 = p1.K;
+  if (!second) {
+    split = id / tiles0;
+    id -= split * tiles0;
+    while (g + 1 < gg.ngroups && gg.tile_start[g + 1] <= id) ++g;
+    id -= gg.tile_start[g];
+    tiles_n = gg.tiles_n;
+    grow0 = gg.row_off[g];
+    grows = gg.row_off[g + 1] - grow0;
+    a_last = gg.row_off[gg.ngroups] - 1;  // last row of A in memory
+    k0 = sp.kbeg[split];
+    k1 = sp.kbeg[split + 1];
+  }
+  const uint8_t* __restrict__ A = second ? p1.A : A0;
+  const uint8_t* __restrict__ SA = second ? p1.SA : SA0;
+  const int64_t N = second ? p1.N : N0;
+  const int64_t K = second ? p1.K : K0;
+  const float alpha = second ? p1.alpha : alpha0;
+  const int64_t ldc = second ? p1.ldc : ldc0;
+  const bool stream_c = second || sp.stream_c != 0;
+  float* __restrict__ C = second ? p1.C : C0 + split * sp.c_stride;
+  const uint8_t* Bg = second ? p1.B : B0 + (int64_t)g * b_stride_codes;
+  const uint8_t* SBg = second ? p1.SB : SB0 + (int64_t)g * b_stride_scales;
+  const int lt = id;
   const int tiles_m = (int)((grows + BM - 1) / BM);
-  const int span = kGroupM * gg.tiles_n;
+  const int span = kGroupM * tiles_n;
   const int first_m = (lt / span) * kGroupM;
   const int gm = min(tiles_m - first_m, kGroupM);
   const int tm_idx = first_m + (lt % span) % gm;
@@ -216,18 +256,13 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
   const int rows_valid = (int)min<int64_t>(BM, grow0 + grows - m0);
   const int64_t n0 = (int64_t)tn_idx * BN;
   const int cols_valid = (int)min<int64_t>(BN, N - n0);
-  const int64_t a_last = gg.row_off[gg.ngroups] - 1;  // last row of A in memory
-  const uint8_t* Bg = B + (int64_t)g * b_stride_codes;
-  const uint8_t* SBg = SB + (int64_t)g * b_stride_scales;
 
   const int64_t ldk = K / 2;   // code bytes per row
   const int64_t lds = K / 32;  // scale bytes (32-blocks) per row
-  const int64_t k0 = sp.kbeg[split];
-  const int64_t kc_len = sp.kbeg[split + 1] - k0;  // K-values of this split
+  const int64_t kc_len = k1 - k0;  // K-values of this split
   const int64_t kc_bytes = kc_len / 2, kc_blocks = kc_len / 32;
   const int KT = (int)((kc_len + 127) / 128);
   const int tail_kb = (int)(kc_blocks - (int64_t)(KT - 1) * 4);  // valid 32-blocks in the last step
-  C += split * sp.c_stride;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -539,7 +574,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
         if (mrow < rows_valid) {
           float* crow = C + (m0 + mrow) * ldc + n0;
           if (ncol + 3 < cols_valid) {
-            store_c4(crow + ncol, v, sp.stream_c != 0);
+            store_c4(crow + ncol, v, stream_c);
           } else {
             if (ncol + 0 < cols_valid) crow[ncol + 0] = v.x;
             if (ncol + 1 < cols_valid) crow[ncol + 1] = v.y;
@@ -556,7 +591,7 @@ template <int BM, int BN, int WM, int WN, int SC>
 static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                        const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha,
                        float* c, int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales,
-                       GemmSplit sp, hipStream_t st) {
+                       GemmSplit sp, const GemmPlain* p1, hipStream_t st) {
   GemmGroups gg;
   gg.ngroups = (int)groups;
   gg.tiles_n = (int)cdiv(N, BN);
@@ -567,21 +602,31 @@ static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
     gg.tile_start[g + 1] = gg.tile_start[g] + (int)(cdiv(rows, BM) * gg.tiles_n);
   }
   gg.row_off[groups] = offs[groups];
-  const int total = gg.tile_start[groups];
+  const int total = gg.tile_start[groups] * sp.n;
+  if constexpr (BM == 128) {  // paired launches take 128 x 128 tiles only
+    if (p1) {
+      GemmPlain q = *p1;
+      q.tiles = (int)(cdiv(q.M, BM) * cdiv(q.N, BN));
+      q.tiles_n = (int)cdiv(q.N, BN);
+      if (total + q.tiles == 0) return MX_OK;
+      k_gemm_mx<BM, BN, WM, WN, 4, SC, true><<<dim3(total + q.tiles), dim3(WM * WN * 64), 0, st>>>(
+          a, sa, b, sb, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, gg, sp, q);
+      return launch_status();
+    }
+  } else {
+    if (p1) return MX_ERR_SHAPE;
+  }
   if (total == 0) return MX_OK;
-  k_gemm_mx<BM, BN, WM, WN, 4, SC><<<dim3(total * sp.n), dim3(WM * WN * 64), 0, st>>>(
-      a, sa, b, sb, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, gg, sp);
+  k_gemm_mx<BM, BN, WM, WN, 4, SC, false><<<dim3(total), dim3(WM * WN * 64), 0, st>>>(
+      a, sa, b, sb, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, gg, sp, GemmPlain{});
   return launch_status();
 }
 
-// Large tiles when they still give every CU a few tiles, else smaller ones;
-// scale rows go by dword loads when every scale row starts 4-byte aligned.
-static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
-                       const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha,
-                       float* c, int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales,
-                       GemmSplit sp, hipStream_t st) {
-  int64_t tiles256 = 0;
-  for (int64_t g = 0; g < groups; ++g) tiles256 += cdiv(offs[g + 1] - offs[g], 256) * cdiv(N, 256);
+// Scale-load mode of one product: 16-byte groups of four steps, one dword per
+// step, two 2-byte loads or bytes, by what the scale rows' length and
+// alignment allow.
+static int scale_mode(const uint8_t* sa, const uint8_t* sb, int64_t K, int64_t b_stride_scales,
+                      const GemmSplit& sp) {
   const bool al4 = (reinterpret_cast<uintptr_t>(sa) & 3u) == 0 &&
                    (reinterpret_cast<uintptr_t>(sb) & 3u) == 0 && b_stride_scales % 4 == 0;
   const bool al16 = (reinterpret_cast<uintptr_t>(sa) & 15u) == 0 &&
@@ -596,13 +641,35 @@ static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
     k512 = k512 && sp.kbeg[s] % 512 == 0;
     k128 = k128 && sp.kbeg[s] % 128 == 0;
   }
-  const int sc = ((K / 32) % 16 == 0 && al16 && k512)
-                     ? kScGroup
-                     : (((K / 32) % 4 == 0 && al4 && k128)
-                            ? kScDword
-                            : (((K / 32) % 2 == 0 && al2 && k128) ? kScShort : kScByte));
-  const bool big = tiles256 * sp.n >= 512;
-#define MX_GEMM_ARGS a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, sp, st
+  if ((K / 32) % 16 == 0 && al16 && k512) return kScGroup;
+  if ((K / 32) % 4 == 0 && al4 && k128) return kScDword;
+  if ((K / 32) % 2 == 0 && al2 && k128) return kScShort;
+  return kScByte;
+}
+
+// The mode both products of a paired launch can use (the modes, weakest last:
+// group, dword, short, byte).
+static int common_scale_mode(int a, int b) {
+  auto rank = [](int m) { return m == kScGroup ? 0 : (m == kScDword ? 1 : (m == kScShort ? 2 : 3)); };
+  return rank(a) >= rank(b) ? a : b;
+}
+
+// Large tiles when they still give every CU a few tiles, else smaller ones;
+// a paired launch (p1) always takes 128 x 128 tiles.
+static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
+                       const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha,
+                       float* c, int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales,
+                       GemmSplit sp, hipStream_t st, const GemmPlain* p1 = nullptr) {
+  int64_t tiles256 = 0;
+  for (int64_t g = 0; g < groups; ++g) tiles256 += cdiv(offs[g + 1] - offs[g], 256) * cdiv(N, 256);
+  int sc = scale_mode(sa, sb, K, b_stride_scales, sp);
+  if (p1) {
+    GemmSplit one{};
+    one.n = 1;
+    sc = common_scale_mode(sc, scale_mode(p1->SA, p1->SB, p1->K, 0, one));
+  }
+  const bool big = !p1 && tiles256 * sp.n >= 512;
+#define MX_GEMM_ARGS a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, sp, p1, st
   if (big) {
     if (sc == kScGroup) return launch_gemm<256, 256, 2, 2, kScGroup>(MX_GEMM_ARGS);
     if (sc == kScDword) return launch_gemm<256, 256, 2, 2, kScDword>(MX_GEMM_ARGS);
@@ -681,6 +748,45 @@ int gemm_split_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const
   const int64_t n4 = M * (N / 4);
   k_splitk_sum<<<dim3((unsigned)hmin(cdiv(n4, 256), 4096)), dim3(256), 0, st>>>(
       reinterpret_cast<const float4*>(part), plan.n, M, N / 4, alpha, c, ldc);
+  return launch_status();
+}
+
+// Whether two products are small enough to share a launch: neither would take
+// 256 x 256 tiles, and the second needs no split.
+bool gemm_pairable(int64_t M0, int64_t N0, SplitPlan plan0, int64_t M1, int64_t N1,
+                   SplitPlan plan1) {
+  return plan1.n == 1 && cdiv(M0, 256) * cdiv(N0, 256) * plan0.n < 512 &&
+         cdiv(M1, 256) * cdiv(N1, 256) < 512;
+}
+
+// Two products in one launch: C0 [M0][N0] = alpha0 A0 . B0^T with plan0's
+// splits (partial sums in part0, added afterwards) and the plain C1 [M1][N1] =
+// alpha1 A1 . B1^T.  The first product's workgroups are dispatched first, so it
+// should be the one with the longer contraction per workgroup.
+int gemm_pair_impl(const uint8_t* a0, const uint8_t* sa0, const uint8_t* b0, const uint8_t* sb0,
+                   int64_t M0, int64_t N0, int64_t K0, float alpha0, float* c0, int64_t ldc0,
+                   SplitPlan plan0, float* part0, const uint8_t* a1, const uint8_t* sa1,
+                   const uint8_t* b1, const uint8_t* sb1, int64_t M1, int64_t N1, int64_t K1,
+                   float alpha1, float* c1, int64_t ldc1, hipStream_t st) {
+  const int64_t offs[2] = {0, M0};
+  const GemmPlain p1{a1, sa1, b1, sb1, M1, N1, K1, alpha1, c1, ldc1, 0, 0};
+  GemmSplit sp{};
+  if (plan0.n <= 1) {
+    sp.n = 1;
+    sp.stream_c = 1;
+    sp.kbeg[0] = 0;
+    sp.kbeg[1] = K0;
+    return gemm_launch(a0, sa0, b0, sb0, offs, 1, N0, K0, alpha0, c0, ldc0, 0, 0, sp, st, &p1);
+  }
+  sp.n = plan0.n;
+  sp.stream_c = 0;  // partial sums, read back by k_splitk_sum
+  sp.c_stride = M0 * N0;
+  for (int i = 0; i <= plan0.n; ++i) sp.kbeg[i] = hmin((int64_t)i * plan0.kchunk, K0);
+  int s = gemm_launch(a0, sa0, b0, sb0, offs, 1, N0, K0, 1.0f, part0, N0, 0, 0, sp, st, &p1);
+  if (s != MX_OK) return s;
+  const int64_t n4 = M0 * (N0 / 4);
+  k_splitk_sum<<<dim3((unsigned)hmin(cdiv(n4, 256), 4096)), dim3(256), 0, st>>>(
+      reinterpret_cast<const float4*>(part0), plan0.n, M0, N0 / 4, alpha0, c0, ldc0);
   return launch_status();
 }
 

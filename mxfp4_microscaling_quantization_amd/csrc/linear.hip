@@ -44,6 +44,13 @@ SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K);
 int gemm_split_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                     int64_t M, int64_t N, int64_t K, float alpha, float* c, int64_t ldc,
                     SplitPlan plan, float* part, hipStream_t st);
+bool gemm_pairable(int64_t M0, int64_t N0, SplitPlan plan0, int64_t M1, int64_t N1,
+                   SplitPlan plan1);
+int gemm_pair_impl(const uint8_t* a0, const uint8_t* sa0, const uint8_t* b0, const uint8_t* sb0,
+                   int64_t M0, int64_t N0, int64_t K0, float alpha0, float* c0, int64_t ldc0,
+                   SplitPlan plan0, float* part0, const uint8_t* a1, const uint8_t* sa1,
+                   const uint8_t* b1, const uint8_t* sb1, int64_t M1, int64_t N1, int64_t K1,
+                   float alpha1, float* c1, int64_t ldc1, hipStream_t st);
 int gemm_ranges_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                      int64_t M, int64_t N, int64_t K, const int64_t* kbeg, int n, float alpha,
                      float* c, hipStream_t st);
@@ -64,7 +71,8 @@ static size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Workspace layout: four packed operands, each codes then scales, then the
 // split-K partial sums of the dX / dW products when they are split (shared:
-// the two products run one after the other), all 256-byte aligned.
+// the two products run one after the other, and a launch that pairs them
+// splits only dW), all 256-byte aligned.
 struct BwdLayout {
   size_t q3c, q3s, q4c, q4s, q5c, q5s, q6c, q6s, part, total;
   SplitPlan dx, dw;
@@ -180,6 +188,11 @@ static int linear_bwd_impl(const void* dy, int dtype, int64_t M, int64_t N, int6
   if (s != MX_OK) return s;
   const float alpha = had ? kHadamardAlpha : 1.0f;
   float* part = reinterpret_cast<float*>(ws + L.part);
+  if (gemm_pairable(N, K, L.dw, M, K, L.dx)) {  // small products: dW and dX in one launch
+    return gemm_pair_impl(ws + L.q5c, ws + L.q5s, ws + L.q6c, ws + L.q6s, N, K, M, alpha, dw, K,
+                          L.dw, part, ws + L.q3c, ws + L.q3s, ws + L.q4c, ws + L.q4s, M, K, N,
+                          alpha, dx, K, st);
+  }
   s = gemm_split_impl(ws + L.q3c, ws + L.q3s, ws + L.q4c, ws + L.q4s, M, K, N, alpha, dx, K, L.dx,
                       part, st);
   if (s != MX_OK) return s;

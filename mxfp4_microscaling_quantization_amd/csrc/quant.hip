@@ -276,11 +276,12 @@ __global__ __launch_bounds__(256) void k_quant_tile(
   constexpr int NRB = kTileR / 32;                // row blocks per tile (4)
   constexpr int NLOAD = kTileR * CPR / 256;       // chunks per thread (8)
   __shared__ uint32_t s_in[kTileR * kTileRowBytes / 4];
-  __shared__ uint8_t s_scales[TC * NRB];
   // Once the column pass holds its values in registers the tile is no longer
-  // read; its first TC * NRB * 16 bytes then stage the column-block codes.
-  static_assert(TC * NRB * 16 <= kTileR * kTileRowBytes, "code staging fits the tile");
+  // read; its first TC * NRB * 16 bytes then stage the column-block codes and
+  // the next TC * NRB bytes their scales (32 KB of LDS in all).
+  static_assert(TC * NRB * 17 <= kTileR * kTileRowBytes, "code staging fits the tile");
   uint4* const s_codes = reinterpret_cast<uint4*>(s_in);
+  uint8_t* const s_scales = reinterpret_cast<uint8_t*>(s_in) + TC * NRB * 16;
 
   const int64_t col0 = (int64_t)blockIdx.x * TC;
   const TileRows tr = tile_rows(segs, kTileR, rows, (int)blockIdx.y);
