@@ -33,8 +33,8 @@ PEAK_FP4_TFLOPS = 10100.0
 # from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB copy, valid for
 # the GEMM source with this sha256 only (the per-launch table is kept with the
 # committed profiles).
-GEMM_TRAFFIC = {"sha256": "a2762481055143c1bc3cc025008b3327719f0dd23d1fe5f2b6c59e574a59e2ba",
-                "bytes_per_launch": 668290033}
+GEMM_TRAFFIC = {"sha256": "5e521747046f87694326f88321448fc2017985b09f467527643d53dab956666e",
+                "bytes_per_launch": 668333197}
 
 
 def gemm_traffic():
