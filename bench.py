@@ -92,6 +92,23 @@ def bf16_dev(torch, bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
 
+def linear_attainable_ms(M, N, K):
+    """Attainable time of one linear fwd+bwd with bf16 inputs: the sum over its
+    six kernels of max(flops / FP4 peak, algorithmic bytes / HBM peak)."""
+    fl = 2.0 * M * N * K
+    pk = 0.53125  # packed bytes per element (codes + scales)
+    kernels = [  # (flops, algorithmic bytes)
+        (0, (M + N) * K * (2 + pk)),                       # quantize X and W
+        (fl, (M + N) * K * pk + 4 * M * N),                 # Y = Q(X) Q(W)^T
+        (0, M * N * (2 + 2 * pk)),                          # dual quantize dY
+        (0, (N + M) * K * 2 * pk),                          # double quantize W and X
+        (fl, (M + K) * N * pk + 4 * M * K),                 # dX = Q3 [M,N] . Q4 [K,N]^T
+        (fl, (N + K) * M * pk + 4 * N * K),                 # dW = Q5 [N,M] . Q6 [K,M]^T
+    ]
+    return sum(max(a / (PEAK_FP4_TFLOPS * 1e12), c / (PEAK_HBM_GBPS * 1e9))
+               for a, c in kernels) * 1e3
+
+
 # ---------------------------------------------------------------- linear fwd + bwd (the step)
 def bench_linear(torch, mx, synth, dev, steps, warmup, seed=3):
     cfg = synth.llama_config()
@@ -165,7 +182,9 @@ def bench_linear(torch, mx, synth, dev, steps, warmup, seed=3):
                  "frac_hbm": bytes_q[k] / (kern[k] * 1e-3) / 1e9 / PEAK_HBM_GBPS} for k in bytes_q}
     return {
         "M": M, "N": N, "K": K, "ms_per_step": ms_step, "wall_s": wall,
-        "tflops": flops / (ms_step * 1e-3) / 1e12, "gemm_ms": gemm_ms, "gemm_tflops": gemm_tf,
+        "tflops": flops / (ms_step * 1e-3) / 1e12, "attainable_ms": linear_attainable_ms(M, N, K),
+        "frac_attainable": linear_attainable_ms(M, N, K) / ms_step,
+        "gemm_ms": gemm_ms, "gemm_tflops": gemm_tf,
         "gemm_launches": T.count("gemm"), "kernels_us": {k: v * 1e3 for k, v in kern.items()},
         "quantizers": quant, "matches_linear_entry_points": bool(same),
     }
@@ -267,17 +286,7 @@ def bench_linear_deit(torch, mx, synth, dev, steps=50, seed=1):
     graph = a.elapsed_time(b) / steps
     del g
     fl = 2.0 * M * N * K
-    pk = 0.53125  # packed bytes per element (codes + scales)
-    kernels = [  # (flops, algorithmic bytes)
-        (0, (M + N) * K * (2 + pk)),                       # quantize X and W
-        (fl, (M + N) * K * pk + 4 * M * N),                 # Y
-        (0, M * N * (2 + 2 * pk)),                          # dual quantize dY
-        (0, (N + M) * K * 2 * pk),                          # double quantize W and X
-        (fl, (M + N) * N * pk + 4 * M * K),                 # dX
-        (fl, (N + K) * M * pk + 4 * N * K),                 # dW
-    ]
-    ideal_ms = sum(max(a / (PEAK_FP4_TFLOPS * 1e12), c / (PEAK_HBM_GBPS * 1e9))
-                   for a, c in kernels) * 1e3
+    ideal_ms = linear_attainable_ms(M, N, K)
     return {"M": M, "N": N, "K": K, "eager_ms": eager, "graph_ms": graph,
             "graph_replays_equal_eager": bool(replays_equal),
             "TFLOPs_graph": 3 * fl / (graph * 1e-3) / 1e12,
@@ -508,6 +517,8 @@ def main():
         return
     parts["linear_kernels"] = {"kernels_us": lin["kernels_us"], "quantizers": lin["quantizers"],
                                "gemm_launches_timed": lin["gemm_launches"],
+                               "step_attainable_ms": lin["attainable_ms"],
+                               "step_frac_attainable": lin["frac_attainable"],
                                "matches_linear_entry_points": lin["matches_linear_entry_points"]}
     ach = lin["gemm_tflops"]
     line = {

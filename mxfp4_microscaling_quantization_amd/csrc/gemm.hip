@@ -592,6 +592,13 @@ static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
                        const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha,
                        float* c, int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales,
                        GemmSplit sp, const GemmPlain* p1, hipStream_t st) {
+  // a dispatch holds at most 2^32 - 1 work-items (and the kernel counts tiles
+  // in int): a larger launch is rejected
+  constexpr int64_t kMaxWg = 0xFFFFFFFFll / (WM * WN * 64);
+  int64_t t64 = 0;
+  for (int64_t g = 0; g < groups; ++g) t64 += cdiv(offs[g + 1] - offs[g], BM) * cdiv(N, BN);
+  const int64_t p1_tiles = p1 ? cdiv(p1->M, BM) * cdiv(p1->N, BN) : 0;
+  if (t64 * sp.n + p1_tiles > kMaxWg) return MX_ERR_SHAPE;
   GemmGroups gg;
   gg.ngroups = (int)groups;
   gg.tiles_n = (int)cdiv(N, BN);
@@ -606,7 +613,7 @@ static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
   if constexpr (BM == 128) {  // paired launches take 128 x 128 tiles only
     if (p1) {
       GemmPlain q = *p1;
-      q.tiles = (int)(cdiv(q.M, BM) * cdiv(q.N, BN));
+      q.tiles = (int)p1_tiles;
       q.tiles_n = (int)cdiv(q.N, BN);
       if (total + q.tiles == 0) return MX_OK;
       k_gemm_mx<BM, BN, WM, WN, 4, SC, true><<<dim3(total + q.tiles), dim3(WM * WN * 64), 0, st>>>(
