@@ -76,6 +76,27 @@ def test_linear_bwd_split_contraction_with_ragged_last_chunk():
     check_linear(cfg, "bf16", seed=5)
 
 
+@pytest.mark.parametrize("M,N,K", [(544, 320, 224), (96, 160, 4096)])
+def test_linear_bwd_paired_products_equal_separate_launches(M, N, K):
+    """A small layer's backward runs dW and dX in one launch; each product must equal, bit
+    for bit, the same product launched alone through mx_gemm on the operands the public
+    quantizers make (no split-K here: the contraction of dW, M, is below 2048)."""
+    rng = np.random.default_rng(M + N + K)
+    b16 = synth.f32_to_bf16_bits
+    x = upload(b16(rng.standard_normal((M, K)).astype(np.float32)), "bf16")
+    w = upload(b16((rng.standard_normal((N, K)) * 0.02).astype(np.float32)), "bf16")
+    dy = upload(b16((rng.standard_normal((M, N)) * 1e-3).astype(np.float32)), "bf16")
+    seed = 17
+    _, xq, wq = mx.linear_fwd(x, w)
+    gx, gw = mx.linear_bwd(dy, xq, wq, M, N, K, seed)
+    q3 = mx.quantize(dy, mx.MX_ROW, mx.MX_SR, seed + 3)
+    q5 = mx.quantize(dy, mx.MX_COL, mx.MX_SR, seed + 5)
+    q4 = mx.requantize(*wq, N, K, mx.MX_SR, seed + 4)
+    q6 = mx.requantize(*xq, M, K, mx.MX_SR, seed + 6)
+    assert torch.equal(gx, mx.gemm(q3, q4, M, K, N))
+    assert torch.equal(gw, mx.gemm(q5, q6, N, K, M))
+
+
 def test_linear_deit_fc1_full():
     """DeiT-S fc1, X [12608, 384], W [1536, 384], dY [12608, 1536] bf16: every output checked."""
     check_linear(synth.deit_config(), "bf16", seed=1)
