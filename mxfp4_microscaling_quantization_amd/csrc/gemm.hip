@@ -197,13 +197,19 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
   constexpr int LC = LA + LB + (SC == kScGroup ? 0 : QW);  // per-step vector-memory instructions
   static_assert(LA * NW * 16 == BM && LB * NW * 16 == BN, "tile/wave mismatch");
   static_assert(QW * NW == QJ && BM % 64 == 0 && BN % 64 == 0, "scale jobs");
-  static_assert(STAGES == 4 && 2 * LC + QW < 64, "pipeline depth");
+  // STAGES 4: the pipelined ring.  STAGES 3: a short contraction (at most three
+  // K-steps, guaranteed by the host), whose loads are all issued up front: the
+  // fourth stage is never used, and the smaller ring lets one more workgroup
+  // share a CU.
+  static_assert((STAGES == 4 || (STAGES == 3 && SC != kScGroup)) && 2 * LC + QW < 64,
+                "pipeline depth");
 
   // The LDS ring (contiguous, reused by the epilogue); every access uses a
-  // compile-time stage index.
+  // compile-time stage index (with three stages, index 3 is on paths a short
+  // contraction never takes).
   __shared__ StageLds<BM, BN, SC> ring[STAGES];
   __shared__ ScaleGroupLds<(SC == kScGroup ? BM : 1), (SC == kScGroup ? BN : 1)> sg[2];
-  auto stage = [&](auto S) -> StageLds<BM, BN, SC>& { return ring[decltype(S)::value]; };
+  auto stage = [&](auto S) -> StageLds<BM, BN, SC>& { return ring[decltype(S)::value % STAGES]; };
   auto bufA = [&](auto S) -> TileLds<BM, SC>& { return stage(S).a; };
   auto bufB = [&](auto S) -> TileLds<BN, SC>& { return stage(S).b; };
 
@@ -535,24 +541,27 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
 
   // ---- epilogue: lane holds D[n = 8 g + 4 lh + v][m = lr], g, v = 0..3, of each 32x32 tile
   // The LDS ring is idle now: each wave stages its sub-tile there, 64 rows per
-  // pass (row pitch CH 16-byte chunks, chunk index XORed with row & 15, so the
-  // 16-row writes and the row reads are free of bank conflicts), and reads it
-  // back so that every store instruction writes whole row segments of C
-  // (two rows of 512 bytes for 256 x 256 tiles, four of 256 for 128 x 128)
-  // instead of 32-byte pieces of 32 rows.
+  // pass (32 when the ring is too small for that; row pitch CH 16-byte chunks,
+  // chunk index XORed with row & 15, so the 16-row writes and the row reads
+  // are free of bank conflicts), and reads it back so that every store
+  // instruction writes whole row segments of C (two rows of 512 bytes for
+  // 256 x 256 tiles, four of 256 for 128 x 128) instead of 32-byte pieces of
+  // 32 rows.
   {
     constexpr int CH = TN * 8;      // 16-byte chunks per staged row
     constexpr int RB = CH * 16;     // bytes per staged row
     constexpr int RPI = 64 / CH;    // rows per read (one chunk per lane)
-    static_assert(TM % 2 == 0 && CH >= 16 && 64 % CH == 0, "staging shape");
-    static_assert(sizeof(ring) >= NW * 64 * RB, "staging space");
+    constexpr int PR = sizeof(ring) >= NW * 64 * RB ? 64 : 32;  // rows per pass
+    constexpr int PB = PR / 32;     // 32-row MFMA tiles per pass
+    static_assert(TM % PB == 0 && CH >= 16 && 64 % CH == 0, "staging shape");
+    static_assert(sizeof(ring) >= NW * PR * RB, "staging space");
     __syncthreads();  // every wave is done reading the ring
-    char* stg = reinterpret_cast<char*>(ring) + wave * 64 * RB;
+    char* stg = reinterpret_cast<char*>(ring) + wave * PR * RB;
 #pragma unroll
-    for (int p = 0; p < TM / 2; ++p) {
+    for (int p = 0; p < TM / PB; ++p) {
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb) {
-        const int b = 2 * p + bb;
+      for (int bb = 0; bb < PB; ++bb) {
+        const int b = PB * p + bb;
         const int rl = bb * 32 + lr;
 #pragma unroll
         for (int a = 0; a < TN; ++a)
@@ -565,11 +574,11 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
           }
       }
 #pragma unroll 4
-      for (int it = 0; it < 64 / RPI; ++it) {
+      for (int it = 0; it < PR / RPI; ++it) {
         const int rl = it * RPI + lane / CH, ch = lane % CH;
         const float4 v =
             *reinterpret_cast<const float4*>(stg + rl * RB + ((ch ^ (rl & 15)) * 16));
-        const int mrow = wm_off + p * 64 + rl;
+        const int mrow = wm_off + p * PR + rl;
         const int ncol = wn_off + ch * 4;
         if (mrow < rows_valid) {
           float* crow = C + (m0 + mrow) * ldc + n0;
@@ -587,7 +596,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
 }
 
 // ---------------------------------------------------------------- host side
-template <int BM, int BN, int WM, int WN, int SC>
+template <int BM, int BN, int WM, int WN, int SC, int STAGES = 4>
 static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                        const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha,
                        float* c, int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales,
@@ -624,7 +633,7 @@ static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
     if (p1) return MX_ERR_SHAPE;
   }
   if (total == 0) return MX_OK;
-  k_gemm_mx<BM, BN, WM, WN, 4, SC, false><<<dim3(total), dim3(WM * WN * 64), 0, st>>>(
+  k_gemm_mx<BM, BN, WM, WN, STAGES, SC, false><<<dim3(total), dim3(WM * WN * 64), 0, st>>>(
       a, sa, b, sb, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, gg, sp, GemmPlain{});
   return launch_status();
 }
@@ -682,6 +691,15 @@ static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
     if (sc == kScDword) return launch_gemm<256, 256, 2, 2, kScDword>(MX_GEMM_ARGS);
     if (sc == kScShort) return launch_gemm<256, 256, 2, 2, kScShort>(MX_GEMM_ARGS);
     return launch_gemm<256, 256, 2, 2, kScByte>(MX_GEMM_ARGS);
+  }
+  // at most three K-steps in every range: the short-contraction variant (three
+  // stages, three workgroups per CU); group-mode scales need K % 512 == 0
+  int64_t klen = 0;
+  for (int s = 0; s < sp.n; ++s) klen = klen > sp.kbeg[s + 1] - sp.kbeg[s] ? klen : sp.kbeg[s + 1] - sp.kbeg[s];
+  if (!p1 && klen <= 3 * 128 && sc != kScGroup) {
+    if (sc == kScDword) return launch_gemm<128, 128, 2, 2, kScDword, 3>(MX_GEMM_ARGS);
+    if (sc == kScShort) return launch_gemm<128, 128, 2, 2, kScShort, 3>(MX_GEMM_ARGS);
+    return launch_gemm<128, 128, 2, 2, kScByte, 3>(MX_GEMM_ARGS);
   }
   if (sc == kScGroup) return launch_gemm<128, 128, 2, 2, kScGroup>(MX_GEMM_ARGS);
   if (sc == kScDword) return launch_gemm<128, 128, 2, 2, kScDword>(MX_GEMM_ARGS);
