@@ -33,8 +33,8 @@ PEAK_FP4_TFLOPS = 10100.0
 # from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB copy, valid for
 # the GEMM source with this sha256 only (the per-launch table is kept with the
 # committed profiles).
-GEMM_TRAFFIC = {"sha256": "5e521747046f87694326f88321448fc2017985b09f467527643d53dab956666e",
-                "bytes_per_launch": 668333197}
+GEMM_TRAFFIC = {"sha256": "0863dc9281efa31db9c15fce171c6aeaa5750d88ffa90d2033b82e24a72d9250",
+                "bytes_per_launch": 668299899}
 
 
 def gemm_traffic():
