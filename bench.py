@@ -31,21 +31,35 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_FP4_TFLOPS = 10100.0
 # HBM bytes per GEMM launch (mean of the fwd, dX and dW launches of the step),
 # from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB copy, valid for
-# the GEMM source with this sha256 only (the per-launch table is kept with the
-# committed profiles).
-GEMM_TRAFFIC = {"sha256": "0863dc9281efa31db9c15fce171c6aeaa5750d88ffa90d2033b82e24a72d9250",
+# the GEMM code with this sha256 only (of the source with comments and blank
+# lines removed; the per-launch table is kept with the committed profiles).
+GEMM_TRAFFIC = {"sha256": "b4535da460a8dd352238eb7d4af887af4a413863b08cece3850fbb8bc0b04171",
                 "bytes_per_launch": 668299899}
 
 
-def gemm_traffic():
+def gemm_code_sha256(path):
+    """sha256 of a C++ source with // comments and blank lines removed, so that
+    only code changes (not documentation edits) change it."""
     import hashlib
+    import re
+    lines = []
+    for line in open(path, encoding="utf-8").read().splitlines():
+        line = re.sub(r"//.*$", "", line).rstrip()
+        if line.strip():
+            lines.append(line)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
+def gemm_traffic():
     src = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                        "mxfp4_microscaling_quantization_amd", "csrc", "gemm.hip")
     try:
-        h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        h = gemm_code_sha256(src)
     except OSError:
         return None
     return GEMM_TRAFFIC["bytes_per_launch"] if h == GEMM_TRAFFIC["sha256"] else None
+
+
 METRIC = "MXFP4 quantize GB/s + MXFP4 linear fwd+bwd TFLOP/s (%roofline), 1 MI355X"
 
 

@@ -14,15 +14,18 @@
 // op_sel picks the byte).
 //
 // The instruction is fed B as its first operand and A as its second, so it
-// produces D[n][m]: a lane then holds 4 consecutive n of one output row m and
-// writes them with one 16-byte store.
+// produces D[n][m]: a lane then holds 4 consecutive n of one output row m (one
+// 16-byte piece); the epilogue stages the tile through LDS so that each store
+// instruction writes whole row segments of C.
 //
 // Tiling: a workgroup of WM x WN waves owns a BM x BN tile of C (256 x 256 for
-// large problems: 128 x 128 per wave, 16 accumulator tiles) and walks K in
-// steps of 128 (64 code bytes per row) through a 4-stage LDS ring.  Direct
-// global-to-LDS loads fill a stage three steps ahead; each step reads the
-// second K-half's fragments while the first half's MFMAs run, and the next
-// step's first half while the second half's run, with one barrier per step.
+// large problems: 128 x 128 per wave, 16 accumulator tiles; 128 x 128 for small
+// ones) and walks K in steps of 128 (64 code bytes per row) through a 4-stage
+// LDS ring.  Direct global-to-LDS loads fill a stage three steps ahead; each
+// step reads the second K-half's fragments while the first half's MFMAs run,
+// and the next step's first half while the second half's run, with one
+// barrier per step.  A contraction of at most three steps takes a 3-stage ring
+// (three workgroups per CU); two small products can share one launch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
