@@ -13,8 +13,10 @@ a time so that every kernel is bracketed by events on the stream it runs on.
 value = 6 M N K / step time (TFLOP/s).  The line also carries the dominant
 kernel's roofline (the GEMM, vs the dense FP4 MFMA peak), the oracle's CPU
 throughput on a bounded sample, and the other rows of the path measured on
-their own workloads (quantizer sweep on 8192^2 bf16, MoE grouped GEMM and the
-de-oscillation step on the 32-expert master weights).
+their own workloads: the DeiT-S fc1 layer (12608 x 384 -> 1536) through
+mx_linear_fwd / mx_linear_bwd, eager and as a replayed HIP graph; the rotated
+layer; the quantizer sweep on 8192^2 bf16; the MoE grouped GEMM and backward
+and the de-oscillation and Q-EMA passes on the 32-expert master weights.
 """
 from __future__ import annotations
 
