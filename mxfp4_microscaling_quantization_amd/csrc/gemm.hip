@@ -44,6 +44,7 @@ constexpr int kFmtFp4 = 4;  // cbsz / blgp operand format: FP4 E2M1
 struct GemmGroups {
   int ngroups;
   int tiles_n;                              // tiles along N (same for every group)
+  int64_t lds_a, lds_b;                     // bytes between scale rows of A and of B
   int tile_start[MX_MAX_GROUPS + 1];        // prefix sum of tiles per group
   int64_t row_off[MX_MAX_GROUPS + 1];       // rows of A / C per group
 };
@@ -73,6 +74,7 @@ struct GemmPlain {
   float alpha;
   float* C;
   int64_t ldc;
+  int64_t lds_a, lds_b;  // bytes between scale rows of A and of B
   int tiles, tiles_n;
 };
 
@@ -267,7 +269,8 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
   const int cols_valid = (int)min<int64_t>(BN, N - n0);
 
   const int64_t ldk = K / 2;   // code bytes per row
-  const int64_t lds = K / 32;  // scale bytes (32-blocks) per row
+  const int64_t lds_a = second ? p1.lds_a : gg.lds_a;  // bytes between scale rows
+  const int64_t lds_b = second ? p1.lds_b : gg.lds_b;
   const int64_t kc_len = k1 - k0;  // K-values of this split
   const int64_t kc_bytes = kc_len / 2, kc_blocks = kc_len / 32;
   const int KT = (int)((kc_len + 127) / 128);
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
     const bool isA = grp < BM / 64;
     const int r0 = (isA ? grp : grp - BM / 64) * 64;
     const int64_t row = isA ? lmin(m0 + r0 + lane, a_last) : lmin(n0 + r0 + lane, N - 1);
-    s_src[j] = (isA ? SA : SBg) + row * lds + k0 / 32 + kb;
+    s_src[j] = (isA ? SA : SBg) + row * (isA ? lds_a : lds_b) + k0 / 32 + kb;
     s_dst[j] = ((SC == kScByte || SC == kScShort) ? part * (isA ? BM : BN) + r0 : r0) +
                (isA ? 0 : (1 << 20));
   }
@@ -603,7 +606,8 @@ template <int BM, int BN, int WM, int WN, int SC, int STAGES = 4>
 static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                        const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha,
                        float* c, int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales,
-                       GemmSplit sp, const GemmPlain* p1, hipStream_t st) {
+                       int64_t lds_a, int64_t lds_b, GemmSplit sp, const GemmPlain* p1,
+                       hipStream_t st) {
   // a dispatch holds at most 2^32 - 1 work-items (and the kernel counts tiles
   // in int): a larger launch is rejected
   constexpr int64_t kMaxWg = 0xFFFFFFFFll / (WM * WN * 64);
@@ -614,6 +618,8 @@ static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
   GemmGroups gg;
   gg.ngroups = (int)groups;
   gg.tiles_n = (int)cdiv(N, BN);
+  gg.lds_a = lds_a;
+  gg.lds_b = lds_b;
   gg.tile_start[0] = 0;
   for (int64_t g = 0; g < groups; ++g) {
     gg.row_off[g] = offs[g];
@@ -642,16 +648,17 @@ static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
 }
 
 // Scale-load mode of one product: 16-byte groups of four steps, one dword per
-// step, two 2-byte loads or bytes, by what the scale rows' length and
-// alignment allow.
-static int scale_mode(const uint8_t* sa, const uint8_t* sb, int64_t K, int64_t b_stride_scales,
-                      const GemmSplit& sp) {
-  const bool al4 = (reinterpret_cast<uintptr_t>(sa) & 3u) == 0 &&
-                   (reinterpret_cast<uintptr_t>(sb) & 3u) == 0 && b_stride_scales % 4 == 0;
-  const bool al16 = (reinterpret_cast<uintptr_t>(sa) & 15u) == 0 &&
-                    (reinterpret_cast<uintptr_t>(sb) & 15u) == 0 && b_stride_scales % 16 == 0;
-  const bool al2 = (reinterpret_cast<uintptr_t>(sa) & 1u) == 0 &&
-                   (reinterpret_cast<uintptr_t>(sb) & 1u) == 0 && b_stride_scales % 2 == 0;
+// step, two 2-byte loads or bytes, by what the scale rows' pitch (lds_a,
+// lds_b: at least K / 32, padding past K / 32 is never used) and alignment
+// allow.  A group of four steps may run past K / 32 into a row's padding but
+// not past its pitch, since the pitch is then a multiple of 16.
+static int scale_mode(const uint8_t* sa, const uint8_t* sb, int64_t lds_a, int64_t lds_b,
+                      int64_t b_stride_scales, const GemmSplit& sp) {
+  auto al = [&](uintptr_t m) {
+    return (reinterpret_cast<uintptr_t>(sa) & (m - 1)) == 0 &&
+           (reinterpret_cast<uintptr_t>(sb) & (m - 1)) == 0 && b_stride_scales % (int64_t)m == 0 &&
+           lds_a % (int64_t)m == 0 && lds_b % (int64_t)m == 0;
+  };
   // scale rows of every split must start aligned as well (group mode reads 16
   // bytes of four steps, dword mode 4 bytes of one; every split starts at a
   // multiple of 128 K-values, i.e. 4 scale bytes)
@@ -660,9 +667,9 @@ static int scale_mode(const uint8_t* sa, const uint8_t* sb, int64_t K, int64_t b
     k512 = k512 && sp.kbeg[s] % 512 == 0;
     k128 = k128 && sp.kbeg[s] % 128 == 0;
   }
-  if ((K / 32) % 16 == 0 && al16 && k512) return kScGroup;
-  if ((K / 32) % 4 == 0 && al4 && k128) return kScDword;
-  if ((K / 32) % 2 == 0 && al2 && k128) return kScShort;
+  if (al(16) && k512) return kScGroup;
+  if (al(4) && k128) return kScDword;
+  if (al(2) && k128) return kScShort;
   return kScByte;
 }
 
@@ -678,17 +685,18 @@ static int common_scale_mode(int a, int b) {
 static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                        const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha,
                        float* c, int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales,
-                       GemmSplit sp, hipStream_t st, const GemmPlain* p1 = nullptr) {
+                       int64_t lds_a, int64_t lds_b, GemmSplit sp, hipStream_t st,
+                       const GemmPlain* p1 = nullptr) {
   int64_t tiles256 = 0;
   for (int64_t g = 0; g < groups; ++g) tiles256 += cdiv(offs[g + 1] - offs[g], 256) * cdiv(N, 256);
-  int sc = scale_mode(sa, sb, K, b_stride_scales, sp);
+  int sc = scale_mode(sa, sb, lds_a, lds_b, b_stride_scales, sp);
   if (p1) {
     GemmSplit one{};
     one.n = 1;
-    sc = common_scale_mode(sc, scale_mode(p1->SA, p1->SB, p1->K, 0, one));
+    sc = common_scale_mode(sc, scale_mode(p1->SA, p1->SB, p1->lds_a, p1->lds_b, 0, one));
   }
   const bool big = !p1 && tiles256 * sp.n >= 512;
-#define MX_GEMM_ARGS a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, sp, p1, st
+#define MX_GEMM_ARGS a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, lds_a, lds_b, sp, p1, st
   if (big) {
     if (sc == kScGroup) return launch_gemm<256, 256, 2, 2, kScGroup>(MX_GEMM_ARGS);
     if (sc == kScDword) return launch_gemm<256, 256, 2, 2, kScDword>(MX_GEMM_ARGS);
@@ -711,16 +719,19 @@ static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
 #undef MX_GEMM_ARGS
 }
 
+// lds_a, lds_b: bytes between the scale rows of A and of B (K / 32 when
+// packed; the backward layers pad their own operands' rows to 16 bytes).
 int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
               const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha, float* c,
-              int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, hipStream_t st) {
+              int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, int64_t lds_a,
+              int64_t lds_b, hipStream_t st) {
   GemmSplit one{};
   one.n = 1;
   one.stream_c = 1;
   one.kbeg[0] = 0;
   one.kbeg[1] = K;
   return gemm_launch(a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes,
-                     b_stride_scales, one, st);
+                     b_stride_scales, lds_a, lds_b, one, st);
 }
 
 // ---------------------------------------------------------------- split-K
@@ -763,15 +774,16 @@ __global__ __launch_bounds__(256) void k_splitk_sum(const float4* __restrict__ p
 // floats of workspace (16-byte aligned); N % 4 == 0.
 int gemm_split_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                     int64_t M, int64_t N, int64_t K, float alpha, float* c, int64_t ldc,
-                    SplitPlan plan, float* part, hipStream_t st) {
+                    SplitPlan plan, float* part, int64_t lds_a, int64_t lds_b, hipStream_t st) {
   const int64_t offs[2] = {0, M};
-  if (plan.n <= 1) return gemm_impl(a, sa, b, sb, offs, 1, N, K, alpha, c, ldc, 0, 0, st);
+  if (plan.n <= 1)
+    return gemm_impl(a, sa, b, sb, offs, 1, N, K, alpha, c, ldc, 0, 0, lds_a, lds_b, st);
   GemmSplit sp{};
   sp.n = plan.n;
   sp.stream_c = 0;  // partial sums, read back by k_splitk_sum
   sp.c_stride = M * N;
   for (int i = 0; i <= plan.n; ++i) sp.kbeg[i] = hmin((int64_t)i * plan.kchunk, K);
-  int s = gemm_launch(a, sa, b, sb, offs, 1, N, K, 1.0f, part, N, 0, 0, sp, st);
+  int s = gemm_launch(a, sa, b, sb, offs, 1, N, K, 1.0f, part, N, 0, 0, lds_a, lds_b, sp, st);
   if (s != MX_OK) return s;
   const int64_t n4 = M * (N / 4);
   k_splitk_sum<<<dim3((unsigned)hmin(cdiv(n4, 256), 4096)), dim3(256), 0, st>>>(
@@ -793,24 +805,27 @@ bool gemm_pairable(int64_t M0, int64_t N0, SplitPlan plan0, int64_t M1, int64_t 
 // should be the one with the longer contraction per workgroup.
 int gemm_pair_impl(const uint8_t* a0, const uint8_t* sa0, const uint8_t* b0, const uint8_t* sb0,
                    int64_t M0, int64_t N0, int64_t K0, float alpha0, float* c0, int64_t ldc0,
-                   SplitPlan plan0, float* part0, const uint8_t* a1, const uint8_t* sa1,
-                   const uint8_t* b1, const uint8_t* sb1, int64_t M1, int64_t N1, int64_t K1,
-                   float alpha1, float* c1, int64_t ldc1, hipStream_t st) {
+                   SplitPlan plan0, float* part0, int64_t lds_a0, int64_t lds_b0,
+                   const uint8_t* a1, const uint8_t* sa1, const uint8_t* b1, const uint8_t* sb1,
+                   int64_t M1, int64_t N1, int64_t K1, float alpha1, float* c1, int64_t ldc1,
+                   int64_t lds_a1, int64_t lds_b1, hipStream_t st) {
   const int64_t offs[2] = {0, M0};
-  const GemmPlain p1{a1, sa1, b1, sb1, M1, N1, K1, alpha1, c1, ldc1, 0, 0};
+  const GemmPlain p1{a1, sa1, b1, sb1, M1, N1, K1, alpha1, c1, ldc1, lds_a1, lds_b1, 0, 0};
   GemmSplit sp{};
   if (plan0.n <= 1) {
     sp.n = 1;
     sp.stream_c = 1;
     sp.kbeg[0] = 0;
     sp.kbeg[1] = K0;
-    return gemm_launch(a0, sa0, b0, sb0, offs, 1, N0, K0, alpha0, c0, ldc0, 0, 0, sp, st, &p1);
+    return gemm_launch(a0, sa0, b0, sb0, offs, 1, N0, K0, alpha0, c0, ldc0, 0, 0, lds_a0, lds_b0,
+                       sp, st, &p1);
   }
   sp.n = plan0.n;
   sp.stream_c = 0;  // partial sums, read back by k_splitk_sum
   sp.c_stride = M0 * N0;
   for (int i = 0; i <= plan0.n; ++i) sp.kbeg[i] = hmin((int64_t)i * plan0.kchunk, K0);
-  int s = gemm_launch(a0, sa0, b0, sb0, offs, 1, N0, K0, 1.0f, part0, N0, 0, 0, sp, st, &p1);
+  int s = gemm_launch(a0, sa0, b0, sb0, offs, 1, N0, K0, 1.0f, part0, N0, 0, 0, lds_a0, lds_b0,
+                      sp, st, &p1);
   if (s != MX_OK) return s;
   const int64_t n4 = M0 * (N0 / 4);
   k_splitk_sum<<<dim3((unsigned)hmin(cdiv(n4, 256), 4096)), dim3(256), 0, st>>>(
@@ -823,14 +838,14 @@ int gemm_pair_impl(const uint8_t* a0, const uint8_t* sa0, const uint8_t* b0, con
 // a multiple of 128; an empty range writes zeros).
 int gemm_ranges_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                      int64_t M, int64_t N, int64_t K, const int64_t* kbeg, int n, float alpha,
-                     float* c, hipStream_t st) {
+                     float* c, int64_t lds_a, int64_t lds_b, hipStream_t st) {
   GemmSplit sp{};
   sp.n = n;
   sp.stream_c = 1;
   sp.c_stride = M * N;
   for (int i = 0; i <= n; ++i) sp.kbeg[i] = kbeg[i];
   const int64_t offs[2] = {0, M};
-  return gemm_launch(a, sa, b, sb, offs, 1, N, K, alpha, c, N, 0, 0, sp, st);
+  return gemm_launch(a, sa, b, sb, offs, 1, N, K, alpha, c, N, 0, 0, lds_a, lds_b, sp, st);
 }
 
 }  // namespace mx
@@ -850,7 +865,7 @@ extern "C" int mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const ui
   if (K > 0) MX_REQUIRE(aligned16(a_codes) && aligned16(b_codes), MX_ERR_ALIGN);
   const int64_t offs[2] = {0, M};
   return gemm_impl(a_codes, a_scales, b_codes, b_scales, offs, 1, N, K, alpha, c, ldc, 0, 0,
-                   as_stream(stream));
+                   K / 32, K / 32, as_stream(stream));
 }
 
 extern "C" int mx_gemm_grouped(const uint8_t* a_codes, const uint8_t* a_scales,
@@ -870,5 +885,5 @@ extern "C" int mx_gemm_grouped(const uint8_t* a_codes, const uint8_t* a_scales,
   MX_REQUIRE(aligned16(c), MX_ERR_ALIGN);
   if (K > 0) MX_REQUIRE(aligned16(a_codes) && aligned16(b_codes), MX_ERR_ALIGN);
   return gemm_impl(a_codes, a_scales, b_codes, b_scales, offs, groups, N, K, alpha, c, N,
-                   N * K / 2, N * K / 32, as_stream(stream));
+                   N * K / 2, N * K / 32, K / 32, K / 32, as_stream(stream));
 }

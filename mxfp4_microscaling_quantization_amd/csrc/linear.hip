@@ -22,7 +22,7 @@ int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, int axis
 int quantize_dual_impl(const void* x, int dtype, int64_t rows, int64_t cols, int round,
                        uint64_t seed_row, uint64_t seed_col, int had, uint32_t mask,
                        uint8_t* codes_row, uint8_t* scales_row, uint8_t* codes_col,
-                       uint8_t* scales_col, hipStream_t st);
+                       uint8_t* scales_col, hipStream_t st, int64_t sp_row, int64_t sp_col);
 int quantize_rows2_impl(const void* x0, int64_t rows0, int64_t cols0, uint8_t* codes0,
                         uint8_t* scales0, uint64_t seed0, const void* x1, int64_t rows1,
                         int64_t cols1, uint8_t* codes1, uint8_t* scales1, uint64_t seed1,
@@ -31,7 +31,7 @@ int requantize_pair_impl(const uint8_t* codes_in0, const uint8_t* scales_in0, in
                          const uint8_t* codes_in1, const uint8_t* scales_in1, int64_t rows1,
                          int64_t cols, int round, uint64_t seed0, uint64_t seed1,
                          uint8_t* codes0, uint8_t* scales0, uint8_t* codes1, uint8_t* scales1,
-                         hipStream_t st);
+                         hipStream_t st, int64_t s_pitch0, int64_t s_pitch1);
 int requantize_rht_pair_impl(const uint8_t* codes_in0, const uint8_t* scales_in0, int64_t rows0,
                              const uint8_t* codes_in1, const uint8_t* scales_in1, int64_t rows1,
                              int64_t cols, int round, uint64_t seed0, uint64_t seed1,
@@ -39,42 +39,52 @@ int requantize_rht_pair_impl(const uint8_t* codes_in0, const uint8_t* scales_in0
                              uint8_t* scales1, hipStream_t st);
 int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
               const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha, float* c,
-              int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, hipStream_t st);
+              int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, int64_t lds_a,
+              int64_t lds_b, hipStream_t st);
 SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K);
 int gemm_split_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                     int64_t M, int64_t N, int64_t K, float alpha, float* c, int64_t ldc,
-                    SplitPlan plan, float* part, hipStream_t st);
+                    SplitPlan plan, float* part, int64_t lds_a, int64_t lds_b, hipStream_t st);
 bool gemm_pairable(int64_t M0, int64_t N0, SplitPlan plan0, int64_t M1, int64_t N1,
                    SplitPlan plan1);
 int gemm_pair_impl(const uint8_t* a0, const uint8_t* sa0, const uint8_t* b0, const uint8_t* sb0,
                    int64_t M0, int64_t N0, int64_t K0, float alpha0, float* c0, int64_t ldc0,
-                   SplitPlan plan0, float* part0, const uint8_t* a1, const uint8_t* sa1,
-                   const uint8_t* b1, const uint8_t* sb1, int64_t M1, int64_t N1, int64_t K1,
-                   float alpha1, float* c1, int64_t ldc1, hipStream_t st);
+                   SplitPlan plan0, float* part0, int64_t lds_a0, int64_t lds_b0,
+                   const uint8_t* a1, const uint8_t* sa1, const uint8_t* b1, const uint8_t* sb1,
+                   int64_t M1, int64_t N1, int64_t K1, float alpha1, float* c1, int64_t ldc1,
+                   int64_t lds_a1, int64_t lds_b1, hipStream_t st);
 int gemm_ranges_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                      int64_t M, int64_t N, int64_t K, const int64_t* kbeg, int n, float alpha,
-                     float* c, hipStream_t st);
+                     float* c, int64_t lds_a, int64_t lds_b, hipStream_t st);
 int requantize_batched_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t batch,
                             int64_t rows, int64_t cols, int round, uint64_t seed, uint8_t* codes,
-                            uint8_t* scales, hipStream_t st);
+                            uint8_t* scales, hipStream_t st, int64_t s_pitch);
 int quantize_dual_segments_impl(const void* x, int dtype, int64_t rows, int64_t cols,
                                 const int64_t* offs, int64_t groups, int round, uint64_t seed_row,
                                 uint64_t seed_col, uint8_t* codes_row, uint8_t* scales_row,
-                                uint8_t* codes_col, uint8_t* scales_col, hipStream_t st);
+                                uint8_t* codes_col, uint8_t* scales_col, hipStream_t st,
+                                int64_t sp_row, int64_t sp_col);
 int requantize_segments_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
                              int64_t cols, const int64_t* offs, int64_t groups, int round,
-                             uint64_t seed, uint8_t* codes, uint8_t* scales, hipStream_t st);
+                             uint64_t seed, uint8_t* codes, uint8_t* scales, hipStream_t st,
+                             int64_t s_pitch);
 int64_t segments_padded_rows(const int64_t* offs, int64_t groups);
 void segments_padded_offsets(const int64_t* offs, int64_t groups, int64_t* out);
 
 static size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Workspace layout: four packed operands, each codes then scales, then the
-// split-K partial sums of the dX / dW products when they are split (shared:
-// the two products run one after the other, and a launch that pairs them
-// splits only dW), all 256-byte aligned.
+// Scale rows of the backward operands in the workspace are padded to a
+// multiple of 16 bytes, so every product can load four steps' scales of a row
+// with one 16-byte access (the padding is never read as data).
+static int64_t pad16(int64_t v) { return (v + 15) / 16 * 16; }
+
+// Workspace layout: four packed operands, each codes then scales (scale rows
+// p3..p6 bytes apart), then the split-K partial sums of the dX / dW products
+// when they are split (shared: the two products run one after the other, and a
+// launch that pairs them splits only dW), all 256-byte aligned.
 struct BwdLayout {
   size_t q3c, q3s, q4c, q4s, q5c, q5s, q6c, q6s, part, total;
+  int64_t p3, p4, p5, p6;
   SplitPlan dx, dw;
 };
 
@@ -86,10 +96,12 @@ static BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K) {
     o += round256(bytes);
     return at;
   };
-  L.q3c = take((size_t)M * N / 2);  L.q3s = take((size_t)M * N / 32);   // dY rows   [M][N]
-  L.q4c = take((size_t)K * N / 2);  L.q4s = take((size_t)K * N / 32);   // W^T blocks [K][N]
-  L.q5c = take((size_t)N * M / 2);  L.q5s = take((size_t)N * M / 32);   // dY^T      [N][M]
-  L.q6c = take((size_t)K * M / 2);  L.q6s = take((size_t)K * M / 32);   // X^T blocks [K][M]
+  L.p3 = L.p4 = pad16(N / 32);
+  L.p5 = L.p6 = pad16(M / 32);
+  L.q3c = take((size_t)M * N / 2);  L.q3s = take((size_t)(M * L.p3));   // dY rows   [M][N]
+  L.q4c = take((size_t)K * N / 2);  L.q4s = take((size_t)(K * L.p4));   // W^T blocks [K][N]
+  L.q5c = take((size_t)N * M / 2);  L.q5s = take((size_t)(N * L.p5));   // dY^T      [N][M]
+  L.q6c = take((size_t)K * M / 2);  L.q6s = take((size_t)(K * L.p6));   // X^T blocks [K][M]
   L.dx = gemm_split_plan(M, K, N);   // dX [M][K], contraction over N
   L.dw = gemm_split_plan(N, K, M);   // dW [N][K], contraction over M
   const size_t px = L.dx.n > 1 ? (size_t)L.dx.n * M * K * 4 : 0;
@@ -100,10 +112,11 @@ static BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K) {
 }
 
 // Grouped (mixture-of-experts) backward workspace: Q3 [R][N], the experts'
-// Q4 [E][K][N], Q5 [N][P] and Q6 [K][P] packed, P = the padded token axis.
+// Q4 [E][K][N], Q5 [N][P] and Q6 [K][P] packed, P = the padded token axis;
+// scale rows p3..p6 bytes apart.
 struct GroupedLayout {
   size_t q3c, q3s, q4c, q4s, q5c, q5s, q6c, q6s, total;
-  int64_t P;
+  int64_t P, p3, p4, p5, p6;
 };
 
 static GroupedLayout grouped_layout(const int64_t* offs, int64_t E, int64_t N, int64_t K) {
@@ -116,10 +129,12 @@ static GroupedLayout grouped_layout(const int64_t* offs, int64_t E, int64_t N, i
     o += round256(bytes);
     return at;
   };
-  L.q3c = take((size_t)R * N / 2);      L.q3s = take((size_t)R * N / 32);
-  L.q4c = take((size_t)E * K * N / 2);  L.q4s = take((size_t)E * K * N / 32);
-  L.q5c = take((size_t)N * L.P / 2);    L.q5s = take((size_t)N * L.P / 32);
-  L.q6c = take((size_t)K * L.P / 2);    L.q6s = take((size_t)K * L.P / 32);
+  L.p3 = L.p4 = pad16(N / 32);
+  L.p5 = L.p6 = pad16(L.P / 32);
+  L.q3c = take((size_t)R * N / 2);      L.q3s = take((size_t)(R * L.p3));
+  L.q4c = take((size_t)E * K * N / 2);  L.q4s = take((size_t)(E * K * L.p4));
+  L.q5c = take((size_t)N * L.P / 2);    L.q5s = take((size_t)(N * L.p5));
+  L.q6c = take((size_t)K * L.P / 2);    L.q6s = take((size_t)(K * L.p6));
   L.total = o;
   return L;
 }
@@ -154,7 +169,7 @@ static int linear_fwd_impl(const void* x, const void* w, int dtype, int64_t M, i
   if (s != MX_OK) return s;
   const int64_t offs[2] = {0, M};
   return gemm_impl(xq_codes, xq_scales, wq_codes, wq_scales, offs, 1, N, K,
-                   had ? kHadamardAlpha : 1.0f, y, N, 0, 0, st);
+                   had ? kHadamardAlpha : 1.0f, y, N, 0, 0, K / 32, K / 32, st);
 }
 
 static int linear_bwd_impl(const void* dy, int dtype, int64_t M, int64_t N, int64_t K,
@@ -174,8 +189,12 @@ static int linear_bwd_impl(const void* dy, int dtype, int64_t M, int64_t N, int6
   MX_REQUIRE(aligned16(workspace), MX_ERR_ALIGN);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
 
+  // scale pitches of Q3..Q6: padded, except that the rotated kernels write
+  // packed rows (into the same, larger, buffers)
+  const int64_t p3 = had ? N / 32 : L.p3, p4 = had ? N / 32 : L.p4;
+  const int64_t p5 = had ? M / 32 : L.p5, p6 = had ? M / 32 : L.p6;
   int s = quantize_dual_impl(dy, dtype, M, N, MX_SR, seed + 3, seed + 5, had, mask, ws + L.q3c,
-                             ws + L.q3s, ws + L.q5c, ws + L.q5s, st);
+                             ws + L.q3s, ws + L.q5c, ws + L.q5s, st, p3, p5);
   if (s != MX_OK) return s;
   if (had) {  // the rotated Q4 and Q6 in one launch
     s = requantize_rht_pair_impl(wq_codes, wq_scales, N, xq_codes, xq_scales, M, K, MX_SR,
@@ -183,21 +202,21 @@ static int linear_bwd_impl(const void* dy, int dtype, int64_t M, int64_t N, int6
                                  ws + L.q6s, st);
   } else {  // Q4 = Q_S(Q_D(W)) and Q6 = Q_S(Q_D(X)) in one launch
     s = requantize_pair_impl(wq_codes, wq_scales, N, xq_codes, xq_scales, M, K, MX_SR, seed + 4,
-                             seed + 6, ws + L.q4c, ws + L.q4s, ws + L.q6c, ws + L.q6s, st);
+                             seed + 6, ws + L.q4c, ws + L.q4s, ws + L.q6c, ws + L.q6s, st, p4, p6);
   }
   if (s != MX_OK) return s;
   const float alpha = had ? kHadamardAlpha : 1.0f;
   float* part = reinterpret_cast<float*>(ws + L.part);
   if (gemm_pairable(N, K, L.dw, M, K, L.dx)) {  // small products: dW and dX in one launch
     return gemm_pair_impl(ws + L.q5c, ws + L.q5s, ws + L.q6c, ws + L.q6s, N, K, M, alpha, dw, K,
-                          L.dw, part, ws + L.q3c, ws + L.q3s, ws + L.q4c, ws + L.q4s, M, K, N,
-                          alpha, dx, K, st);
+                          L.dw, part, p5, p6, ws + L.q3c, ws + L.q3s, ws + L.q4c, ws + L.q4s, M,
+                          K, N, alpha, dx, K, p3, p4, st);
   }
   s = gemm_split_impl(ws + L.q3c, ws + L.q3s, ws + L.q4c, ws + L.q4s, M, K, N, alpha, dx, K, L.dx,
-                      part, st);
+                      part, p3, p4, st);
   if (s != MX_OK) return s;
   return gemm_split_impl(ws + L.q5c, ws + L.q5s, ws + L.q6c, ws + L.q6s, N, K, M, alpha, dw, K,
-                         L.dw, part, st);
+                         L.dw, part, p5, p6, st);
 }
 
 }  // namespace mx
@@ -277,25 +296,26 @@ extern "C" int mx_grouped_linear_bwd(const void* dy, int dtype, const int64_t* o
   const hipStream_t st = as_stream(stream);
 
   int s = requantize_batched_impl(wq_codes, wq_scales, E, N, K, MX_SR, seed + 4, ws + L.q4c,
-                                  ws + L.q4s, st);
+                                  ws + L.q4s, st, L.p4);
   if (s != MX_OK) return s;
   if (R > 0) {
     // Q3 (1x32 along N, every token) and Q5 (32x1 along each expert's tokens)
     // from one read of dY
     s = quantize_dual_segments_impl(dy, dtype, R, N, offs, E, MX_SR, seed + 3, seed + 5,
-                                    ws + L.q3c, ws + L.q3s, ws + L.q5c, ws + L.q5s, st);
+                                    ws + L.q3c, ws + L.q3s, ws + L.q5c, ws + L.q5s, st, L.p3,
+                                    L.p5);
     if (s != MX_OK) return s;
     s = requantize_segments_impl(xq_codes, xq_scales, R, K, offs, E, MX_SR, seed + 6, ws + L.q6c,
-                                 ws + L.q6s, st);
+                                 ws + L.q6s, st, L.p6);
     if (s != MX_OK) return s;
     s = gemm_impl(ws + L.q3c, ws + L.q3s, ws + L.q4c, ws + L.q4s, offs, E, K, N, 1.0f, dx, K,
-                  K * N / 2, K * N / 32, st);
+                  K * N / 2, K * L.p4, L.p3, L.p4, st);
     if (s != MX_OK) return s;
   }
   int64_t kbeg[MX_MAX_GROUPS + 1];
   segments_padded_offsets(offs, E, kbeg);
   return gemm_ranges_impl(ws + L.q5c, ws + L.q5s, ws + L.q6c, ws + L.q6s, N, K, L.P, kbeg, (int)E,
-                          1.0f, dw, st);
+                          1.0f, dw, L.p5, L.p6, st);
 }
 
 extern "C" const char* mx_status_string(int status) {

@@ -239,14 +239,16 @@ __device__ __forceinline__ uint4 quant_col32(float v[32], uint32_t& byte_out, ui
 }
 
 // Writes staged column-block codes/scales: output row (col0 + c) gets bytes
-// [row0/2, row0/2 + 16 nrb) of codes and [row0/32, row0/32 + nrb) of scales,
-// for c < ncols; staging layout [c][rb], NRB row blocks per column.
+// [row0/2, row0/2 + 16 nrb) of codes and [row0/32, row0/32 + nrb) of scales
+// (scale rows ld_s bytes apart, at least rows / 32), for c < ncols; staging
+// layout [c][rb], NRB row blocks per column.
 template <int NC, int NRB>
 __device__ __forceinline__ void store_col_tile(const uint4* s_codes, const uint8_t* s_scales,
-                                               int64_t rows, int64_t col0, int ncols, int64_t row0,
-                                               int nrb, uint8_t* __restrict__ codes,
+                                               int64_t rows, int64_t ld_s, int64_t col0,
+                                               int ncols, int64_t row0, int nrb,
+                                               uint8_t* __restrict__ codes,
                                                uint8_t* __restrict__ scales) {
-  const int64_t ld_c = rows / 2, ld_s = rows / 32;
+  const int64_t ld_c = rows / 2;
   for (int i = threadIdx.x; i < NC * NRB; i += blockDim.x) {
     const int c = i / NRB, rb = i % NRB;
     if (c < ncols && rb < nrb) {
@@ -268,7 +270,8 @@ template <typename T, int ROUND, bool ROW, bool HAD>
 __global__ __launch_bounds__(256) void k_quant_tile(
     const T* __restrict__ x, int64_t rows, int64_t cols, uint64_t seed_row, uint64_t seed_col,
     uint32_t sign_mask, uint8_t* __restrict__ codes_row, uint8_t* __restrict__ scales_row,
-    uint8_t* __restrict__ codes_col, uint8_t* __restrict__ scales_col, const Segs segs) {
+    uint8_t* __restrict__ codes_col, uint8_t* __restrict__ scales_col, const Segs segs,
+    int64_t sp_row, int64_t sp_col) {
   constexpr int E = 16 / sizeof(T);               // elements per 16-byte chunk
   constexpr int TC = kTileRowBytes / sizeof(T);   // tile columns
   constexpr int CPR = kTileRowBytes / 16;         // chunks per tile row (16)
@@ -336,7 +339,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(
       const uint32_t packed = quant_run<ROUND, E>(v, byte, seed_row, idx0);
       if constexpr (E == 8) reinterpret_cast<uint32_t*>(codes_row)[idx0 / 8] = packed;
       else reinterpret_cast<uint16_t*>(codes_row)[idx0 / 4] = (uint16_t)packed;
-      if (lc % (32 / E) == 0) scales_row[idx0 / 32] = (uint8_t)byte;
+      if (lc % (32 / E) == 0) scales_row[(row0 + r) * sp_row + (col0 + lc * E) / 32] = (uint8_t)byte;
     }
   }
   __syncthreads();
@@ -374,8 +377,8 @@ __global__ __launch_bounds__(256) void k_quant_tile(
     }
   }
   __syncthreads();
-  store_col_tile<TC, NRB>(s_codes, s_scales, tr.out_len, col0, ncols, tr.out0, nrb, codes_col,
-                          scales_col);
+  store_col_tile<TC, NRB>(s_codes, s_scales, tr.out_len, sp_col, col0, ncols, tr.out0, nrb,
+                          codes_col, scales_col);
 }
 
 // ============================================================== double quantization
@@ -402,6 +405,7 @@ struct RqJob {
   uint64_t seed;
   uint8_t* codes;
   uint8_t* scales;
+  int64_t s_pitch;  // bytes between output scale rows (at least the output row's blocks)
 };
 
 template <int ROUND>
@@ -420,7 +424,7 @@ __global__ __launch_bounds__(256) void k_requant(const RqJob j0, const RqJob j1,
   const uint8_t* __restrict__ codes_in = job.codes_in + z * rows * (cols / 2);
   const uint8_t* __restrict__ scales_in = job.scales_in + z * rows * (cols / 32);
   uint8_t* __restrict__ codes = job.codes + z * rows * (cols / 2);
-  uint8_t* __restrict__ scales = job.scales + z * rows * (cols / 32);
+  uint8_t* __restrict__ scales = job.scales + z * cols * job.s_pitch;
   const int64_t col0 = (int64_t)blockIdx.x * kRqC;
   const TileRows tr = tile_rows(segs, kRqR, rows, ty);
   const int64_t row0 = tr.row0;
@@ -464,7 +468,7 @@ __global__ __launch_bounds__(256) void k_requant(const RqJob j0, const RqJob j1,
     }
   }
   __syncthreads();
-  store_col_tile<kRqC, NRB>(s_codes, s_scales, tr.out_len, col0, ncols, tr.out0, nrb, codes,
+  store_col_tile<kRqC, NRB>(s_codes, s_scales, tr.out_len, job.s_pitch, col0, ncols, tr.out0, nrb, codes,
                             scales);
 }
 
@@ -554,7 +558,8 @@ __global__ __launch_bounds__(256) void k_requant_rht(const RhtJobs jobs, int64_t
     }
   }
   __syncthreads();
-  store_col_tile<kRhtC, NRB>(s_codes, s_scales, rows, col0, ncols, row0, nrb, codes, scales);
+  store_col_tile<kRhtC, NRB>(s_codes, s_scales, rows, rows / 32, col0, ncols, row0, nrb, codes,
+                             scales);
 }
 
 // ============================================================== dequantization
@@ -730,12 +735,16 @@ template <typename T, bool ROW>
 static int launch_quant_tile(const T* x, int64_t rows, int64_t cols, int round, uint64_t seed_row,
                              uint64_t seed_col, int had, uint32_t mask, uint8_t* codes_row,
                              uint8_t* scales_row, uint8_t* codes_col, uint8_t* scales_col,
-                             hipStream_t st, const Segs& segs = plain_segs()) {
+                             hipStream_t st, const Segs& segs = plain_segs(),
+                             int64_t sp_row = 0, int64_t sp_col = 0) {
   constexpr int TC = kTileRowBytes / sizeof(T);
+  // scale row pitches of the two outputs: 0 = packed (blocks per row)
+  if (sp_row == 0) sp_row = cols / 32;
+  if (sp_col == 0) sp_col = (segs.n ? segs.out_len : rows) / 32;
   const unsigned ty = segs.n ? (unsigned)segs.tile_start[segs.n] : (unsigned)cdiv(rows, kTileR);
   if (ty == 0) return MX_OK;
   const dim3 grid((unsigned)cdiv(cols, TC), ty), block(256);
-#define MX_TILE_ARGS x, rows, cols, seed_row, seed_col, mask, codes_row, scales_row, codes_col, scales_col, segs
+#define MX_TILE_ARGS x, rows, cols, seed_row, seed_col, mask, codes_row, scales_row, codes_col, scales_col, segs, sp_row, sp_col
   constexpr bool kHad = !ROW || sizeof(T) == 2;  // rotated row pass: bf16 only
   if (round == MX_RNE) {
     if (had && kHad) k_quant_tile<T, MX_RNE, ROW, kHad><<<grid, block, 0, st>>>(MX_TILE_ARGS);
@@ -778,9 +787,10 @@ static int launch_requant_jobs(const RqJob& j0, const RqJob& j1, int ty0, int ty
 
 static int launch_requant(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
                           int64_t cols, int round, uint64_t seed, uint8_t* codes, uint8_t* scales,
-                          int64_t batch, const Segs& segs, hipStream_t st) {
+                          int64_t batch, const Segs& segs, hipStream_t st, int64_t s_pitch = 0) {
   const int ty = segs.n ? segs.tile_start[segs.n] : (int)cdiv(rows, kRqR);
-  const RqJob j{codes_in, scales_in, rows, seed, codes, scales};
+  if (s_pitch == 0) s_pitch = (segs.n ? segs.out_len : rows) / 32;
+  const RqJob j{codes_in, scales_in, rows, seed, codes, scales, s_pitch};
   return launch_requant_jobs(j, j, ty, 0, cols, round, batch, segs, st);
 }
 
@@ -792,15 +802,18 @@ int requantize_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t r
 }
 
 // Two packed row-blocked matrices [rows0, cols] and [rows1, cols] requantized
-// (32x1, transposed outputs) by one launch, each with its own seed.
+// (32x1, transposed outputs) by one launch, each with its own seed; the output
+// scale rows are s_pitch0 / s_pitch1 bytes apart (0: packed).
 int requantize_pair_impl(const uint8_t* codes_in0, const uint8_t* scales_in0, int64_t rows0,
                          const uint8_t* codes_in1, const uint8_t* scales_in1, int64_t rows1,
                          int64_t cols, int round, uint64_t seed0, uint64_t seed1,
                          uint8_t* codes0, uint8_t* scales0, uint8_t* codes1, uint8_t* scales1,
-                         hipStream_t st) {
+                         hipStream_t st, int64_t s_pitch0 = 0, int64_t s_pitch1 = 0) {
   if (cols == 0) return MX_OK;
-  const RqJob j0{codes_in0, scales_in0, rows0, seed0, codes0, scales0};
-  const RqJob j1{codes_in1, scales_in1, rows1, seed1, codes1, scales1};
+  const RqJob j0{codes_in0, scales_in0, rows0, seed0, codes0, scales0,
+                 s_pitch0 ? s_pitch0 : rows0 / 32};
+  const RqJob j1{codes_in1, scales_in1, rows1, seed1, codes1, scales1,
+                 s_pitch1 ? s_pitch1 : rows1 / 32};
   return launch_requant_jobs(j0, j1, (int)cdiv(rows0, kRqR), (int)cdiv(rows1, kRqR), cols, round,
                              1, plain_segs(), st);
 }
@@ -809,10 +822,10 @@ int requantize_pair_impl(const uint8_t* codes_in0, const uint8_t* scales_in0, in
 // experts' weights); stochastic rounding indexes the stacked [batch*rows, cols].
 int requantize_batched_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t batch,
                             int64_t rows, int64_t cols, int round, uint64_t seed, uint8_t* codes,
-                            uint8_t* scales, hipStream_t st) {
+                            uint8_t* scales, hipStream_t st, int64_t s_pitch = 0) {
   if (rows == 0 || cols == 0) return MX_OK;
   return launch_requant(codes_in, scales_in, rows, cols, round, seed, codes, scales, batch,
-                        plain_segs(), st);
+                        plain_segs(), st, s_pitch);
 }
 
 template <typename T>
@@ -871,39 +884,46 @@ int quantize_segments_impl(const void* x, int dtype, int64_t rows, int64_t cols,
 int quantize_dual_segments_impl(const void* x, int dtype, int64_t rows, int64_t cols,
                                 const int64_t* offs, int64_t groups, int round, uint64_t seed_row,
                                 uint64_t seed_col, uint8_t* codes_row, uint8_t* scales_row,
-                                uint8_t* codes_col, uint8_t* scales_col, hipStream_t st) {
+                                uint8_t* codes_col, uint8_t* scales_col, hipStream_t st,
+                                int64_t sp_row = 0, int64_t sp_col = 0) {
   if (rows == 0 || cols == 0) return MX_OK;
   const Segs s = make_segs(offs, groups, kTileR);
   return dtype == MX_BF16
              ? launch_quant_tile<uint16_t, true>(static_cast<const uint16_t*>(x), rows, cols, round,
                                                  seed_row, seed_col, 0, 0, codes_row, scales_row,
-                                                 codes_col, scales_col, st, s)
+                                                 codes_col, scales_col, st, s, sp_row, sp_col)
              : launch_quant_tile<float, true>(static_cast<const float*>(x), rows, cols, round,
                                               seed_row, seed_col, 0, 0, codes_row, scales_row,
-                                              codes_col, scales_col, st, s);
+                                              codes_col, scales_col, st, s, sp_row, sp_col);
 }
 
 int requantize_segments_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
                              int64_t cols, const int64_t* offs, int64_t groups, int round,
-                             uint64_t seed, uint8_t* codes, uint8_t* scales, hipStream_t st) {
+                             uint64_t seed, uint8_t* codes, uint8_t* scales, hipStream_t st,
+                             int64_t s_pitch = 0) {
   if (rows == 0 || cols == 0) return MX_OK;
   return launch_requant(codes_in, scales_in, rows, cols, round, seed, codes, scales, 1,
-                        make_segs(offs, groups, kRqR), st);
+                        make_segs(offs, groups, kRqR), st, s_pitch);
 }
 
+// sp_row / sp_col: bytes between scale rows of the row-blocked [rows][cols/32]
+// and column-blocked [cols][rows/32] outputs (0: packed).
 int quantize_dual_impl(const void* x, int dtype, int64_t rows, int64_t cols, int round,
                        uint64_t seed_row, uint64_t seed_col, int had, uint32_t mask,
                        uint8_t* codes_row, uint8_t* scales_row, uint8_t* codes_col,
-                       uint8_t* scales_col, hipStream_t st) {
+                       uint8_t* scales_col, hipStream_t st, int64_t sp_row = 0,
+                       int64_t sp_col = 0) {
   if (rows == 0 || cols == 0) return MX_OK;
   if (dtype == MX_BF16)
     return launch_quant_tile<uint16_t, true>(static_cast<const uint16_t*>(x), rows, cols, round,
                                              seed_row, seed_col, had, mask, codes_row, scales_row,
-                                             codes_col, scales_col, st);
+                                             codes_col, scales_col, st, plain_segs(), sp_row,
+                                             sp_col);
   if (!had)
     return launch_quant_tile<float, true>(static_cast<const float*>(x), rows, cols, round,
                                           seed_row, seed_col, 0, 0, codes_row, scales_row,
-                                          codes_col, scales_col, st);
+                                          codes_col, scales_col, st, plain_segs(), sp_row, sp_col);
+  if ((sp_row && sp_row != cols / 32) || (sp_col && sp_col != rows / 32)) return MX_ERR_SHAPE;
   // float32 with the rotation: a row block spans 8 lanes of the tile kernel, so
   // the two block shapes go through the row kernel and the column tile kernel
   const int s = quantize_impl(x, dtype, rows, cols, MX_ROW, round, seed_row, 1, mask, codes_row,
