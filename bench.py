@@ -35,8 +35,8 @@ PEAK_FP4_TFLOPS = 10100.0
 # from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB copy, valid for
 # the GEMM code with this sha256 only (of the source with comments and blank
 # lines removed; the per-launch table is kept with the committed profiles).
-GEMM_TRAFFIC = {"sha256": "b4535da460a8dd352238eb7d4af887af4a413863b08cece3850fbb8bc0b04171",
-                "bytes_per_launch": 668299899}
+GEMM_TRAFFIC = {"sha256": "4640713cf0d4664a0cd78a10a5c0644fdf5de2d3bc0fe7b0007ac202f29cbe1d",
+                "bytes_per_launch": 668222061}
 
 
 def gemm_code_sha256(path):
