@@ -25,3 +25,36 @@ def test_defaults_are_one_gpu_and_a_short_run():
     finally:
         sys.argv = old
     assert a.gpus == 1 and 1 <= a.steps <= 50 and 0 <= a.warmup <= 10
+
+
+def test_attainable_time_of_the_deit_layer():
+    """Sum over the six kernels of max(flops / 10.1 PFLOP/s, bytes / 8 TB/s), written out
+    for M, N, K = 12608, 1536, 384 (every kernel is bandwidth-bound at this shape)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    M, N, K = 12608, 1536, 384
+    pk = 17 / 32  # packed bytes per element: half a code byte + 1/32 scale byte
+    bytes_ = [(M + N) * K * (2 + pk),            # quantize X and W
+              (M + N) * K * pk + 4 * M * N,      # Y
+              M * N * (2 + 2 * pk),              # dual quantization of dY
+              (N + M) * K * 2 * pk,              # double quantization of W and X
+              (M + K) * N * pk + 4 * M * K,      # dX = Q3 [M, N] . Q4 [K, N]^T
+              (N + K) * M * pk + 4 * N * K]      # dW = Q5 [N, M] . Q6 [K, M]^T
+    flops = 2.0 * M * N * K
+    for b, f in zip(bytes_, [0, flops, 0, 0, flops, flops]):
+        assert b / 8e12 >= f / 10.1e15      # bandwidth-bound
+    want_ms = sum(bytes_) / 8e12 * 1e3
+    assert abs(bench.linear_attainable_ms(M, N, K) - want_ms) < 1e-12
+
+
+def test_gemm_code_hash_ignores_comments_only(tmp_path):
+    sys.path.insert(0, ROOT)
+    import bench
+    a = tmp_path / "a.hip"
+    b = tmp_path / "b.hip"
+    c = tmp_path / "c.hip"
+    a.write_text("int f() {\n  return 1;  // one\n}\n")
+    b.write_text("// header\n\nint f() {\n  return 1;\n}\n\n")
+    c.write_text("int f() {\n  return 2;\n}\n")
+    assert bench.gemm_code_sha256(a) == bench.gemm_code_sha256(b)
+    assert bench.gemm_code_sha256(a) != bench.gemm_code_sha256(c)
