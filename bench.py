@@ -9,9 +9,12 @@ channels x30, weights N(0, 0.02), dY N(0, 1e-3)):
   one launch), GEMM dX, GEMM dW
 
 -- the kernels mx_linear_fwd / mx_linear_bwd launch, issued one entry point at
-a time so that every kernel is bracketed by events on the stream it runs on.
-value = 6 M N K / step time (TFLOP/s).  The line also carries the dominant
-kernel's roofline (the GEMM, vs the dense FP4 MFMA peak), the oracle's CPU
+a time on one stream.  value = 6 M N K / step time (TFLOP/s), the steps timed
+back to back with events at the two ends of the timed region only (an event
+record between kernels stops the next one from starting while the previous one
+drains).  The GEMM's launch duration for its roofline comes from a second pass
+of the same steps with an event pair around every GEMM launch.  The line also
+carries the dominant kernel's roofline (the GEMM, vs the dense FP4 MFMA peak), the oracle's CPU
 throughput on a bounded sample, and the other rows of the path measured on
 their own workloads: the DeiT-S fc1 layer (12608 x 384 -> 1536) through
 mx_linear_fwd / mx_linear_bwd, eager and as a replayed HIP graph; the rotated
@@ -69,7 +72,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parts", action="store_true", help="skip the quantizer sweep / MoE rows")
     p.add_argument("--only", default=None, help="run one part only: linear|deit|rht|sweep|moe|deosc")
@@ -145,9 +148,11 @@ def bench_linear(torch, mx, synth, dev, steps, warmup, seed=3):
 
     def step(timer, timed=("gemm",)):
         """One linear fwd+bwd.  Only the kernels named in `timed` get event pairs
-        (an event record between kernels costs a few microseconds)."""
+        (timer None: none).  An event record between two kernels keeps the second
+        from starting while the first drains its last tiles (~20 us a record), so
+        the step's own timed region has none."""
         def run(name, fn):
-            (timer.run(name, fn) if name in timed else fn())
+            (timer.run(name, fn) if timer is not None and name in timed else fn())
         run("quant_xw", lambda: mx.mx_quantize_pair(x, M, w, N, K, BF, mx.MX_RNE, 0, 0, 0, 0,
                                                    *xq, *wq, st))
         run("gemm", lambda: mx.mx_gemm(*xq, *wq, M, N, K, 1.0, y, N, st))
@@ -158,36 +163,48 @@ def bench_linear(torch, mx, synth, dev, steps, warmup, seed=3):
         run("gemm", lambda: mx.mx_gemm(*q3, *q4, M, K, N, 1.0, dx, K, st))
         run("gemm", lambda: mx.mx_gemm(*q5, *q6, N, K, M, 1.0, dw, K, st))
 
-    warm = Timer(torch, st)
-    for _ in range(warmup):
-        step(warm)
-    torch.cuda.synchronize()
     # the composed step equals the library's own linear entry points, bit for bit
+    # (checked first: the host-side comparison idles the GPU, whose clock then
+    # needs the warm-up steps to come back up before the timed region)
+    step(None)
     y2, xq2, wq2 = mx.linear_fwd(x, w)
     dx2, dw2 = mx.linear_bwd(dy, xq2, wq2, M, N, K, seed)
     torch.cuda.synchronize()
     same = all(torch.equal(a, b) for a, b in ((y, y2), (dx, dx2), (dw, dw2)))
     del y2, xq2, wq2, dx2, dw2
     torch.cuda.synchronize()
+    for _ in range(warmup):
+        step(None)
 
+    # the timed region: `steps` steps back to back, events at its two ends only
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(st)
     for _ in range(steps):
-        step(T)
+        step(None)
     end.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / steps
     flops = 6.0 * M * N * K
+    # the GEMM launch duration for the roofline: a second live pass of `steps`
+    # steps with an event pair around every GEMM launch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(steps):
+        step(T)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms_step_events = e0.elapsed_time(e1) / steps
     # per-kernel breakdown of the quantizers: a separate pass with every kernel timed
     B = Timer(torch, st)
     for _ in range(5):
         step(B, timed=("quant_xw", "dual_dy", "requant_wx", "gemm"))
     torch.cuda.synchronize()
     kern = {k: B.mean_ms(k) for k in B.pairs}
-    kern["gemm"] = T.mean_ms("gemm")  # the GEMM launches of the timed region itself
+    kern["gemm"] = T.mean_ms("gemm")  # the GEMM launches of the second pass
     gemm_ms = kern["gemm"]
     gemm_tf = 2.0 * M * N * K / (gemm_ms * 1e-3) / 1e12
     bytes_q = {
@@ -198,6 +215,7 @@ def bench_linear(torch, mx, synth, dev, steps, warmup, seed=3):
                  "frac_hbm": bytes_q[k] / (kern[k] * 1e-3) / 1e9 / PEAK_HBM_GBPS} for k in bytes_q}
     return {
         "M": M, "N": N, "K": K, "ms_per_step": ms_step, "wall_s": wall,
+        "ms_per_step_with_gemm_events": ms_step_events,
         "tflops": flops / (ms_step * 1e-3) / 1e12, "attainable_ms": linear_attainable_ms(M, N, K),
         "frac_attainable": linear_attainable_ms(M, N, K) / ms_step,
         "gemm_ms": gemm_ms, "gemm_tflops": gemm_tf,
@@ -209,7 +227,9 @@ def bench_linear(torch, mx, synth, dev, steps, warmup, seed=3):
 # ---------------------------------------------------------------- rotated linear layer
 def bench_linear_rht(torch, mx, synth, dev, steps=10, seed=3, mask=0x9E3779B9):
     """The Llama up-projection through the random-sign Hadamard layer
-    (mx_linear_fwd_rht + mx_linear_bwd_rht), forward and backward timed apart."""
+    (mx_linear_fwd_rht + mx_linear_bwd_rht): after 5 untimed layers, the layer
+    timed as `steps` fwd+bwd calls back to back (events at the ends only), then
+    forward and backward apart with an event pair around each call."""
     cfg = synth.llama_config()
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
     x = bf16_dev(torch, cfg["x"], dev)
@@ -225,9 +245,18 @@ def bench_linear_rht(torch, mx, synth, dev, steps=10, seed=3, mask=0x9E3779B9):
     fwd = lambda: mx.mx_linear_fwd_rht(x, w, BF, M, N, K, mask, y, *xq, *wq, st)
     bwd = lambda: mx.mx_linear_bwd_rht(dy, BF, M, N, K, *xq, *wq, seed, mask, dx, dw, ws,
                                        ws.numel(), st)
-    for _ in range(2):
+    for _ in range(5):
         fwd()
         bwd()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(steps):
+        fwd()
+        bwd()
+    e1.record(st)
+    torch.cuda.synchronize()
+    layer = e0.elapsed_time(e1) / steps
     T = Timer(torch, st)
     for _ in range(steps):
         T.run("fwd", fwd)
@@ -235,8 +264,8 @@ def bench_linear_rht(torch, mx, synth, dev, steps=10, seed=3, mask=0x9E3779B9):
     torch.cuda.synchronize()
     f, b = T.mean_ms("fwd"), T.mean_ms("bwd")
     fl = 2.0 * M * N * K
-    return {"fwd_us": f * 1e3, "bwd_us": b * 1e3, "fwd_bwd_ms": f + b,
-            "TFLOPs": 3 * fl / ((f + b) * 1e-3) / 1e12, "sign_mask": mask}
+    return {"fwd_us": f * 1e3, "bwd_us": b * 1e3, "fwd_bwd_ms": layer,
+            "TFLOPs": 3 * fl / (layer * 1e-3) / 1e12, "sign_mask": mask}
 
 
 # ---------------------------------------------------------------- DeiT-S fc1 layer
@@ -535,6 +564,7 @@ def main():
                                "gemm_launches_timed": lin["gemm_launches"],
                                "step_attainable_ms": lin["attainable_ms"],
                                "step_frac_attainable": lin["frac_attainable"],
+                               "ms_per_step_with_gemm_events": lin["ms_per_step_with_gemm_events"],
                                "matches_linear_entry_points": lin["matches_linear_entry_points"]}
     ach = lin["gemm_tflops"]
     line = {

@@ -19,8 +19,8 @@
 // instruction writes whole row segments of C.
 //
 // Tiling: a workgroup of WM x WN waves owns a BM x BN tile of C (256 x 256 for
-// large problems: 128 x 128 per wave, 16 accumulator tiles; 128 x 128 for small
-// ones) and walks K in steps of 128 (64 code bytes per row) through a 4-stage
+// large problems: 2 x 4 waves of 128 x 64 with 16-byte scale-group loads, else
+// 2 x 2 waves of 128 x 128, 16 accumulator tiles; 128 x 128 for small ones) and walks K in steps of 128 (64 code bytes per row) through a 4-stage
 // LDS ring.  Direct global-to-LDS loads fill a stage three steps ahead; each
 // step reads the second K-half's fragments while the first half's MFMAs run,
 // and the next step's first half while the second half's run, with one
@@ -698,7 +698,10 @@ static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
   const bool big = !p1 && tiles256 * sp.n >= 512;
 #define MX_GEMM_ARGS a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, lds_a, lds_b, sp, p1, st
   if (big) {
-    if (sc == kScGroup) return launch_gemm<256, 256, 2, 2, kScGroup>(MX_GEMM_ARGS);
+    // group-mode scale loads leave registers for eight waves (two per SIMD, 128 x 64
+    // per wave: one wave's LDS waits and barrier overlap the other's MFMAs); the
+    // other modes keep four waves, where eight would spill in the K loop
+    if (sc == kScGroup) return launch_gemm<256, 256, 2, 4, kScGroup>(MX_GEMM_ARGS);
     if (sc == kScDword) return launch_gemm<256, 256, 2, 2, kScDword>(MX_GEMM_ARGS);
     if (sc == kScShort) return launch_gemm<256, 256, 2, 2, kScShort>(MX_GEMM_ARGS);
     return launch_gemm<256, 256, 2, 2, kScByte>(MX_GEMM_ARGS);

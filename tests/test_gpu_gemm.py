@@ -82,15 +82,19 @@ def test_gemm_tiny_config_end_to_end():
     assert_gemm_close(y, O.gemm(*oxq, *owq, 256, 256, 256), O.gemm_abs(*oxq, *owq, 256, 256, 256), "Y")
 
 
-def test_gemm_large_tile_path_sampled():
-    """6144 x 6144 x 512 takes the 256 x 256 workgroup tile; 64 sampled rows x all columns."""
+@pytest.mark.parametrize("M,N,K", [(6144, 6144, 512),     # 16-byte scale groups: 2 x 4 waves
+                                   (4000, 9000, 1536),    # the same, ragged M and N tiles
+                                   (6144, 6144, 640),     # dword scale loads: 2 x 2 waves
+                                   (5000, 7000, 2880),    # 2-byte scale loads, K tail
+                                   (6144, 6144, 480)])    # byte scale loads
+def test_gemm_large_tile_path_sampled(M, N, K):
+    """Shapes that take the 256 x 256 workgroup tile in each of its wave layouts; 64
+    sampled rows (the last one always included) x all columns."""
     rng = np.random.default_rng(5)
-    M = N = 6144
-    K = 512
     a = random_operand(rng, M, K)
     b = random_operand(rng, N, K)
     got = run_gemm(a, b, M, N, K)
-    rows = np.sort(rng.choice(M, 64, replace=False))
+    rows = np.sort(np.append(rng.choice(M - 1, 63, replace=False), M - 1))
     want = O.gemm(a[0][rows], a[1][rows], *b, 64, N, K)
     assert_gemm_close(got[rows], want, O.gemm_abs(a[0][rows], a[1][rows], *b, 64, N, K), "sampled")
 
