@@ -395,26 +395,45 @@ def bench_moe(torch, mx, synth, dev, iters=10, deosc_steps=20):
     st = torch.cuda.current_stream()
     wq = mx.quantize(w)
     xq_up, xq_dn = mx.quantize(x_up), mx.quantize(x_dn)
+    # the forward's operands also with their scale rows padded to 16 bytes
+    # (H = 2880: 90 scale bytes per row, 96 apart), the layout a caller picks so
+    # that the grouped product loads four K-steps' scales of a row at once
+    ld = (H // 32 + 15) // 16 * 16
+
+    def quantize_ld(x):
+        c = torch.empty((x.shape[0], H // 2), dtype=torch.uint8, device=dev)
+        s_ = torch.empty((x.shape[0], ld), dtype=torch.uint8, device=dev)
+        mx.mx_quantize_ld(x, mx.dtype_code(x), x.shape[0], H, mx.MX_ROW, mx.MX_RNE, 0, 0, 0, c, s_,
+                          ld, st)
+        return c, s_
+
+    wl, xl_up, xl_dn = quantize_ld(w), quantize_ld(x_up), quantize_ld(x_dn)
     c_up = torch.empty((int(offs[-1]), F), dtype=torch.float32, device=dev)
     c_dn = torch.empty((int(offs[-1]), H), dtype=torch.float32, device=dev)
     T = Timer(torch, st)
+    runs = {
+        "up_packed": lambda: mx.mx_gemm_grouped(*xq_up, wq[0][:E * F], wq[1][:E * F], offs, E, F, H,
+                                                1.0, c_up, st),
+        "down_packed": lambda: mx.mx_gemm_grouped(*xq_dn, wq[0][E * F:], wq[1][E * F:], offs, E, H,
+                                                  H, 1.0, c_dn, st),
+        "up": lambda: mx.mx_gemm_grouped_ld(xl_up[0], xl_up[1], ld, wl[0][:E * F], wl[1][:E * F], ld,
+                                            offs, E, F, H, 1.0, c_up, st),
+        "down": lambda: mx.mx_gemm_grouped_ld(xl_dn[0], xl_dn[1], ld, wl[0][E * F:], wl[1][E * F:],
+                                              ld, offs, E, H, H, 1.0, c_dn, st),
+    }
     for i in range(iters + 2):
-        f_up = lambda: mx.mx_gemm_grouped(*xq_up, wq[0][:E * F], wq[1][:E * F], offs, E, F, H, 1.0, c_up, st)
-        f_dn = lambda: mx.mx_gemm_grouped(*xq_dn, wq[0][E * F:], wq[1][E * F:], offs, E, H, H, 1.0, c_dn, st)
-        if i >= 2:
-            T.run("up", f_up)
-            T.run("down", f_dn)
-        else:
-            f_up()
-            f_dn()
+        for key, fn in runs.items():
+            (T.run(key, fn) if i >= 2 else fn())
     torch.cuda.synchronize()
     R = int(offs[-1])
     res = {}
-    for key, n_out in (("up", F), ("down", H)):
+    for key in runs:
+        n_out = F if key.startswith("up") else H
         ms = T.mean_ms(key)
         res[f"grouped_{key}"] = {"us": ms * 1e3,
                                  "TFLOPs": 2.0 * R * n_out * H / (ms * 1e-3) / 1e12,
                                  "frac_fp4_peak": 2.0 * R * n_out * H / (ms * 1e-3) / 1e12 / PEAK_FP4_TFLOPS}
+    del wl, xl_up, xl_dn
     # grouped backward (dX and every expert's dW): dY N(0, 1e-3) bf16 drawn on the
     # device with a fixed seed; 4 R N K flops (dX and dW each 2 R N K)
     gen = torch.Generator(device=dev)

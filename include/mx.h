@@ -40,7 +40,7 @@
  *
  * Ownership and execution
  *  - Every pointer argument is a DEVICE pointer owned by the caller, except
- *    `offs` of mx_gemm_grouped (host).  The library never allocates, frees or
+ *    `offs` of the grouped calls (host).  The library never allocates, frees or
  *    synchronizes; it keeps no state between calls, so every entry point is
  *    reentrant.  Work is enqueued on `stream` (a hipStream_t; NULL = default
  *    stream) and the call returns before it runs.
@@ -107,6 +107,17 @@ const char* mx_status_string(int status);
 int mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int axis, int round,
                 uint64_t seed, int hadamard, uint32_t sign_mask,
                 uint8_t* codes, uint8_t* scales, void* stream);
+
+/* mx_quantize_ld: mx_quantize with the output's scale rows scale_ld bytes apart
+ * (scale row r starts at scales + r * scale_ld; scale_ld >= the blocks per
+ * output row, cols/32 for MX_ROW, rows/32 for MX_COL, else MX_ERR_SHAPE).  The
+ * bytes of a scale row past its blocks are not written.  Codes are packed as
+ * for mx_quantize.  Scale rows padded to a multiple of 16 bytes let the GEMMs
+ * load the scales of four K-steps of a row at once (mx_gemm_ld,
+ * mx_gemm_grouped_ld). */
+int mx_quantize_ld(const void* x, int dtype, int64_t rows, int64_t cols, int axis, int round,
+                   uint64_t seed, int hadamard, uint32_t sign_mask,
+                   uint8_t* codes, uint8_t* scales, int64_t scale_ld, void* stream);
 
 /* mx_quantize_dual: one read of a [rows, cols] tensor, two quantizations:
  * a MX_ROW one (codes_row [rows][cols/2], scales_row [rows][cols/32], seed
@@ -214,6 +225,22 @@ int mx_gemm_grouped(const uint8_t* a_codes, const uint8_t* a_scales,
                     const uint8_t* b_codes, const uint8_t* b_scales,
                     const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha,
                     float* c, void* stream);
+
+/* mx_gemm_ld / mx_gemm_grouped_ld: mx_gemm / mx_gemm_grouped with the scale
+ * rows of A and of B a_scale_ld and b_scale_ld bytes apart (each >= K/32, else
+ * MX_ERR_SHAPE; the bytes past K/32 in a row are never used as data); for the
+ * grouped form, B_g's scales start at b_scales + g*N*b_scale_ld.  Codes are
+ * packed as for mx_gemm.  Same results, bit for bit, as the packed calls on the
+ * same values; pitches that are multiples of 16 (with 16-byte aligned scale
+ * arrays) take the fastest scale loads whatever K is. */
+int mx_gemm_ld(const uint8_t* a_codes, const uint8_t* a_scales, int64_t a_scale_ld,
+               const uint8_t* b_codes, const uint8_t* b_scales, int64_t b_scale_ld,
+               int64_t M, int64_t N, int64_t K, float alpha, float* c, int64_t ldc,
+               void* stream);
+int mx_gemm_grouped_ld(const uint8_t* a_codes, const uint8_t* a_scales, int64_t a_scale_ld,
+                       const uint8_t* b_codes, const uint8_t* b_scales, int64_t b_scale_ld,
+                       const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha,
+                       float* c, void* stream);
 
 /* ------------------------------------------------------------------ token segments
  * The 32x1 quantizers of a grouped (mixture-of-experts) layer run per token

@@ -871,6 +871,46 @@ extern "C" int mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const ui
                    K / 32, K / 32, as_stream(stream));
 }
 
+extern "C" int mx_gemm_ld(const uint8_t* a_codes, const uint8_t* a_scales, int64_t a_scale_ld,
+                          const uint8_t* b_codes, const uint8_t* b_scales, int64_t b_scale_ld,
+                          int64_t M, int64_t N, int64_t K, float alpha, float* c, int64_t ldc,
+                          void* stream) {
+  MX_REQUIRE(M >= 0 && N >= 0 && K >= 0 && K % 32 == 0, MX_ERR_SHAPE);
+  MX_REQUIRE(ldc >= N && ldc % 4 == 0, MX_ERR_SHAPE);
+  MX_REQUIRE(a_scale_ld >= K / 32 && b_scale_ld >= K / 32, MX_ERR_SHAPE);
+  MX_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31, MX_ERR_SHAPE);
+  if (M == 0 || N == 0) return MX_OK;
+  MX_REQUIRE(c, MX_ERR_NULL);
+  if (K > 0) MX_REQUIRE(a_codes && a_scales && b_codes && b_scales, MX_ERR_NULL);
+  MX_REQUIRE(aligned16(c), MX_ERR_ALIGN);
+  if (K > 0) MX_REQUIRE(aligned16(a_codes) && aligned16(b_codes), MX_ERR_ALIGN);
+  const int64_t offs[2] = {0, M};
+  return gemm_impl(a_codes, a_scales, b_codes, b_scales, offs, 1, N, K, alpha, c, ldc, 0, 0,
+                   a_scale_ld, b_scale_ld, as_stream(stream));
+}
+
+extern "C" int mx_gemm_grouped_ld(const uint8_t* a_codes, const uint8_t* a_scales,
+                                  int64_t a_scale_ld, const uint8_t* b_codes,
+                                  const uint8_t* b_scales, int64_t b_scale_ld,
+                                  const int64_t* offs, int64_t groups, int64_t N, int64_t K,
+                                  float alpha, float* c, void* stream) {
+  MX_REQUIRE(offs, MX_ERR_NULL);
+  MX_REQUIRE(groups >= 1 && groups <= MX_MAX_GROUPS, MX_ERR_SHAPE);
+  MX_REQUIRE(N >= 0 && K >= 0 && K % 32 == 0 && N % 4 == 0, MX_ERR_SHAPE);
+  MX_REQUIRE(a_scale_ld >= K / 32 && b_scale_ld >= K / 32, MX_ERR_SHAPE);
+  MX_REQUIRE(offs[0] == 0, MX_ERR_SHAPE);
+  for (int64_t g = 0; g < groups; ++g) MX_REQUIRE(offs[g + 1] >= offs[g], MX_ERR_SHAPE);
+  const int64_t M = offs[groups];
+  MX_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31, MX_ERR_SHAPE);
+  if (M == 0 || N == 0) return MX_OK;
+  MX_REQUIRE(c, MX_ERR_NULL);
+  if (K > 0) MX_REQUIRE(a_codes && a_scales && b_codes && b_scales, MX_ERR_NULL);
+  MX_REQUIRE(aligned16(c), MX_ERR_ALIGN);
+  if (K > 0) MX_REQUIRE(aligned16(a_codes) && aligned16(b_codes), MX_ERR_ALIGN);
+  return gemm_impl(a_codes, a_scales, b_codes, b_scales, offs, groups, N, K, alpha, c, N,
+                   N * K / 2, N * b_scale_ld, a_scale_ld, b_scale_ld, as_stream(stream));
+}
+
 extern "C" int mx_gemm_grouped(const uint8_t* a_codes, const uint8_t* a_scales,
                                const uint8_t* b_codes, const uint8_t* b_scales,
                                const int64_t* offs, int64_t groups, int64_t N, int64_t K,

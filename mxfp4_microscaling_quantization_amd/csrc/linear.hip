@@ -16,9 +16,6 @@
 #include "mx_host.h"
 
 namespace mx {
-int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, int axis, int round,
-                  uint64_t seed, int had, uint32_t mask, uint8_t* codes, uint8_t* scales,
-                  hipStream_t st);
 int quantize_dual_impl(const void* x, int dtype, int64_t rows, int64_t cols, int round,
                        uint64_t seed_row, uint64_t seed_col, int had, uint32_t mask,
                        uint8_t* codes_row, uint8_t* scales_row, uint8_t* codes_col,

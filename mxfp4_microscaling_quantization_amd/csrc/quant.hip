@@ -110,9 +110,10 @@ struct RowJobs {  // named fields: selected with ternaries, never indexed at run
   int64_t n0, n1;
   int64_t w0;  // windows of tensor 0
   int64_t nwin;
+  int64_t nbr, sld;  // one tensor with LD: blocks per row and bytes between scale rows
 };
 
-template <typename T, int ROUND, bool HAD, bool PAIR>
+template <typename T, int ROUND, bool HAD, bool PAIR, bool LD = false>
 __global__ __launch_bounds__(256) void k_quant_row(const RowJobs<T> jobs, uint32_t sign_mask) {
   const int q = threadIdx.x & 3;
   const int j = threadIdx.x >> 2;
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(256) void k_quant_row(const RowJobs<T> jobs, uint32
       m = quad_max_u32(m);
       const uint32_t byte = scale_byte_of(m);
       codes[b * 4 + q] = quant8<ROUND>(v[u], byte, seed, (uint64_t)b * 32 + q * 8);
-      if (q == 0) scales[b] = (uint8_t)byte;
+      if (q == 0) scales[LD ? (b / jobs.nbr) * jobs.sld + b % jobs.nbr : b] = (uint8_t)byte;
     }
   }
 }
@@ -660,6 +661,16 @@ static int launch_quant_row_jobs(RowJobs<T> jobs, int round, int had, uint32_t m
   jobs.nwin = jobs.w0 + cdiv(jobs.n1, per);
   if (jobs.nwin == 0) return MX_OK;
   const dim3 grid(grid_for_row(jobs.nwin * per)), block(256);
+  if (jobs.sld != 0) {  // one tensor, scale rows sld bytes apart
+    if (round == MX_RNE) {
+      if (had) k_quant_row<T, MX_RNE, true, false, true><<<grid, block, 0, st>>>(jobs, mask);
+      else k_quant_row<T, MX_RNE, false, false, true><<<grid, block, 0, st>>>(jobs, mask);
+    } else {
+      if (had) k_quant_row<T, MX_SR, true, false, true><<<grid, block, 0, st>>>(jobs, mask);
+      else k_quant_row<T, MX_SR, false, false, true><<<grid, block, 0, st>>>(jobs, mask);
+    }
+    return launch_status();
+  }
   if (jobs.n1 > 0) {
     if (round == MX_RNE) {
       if (had) k_quant_row<T, MX_RNE, true, true><<<grid, block, 0, st>>>(jobs, mask);
@@ -683,8 +694,12 @@ static int launch_quant_row_jobs(RowJobs<T> jobs, int round, int had, uint32_t m
 template <typename T>
 static int launch_quant_row(const T* x, int64_t rows, int64_t cols, int round, uint64_t seed,
                             int had, uint32_t mask, uint8_t* codes, uint8_t* scales,
-                            hipStream_t st) {
+                            hipStream_t st, int64_t sld = 0) {
   RowJobs<T> jobs{};
+  if (sld != 0 && sld != cols / 32) {  // 0 or cols / 32: packed scale rows
+    jobs.nbr = cols / 32;
+    jobs.sld = sld;
+  }
   jobs.x0 = jobs.x1 = x;
   jobs.codes0 = jobs.codes1 = reinterpret_cast<uint32_t*>(codes);
   jobs.scales0 = jobs.scales1 = scales;
@@ -757,23 +772,25 @@ static int launch_quant_tile(const T* x, int64_t rows, int64_t cols, int round, 
   return launch_status();
 }
 
+// sld: bytes between the output's scale rows (0: packed, blocks per row).
 int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, int axis, int round,
                   uint64_t seed, int had, uint32_t mask, uint8_t* codes, uint8_t* scales,
-                  hipStream_t st) {
+                  hipStream_t st, int64_t sld = 0) {
   if (rows == 0 || cols == 0) return MX_OK;
   if (axis == MX_ROW) {
     return dtype == MX_BF16
                ? launch_quant_row(static_cast<const uint16_t*>(x), rows, cols, round, seed, had,
-                                  mask, codes, scales, st)
+                                  mask, codes, scales, st, sld)
                : launch_quant_row(static_cast<const float*>(x), rows, cols, round, seed, had, mask,
-                                  codes, scales, st);
+                                  codes, scales, st, sld);
   }
   return dtype == MX_BF16
              ? launch_quant_tile<uint16_t, false>(static_cast<const uint16_t*>(x), rows, cols, round,
                                                   0, seed, had, mask, nullptr, nullptr, codes,
-                                                  scales, st)
+                                                  scales, st, plain_segs(), 0, sld)
              : launch_quant_tile<float, false>(static_cast<const float*>(x), rows, cols, round, 0,
-                                               seed, had, mask, nullptr, nullptr, codes, scales, st);
+                                               seed, had, mask, nullptr, nullptr, codes, scales, st,
+                                               plain_segs(), 0, sld);
 }
 
 static int launch_requant_jobs(const RqJob& j0, const RqJob& j1, int ty0, int ty1, int64_t cols,
@@ -981,6 +998,25 @@ extern "C" int mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols,
   MX_REQUIRE(aligned16(x) && aligned16(codes), MX_ERR_ALIGN);
   return quantize_impl(x, dtype, rows, cols, axis, round, seed, hadamard, sign_mask, codes, scales,
                        as_stream(stream));
+}
+
+extern "C" int mx_quantize_ld(const void* x, int dtype, int64_t rows, int64_t cols, int axis,
+                              int round, uint64_t seed, int hadamard, uint32_t sign_mask,
+                              uint8_t* codes, uint8_t* scales, int64_t scale_ld, void* stream) {
+  MX_REQUIRE(dtype == MX_F32 || dtype == MX_BF16, MX_ERR_ENUM);
+  MX_REQUIRE(axis == MX_ROW || axis == MX_COL, MX_ERR_ENUM);
+  MX_REQUIRE(round == MX_RNE || round == MX_SR, MX_ERR_ENUM);
+  MX_REQUIRE(hadamard == 0 || hadamard == 1, MX_ERR_ENUM);
+  MX_REQUIRE(rows >= 0 && cols >= 0, MX_ERR_SHAPE);
+  if (axis == MX_ROW) MX_REQUIRE(cols % 32 == 0, MX_ERR_SHAPE);
+  else MX_REQUIRE(rows % 32 == 0 && cols % 8 == 0, MX_ERR_SHAPE);
+  MX_REQUIRE(scale_ld >= (axis == MX_ROW ? cols : rows) / 32, MX_ERR_SHAPE);
+  if (rows == 0 || cols == 0) return MX_OK;
+  MX_REQUIRE(x && codes && scales, MX_ERR_NULL);
+  MX_REQUIRE(aligned16(x) && aligned16(codes), MX_ERR_ALIGN);
+  const int64_t nb = (axis == MX_ROW ? cols : rows) / 32;  // blocks per output row
+  return quantize_impl(x, dtype, rows, cols, axis, round, seed, hadamard, sign_mask, codes, scales,
+                       as_stream(stream), scale_ld == nb ? 0 : scale_ld);
 }
 
 extern "C" int mx_quantize_pair(const void* x0, int64_t rows0, const void* x1, int64_t rows1,

@@ -29,6 +29,7 @@ _P = _c_void_p
 SIGNATURES = {
     "mx_status_string": ([_i32], ctypes.c_char_p),
     "mx_quantize": ([_P, _i32, _i64, _i64, _i32, _i32, _u64, _i32, _u32, _P, _P, _P], _i32),
+    "mx_quantize_ld": ([_P, _i32, _i64, _i64, _i32, _i32, _u64, _i32, _u32, _P, _P, _i64, _P], _i32),
     "mx_quantize_dual": ([_P, _i32, _i64, _i64, _i32, _u64, _u64, _P, _P, _P, _P, _P], _i32),
     "mx_requantize": ([_P, _P, _i64, _i64, _i32, _u64, _P, _P, _P], _i32),
     "mx_quantize_pair": ([_P, _i64, _P, _i64, _i64, _i32, _i32, _u64, _u64, _i32, _u32,
@@ -43,6 +44,8 @@ SIGNATURES = {
     "mx_dequantize": ([_P, _P, _i64, _i64, _i32, _i32, _u32, _P, _i32, _P], _i32),
     "mx_gemm": ([_P, _P, _P, _P, _i64, _i64, _i64, _f32, _P, _i64, _P], _i32),
     "mx_gemm_grouped": ([_P, _P, _P, _P, _P, _i64, _i64, _i64, _f32, _P, _P], _i32),
+    "mx_gemm_ld": ([_P, _P, _i64, _P, _P, _i64, _i64, _i64, _i64, _f32, _P, _i64, _P], _i32),
+    "mx_gemm_grouped_ld": ([_P, _P, _i64, _P, _P, _i64, _P, _i64, _i64, _i64, _f32, _P, _P], _i32),
     "mx_linear_fwd": ([_P, _P, _i32, _i64, _i64, _i64, _P, _P, _P, _P, _P, _P], _i32),
     "mx_linear_bwd_workspace_size": ([_i64, _i64, _i64], _sz),
     "mx_linear_bwd": ([_P, _i32, _i64, _i64, _i64, _P, _P, _P, _P, _u64, _P, _P, _P, _sz, _P], _i32),
@@ -125,6 +128,13 @@ def mx_quantize(x, dtype, rows, cols, axis, round, seed, hadamard, sign_mask, co
                                             _stream(stream)))
 
 
+def mx_quantize_ld(x, dtype, rows, cols, axis, round, seed, hadamard, sign_mask, codes, scales,
+                   scale_ld, stream=None):
+    _check("mx_quantize_ld", lib().mx_quantize_ld(_ptr(x), dtype, rows, cols, axis, round, seed,
+                                                  hadamard, sign_mask, _ptr(codes), _ptr(scales),
+                                                  scale_ld, _stream(stream)))
+
+
 def mx_quantize_dual(x, dtype, rows, cols, round, seed_row, seed_col, codes_row, scales_row,
                      codes_col, scales_col, stream=None):
     _check("mx_quantize_dual", lib().mx_quantize_dual(
@@ -180,6 +190,13 @@ def mx_gemm(a_codes, a_scales, b_codes, b_scales, M, N, K, alpha, c, ldc, stream
                                     M, N, K, alpha, _ptr(c), ldc, _stream(stream)))
 
 
+def mx_gemm_ld(a_codes, a_scales, a_scale_ld, b_codes, b_scales, b_scale_ld, M, N, K, alpha, c,
+               ldc, stream=None):
+    _check("mx_gemm_ld", lib().mx_gemm_ld(_ptr(a_codes), _ptr(a_scales), a_scale_ld,
+                                          _ptr(b_codes), _ptr(b_scales), b_scale_ld, M, N, K,
+                                          alpha, _ptr(c), ldc, _stream(stream)))
+
+
 def _offsets(offs):
     """Host int64 array of the offsets (kept alive by the caller's reference)."""
     return (ctypes.c_int64 * len(offs))(*[int(o) for o in offs])
@@ -226,6 +243,14 @@ def mx_gemm_grouped(a_codes, a_scales, b_codes, b_scales, offs, groups, N, K, al
     _check("mx_gemm_grouped", lib().mx_gemm_grouped(
         _ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), ctypes.addressof(arr),
         groups, N, K, alpha, _ptr(c), _stream(stream)))
+
+
+def mx_gemm_grouped_ld(a_codes, a_scales, a_scale_ld, b_codes, b_scales, b_scale_ld, offs, groups,
+                       N, K, alpha, c, stream=None):
+    arr = _offsets(offs)
+    _check("mx_gemm_grouped_ld", lib().mx_gemm_grouped_ld(
+        _ptr(a_codes), _ptr(a_scales), a_scale_ld, _ptr(b_codes), _ptr(b_scales), b_scale_ld,
+        ctypes.addressof(arr), groups, N, K, alpha, _ptr(c), _stream(stream)))
 
 
 def mx_linear_fwd(x, w, dtype, M, N, K, y, xq_codes, xq_scales, wq_codes, wq_scales, stream=None):

@@ -118,6 +118,31 @@ def test_grouped_gemm_validation(L):
     assert gg(GOOD, GOOD, GOOD, GOOD, ctypes.addressof(big), 199, 8, 64, 1.0, GOOD, None) == mx.MX_ERR_SHAPE
 
 
+def test_pitched_entry_points_validation(L):
+    """The scale-pitch variants reject a pitch below the blocks per row, then
+    validate like their packed counterparts."""
+    q = L.mx_quantize_ld
+    assert q(GOOD, mx.MX_F32, 64, 128, mx.MX_ROW, 0, 0, 0, 0, GOOD, GOOD, 3, None) == mx.MX_ERR_SHAPE
+    assert q(GOOD, mx.MX_F32, 64, 128, mx.MX_COL, 0, 0, 0, 0, GOOD, GOOD, 1, None) == mx.MX_ERR_SHAPE
+    assert q(GOOD, mx.MX_F32, 64, 100, mx.MX_ROW, 0, 0, 0, 0, GOOD, GOOD, 16, None) == mx.MX_ERR_SHAPE
+    assert q(GOOD, 7, 64, 128, mx.MX_ROW, 0, 0, 0, 0, GOOD, GOOD, 16, None) == mx.MX_ERR_ENUM
+    assert q(GOOD, mx.MX_F32, 64, 128, mx.MX_ROW, 0, 0, 0, 0, None, GOOD, 16, None) == mx.MX_ERR_NULL
+    assert q(BAD, mx.MX_F32, 64, 128, mx.MX_ROW, 0, 0, 0, 0, GOOD, GOOD, 16, None) == mx.MX_ERR_ALIGN
+    assert q(None, mx.MX_F32, 0, 128, mx.MX_ROW, 0, 0, 0, 0, None, None, 16, None) == mx.MX_OK
+    g = L.mx_gemm_ld
+    assert g(GOOD, GOOD, 1, GOOD, GOOD, 2, 4, 4, 64, 1.0, GOOD, 4, None) == mx.MX_ERR_SHAPE  # a_scale_ld < K/32
+    assert g(GOOD, GOOD, 2, GOOD, GOOD, 1, 4, 4, 64, 1.0, GOOD, 4, None) == mx.MX_ERR_SHAPE  # b_scale_ld < K/32
+    assert g(GOOD, GOOD, 16, GOOD, GOOD, 16, 4, 4, 48, 1.0, GOOD, 4, None) == mx.MX_ERR_SHAPE
+    assert g(GOOD, None, 16, GOOD, GOOD, 16, 4, 4, 64, 1.0, GOOD, 4, None) == mx.MX_ERR_NULL
+    assert g(GOOD, GOOD, 16, GOOD, GOOD, 16, 4, 4, 64, 1.0, BAD, 4, None) == mx.MX_ERR_ALIGN
+    ok = (ctypes.c_int64 * 3)(0, 10, 20)
+    gg = L.mx_gemm_grouped_ld
+    assert gg(GOOD, GOOD, 1, GOOD, GOOD, 16, ctypes.addressof(ok), 2, 8, 64, 1.0, GOOD, None) == mx.MX_ERR_SHAPE
+    assert gg(GOOD, GOOD, 16, GOOD, GOOD, 16, None, 2, 8, 64, 1.0, GOOD, None) == mx.MX_ERR_NULL
+    bad = (ctypes.c_int64 * 3)(0, 10, 5)
+    assert gg(GOOD, GOOD, 16, GOOD, GOOD, 16, ctypes.addressof(bad), 2, 8, 64, 1.0, GOOD, None) == mx.MX_ERR_SHAPE
+
+
 def test_linear_validation_and_workspace_size(L):
     need = L.mx_linear_bwd_workspace_size(8192, 14336, 4096)
     packed = 0.53125
