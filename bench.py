@@ -38,8 +38,8 @@ PEAK_FP4_TFLOPS = 10100.0
 # from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB copy, valid for
 # the GEMM code with this sha256 only (of the source with comments and blank
 # lines removed; the per-launch table is kept with the committed profiles).
-GEMM_TRAFFIC = {"sha256": "1e395003d5435e1dcc843ebe591fb4509d8412d74dee6bbd4d699ac9e81e69f0",
-                "bytes_per_launch": 676917057}
+GEMM_TRAFFIC = {"sha256": "5fe42b3fe449f8c69407895eef918a1614c2ad7667658aa1de260c97ddd3bda6",
+                "bytes_per_launch": 676972389}
 
 
 def gemm_code_sha256(path):
