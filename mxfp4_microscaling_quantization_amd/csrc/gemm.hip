@@ -49,16 +49,23 @@ struct GemmGroups {
   int64_t row_off[MX_MAX_GROUPS + 1];       // rows of A / C per group
 };
 
-// Contraction ranges: split s of n covers K-values [kbeg[s], kbeg[s+1]) (each
-// start a multiple of 128) and writes its own output at C + s c_stride, alpha
-// applied per split.  Used for split-K (partial sums added afterwards) and for
-// the experts' weight gradients (each over its own token range).
+// Contraction ranges: split s of n covers K-values [kbeg[s], kbeg[s] + klen[s])
+// (each start a multiple of 128, each length a multiple of 32) and writes its
+// own output at C + s c_stride, alpha applied per split.  Used for split-K
+// (partial sums added afterwards) and for the experts' weight gradients (each
+// over its own token range; a range may end before the next one starts).
 struct GemmSplit {
   int n;
   int stream_c;                       // 1: final outputs, stored non-temporally
   int64_t c_stride;                   // elements between the splits' outputs
   int64_t kbeg[MX_MAX_GROUPS + 1];
+  int32_t klen[MX_MAX_GROUPS];        // range lengths (kbeg[s+1] - kbeg[s] when contiguous)
 };
+
+// Contiguous ranges: split s ends where split s+1 begins.
+static void contiguous_ranges(GemmSplit& sp) {
+  for (int s = 0; s < sp.n; ++s) sp.klen[s] = (int32_t)(sp.kbeg[s + 1] - sp.kbeg[s]);
+}
 
 // A second, plain problem in the same launch (one group, the whole contraction,
 // a final output): workgroups past the first problem's take its tiles.  Two
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
     grows = gg.row_off[g + 1] - grow0;
     a_last = gg.row_off[gg.ngroups] - 1;  // last row of A in memory
     k0 = sp.kbeg[split];
-    k1 = sp.kbeg[split + 1];
+    k1 = k0 + sp.klen[split];
   }
   const uint8_t* __restrict__ A = second ? p1.A : A0;
   const uint8_t* __restrict__ SA = second ? p1.SA : SA0;
@@ -687,6 +694,7 @@ static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
                        float* c, int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales,
                        int64_t lds_a, int64_t lds_b, GemmSplit sp, hipStream_t st,
                        const GemmPlain* p1 = nullptr) {
+  if (K > INT32_MAX) return MX_ERR_SHAPE;  // range lengths are 32-bit
   int64_t tiles256 = 0;
   for (int64_t g = 0; g < groups; ++g) tiles256 += cdiv(offs[g + 1] - offs[g], 256) * cdiv(N, 256);
   int sc = scale_mode(sa, sb, lds_a, lds_b, b_stride_scales, sp);
@@ -709,7 +717,7 @@ static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
   // at most three K-steps in every range: the short-contraction variant (three
   // stages, three workgroups per CU); group-mode scales need K % 512 == 0
   int64_t klen = 0;
-  for (int s = 0; s < sp.n; ++s) klen = klen > sp.kbeg[s + 1] - sp.kbeg[s] ? klen : sp.kbeg[s + 1] - sp.kbeg[s];
+  for (int s = 0; s < sp.n; ++s) klen = klen > sp.klen[s] ? klen : sp.klen[s];
   if (!p1 && klen <= 3 * 128 && sc != kScGroup) {
     if (sc == kScDword) return launch_gemm<128, 128, 2, 2, kScDword, 3>(MX_GEMM_ARGS);
     if (sc == kScShort) return launch_gemm<128, 128, 2, 2, kScShort, 3>(MX_GEMM_ARGS);
@@ -733,6 +741,7 @@ int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8
   one.stream_c = 1;
   one.kbeg[0] = 0;
   one.kbeg[1] = K;
+  contiguous_ranges(one);
   return gemm_launch(a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes,
                      b_stride_scales, lds_a, lds_b, one, st);
 }
@@ -786,6 +795,7 @@ int gemm_split_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const
   sp.stream_c = 0;  // partial sums, read back by k_splitk_sum
   sp.c_stride = M * N;
   for (int i = 0; i <= plan.n; ++i) sp.kbeg[i] = hmin((int64_t)i * plan.kchunk, K);
+  contiguous_ranges(sp);
   int s = gemm_launch(a, sa, b, sb, offs, 1, N, K, 1.0f, part, N, 0, 0, lds_a, lds_b, sp, st);
   if (s != MX_OK) return s;
   const int64_t n4 = M * (N / 4);
@@ -820,6 +830,7 @@ int gemm_pair_impl(const uint8_t* a0, const uint8_t* sa0, const uint8_t* b0, con
     sp.stream_c = 1;
     sp.kbeg[0] = 0;
     sp.kbeg[1] = K0;
+    contiguous_ranges(sp);
     return gemm_launch(a0, sa0, b0, sb0, offs, 1, N0, K0, alpha0, c0, ldc0, 0, 0, lds_a0, lds_b0,
                        sp, st, &p1);
   }
@@ -827,6 +838,7 @@ int gemm_pair_impl(const uint8_t* a0, const uint8_t* sa0, const uint8_t* b0, con
   sp.stream_c = 0;  // partial sums, read back by k_splitk_sum
   sp.c_stride = M0 * N0;
   for (int i = 0; i <= plan0.n; ++i) sp.kbeg[i] = hmin((int64_t)i * plan0.kchunk, K0);
+  contiguous_ranges(sp);
   int s = gemm_launch(a0, sa0, b0, sb0, offs, 1, N0, K0, 1.0f, part0, N0, 0, 0, lds_a0, lds_b0,
                       sp, st, &p1);
   if (s != MX_OK) return s;
@@ -836,17 +848,21 @@ int gemm_pair_impl(const uint8_t* a0, const uint8_t* sa0, const uint8_t* b0, con
   return launch_status();
 }
 
-// C_s [M][N] = alpha * A[:, kbeg[s]:kbeg[s+1]] . B[:, kbeg[s]:kbeg[s+1]]^T for
-// s < n, written at c + s * M * N (A [M, K], B [N, K] packed along K; each kbeg
-// a multiple of 128; an empty range writes zeros).
+// C_s [M][N] = alpha * A[:, kbeg[s]:kbeg[s] + klen[s]] . B[:, same]^T for s < n,
+// written at c + s * M * N (A [M, K], B [N, K] packed along K; each kbeg a
+// multiple of 128, each klen a multiple of 32, klen null: the ranges end where
+// the next begins; an empty range writes zeros).
 int gemm_ranges_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
-                     int64_t M, int64_t N, int64_t K, const int64_t* kbeg, int n, float alpha,
-                     float* c, int64_t lds_a, int64_t lds_b, hipStream_t st) {
+                     int64_t M, int64_t N, int64_t K, const int64_t* kbeg, const int64_t* klen,
+                     int n, float alpha, float* c, int64_t lds_a, int64_t lds_b, hipStream_t st) {
   GemmSplit sp{};
   sp.n = n;
   sp.stream_c = 1;
   sp.c_stride = M * N;
   for (int i = 0; i <= n; ++i) sp.kbeg[i] = kbeg[i];
+  contiguous_ranges(sp);
+  if (klen)
+    for (int i = 0; i < n; ++i) sp.klen[i] = (int32_t)klen[i];
   const int64_t offs[2] = {0, M};
   return gemm_launch(a, sa, b, sb, offs, 1, N, K, alpha, c, N, 0, 0, lds_a, lds_b, sp, st);
 }
@@ -860,7 +876,7 @@ extern "C" int mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const ui
                        float* c, int64_t ldc, void* stream) {
   MX_REQUIRE(M >= 0 && N >= 0 && K >= 0 && K % 32 == 0, MX_ERR_SHAPE);
   MX_REQUIRE(ldc >= N && ldc % 4 == 0, MX_ERR_SHAPE);
-  MX_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31, MX_ERR_SHAPE);
+  MX_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31 && K <= INT32_MAX, MX_ERR_SHAPE);
   if (M == 0 || N == 0) return MX_OK;
   MX_REQUIRE(c, MX_ERR_NULL);
   if (K > 0) MX_REQUIRE(a_codes && a_scales && b_codes && b_scales, MX_ERR_NULL);
@@ -878,7 +894,7 @@ extern "C" int mx_gemm_ld(const uint8_t* a_codes, const uint8_t* a_scales, int64
   MX_REQUIRE(M >= 0 && N >= 0 && K >= 0 && K % 32 == 0, MX_ERR_SHAPE);
   MX_REQUIRE(ldc >= N && ldc % 4 == 0, MX_ERR_SHAPE);
   MX_REQUIRE(a_scale_ld >= K / 32 && b_scale_ld >= K / 32, MX_ERR_SHAPE);
-  MX_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31, MX_ERR_SHAPE);
+  MX_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31 && K <= INT32_MAX, MX_ERR_SHAPE);
   if (M == 0 || N == 0) return MX_OK;
   MX_REQUIRE(c, MX_ERR_NULL);
   if (K > 0) MX_REQUIRE(a_codes && a_scales && b_codes && b_scales, MX_ERR_NULL);
@@ -901,7 +917,7 @@ extern "C" int mx_gemm_grouped_ld(const uint8_t* a_codes, const uint8_t* a_scale
   MX_REQUIRE(offs[0] == 0, MX_ERR_SHAPE);
   for (int64_t g = 0; g < groups; ++g) MX_REQUIRE(offs[g + 1] >= offs[g], MX_ERR_SHAPE);
   const int64_t M = offs[groups];
-  MX_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31, MX_ERR_SHAPE);
+  MX_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31 && K <= INT32_MAX, MX_ERR_SHAPE);
   if (M == 0 || N == 0) return MX_OK;
   MX_REQUIRE(c, MX_ERR_NULL);
   if (K > 0) MX_REQUIRE(a_codes && a_scales && b_codes && b_scales, MX_ERR_NULL);
@@ -921,7 +937,7 @@ extern "C" int mx_gemm_grouped(const uint8_t* a_codes, const uint8_t* a_scales,
   MX_REQUIRE(offs[0] == 0, MX_ERR_SHAPE);
   for (int64_t g = 0; g < groups; ++g) MX_REQUIRE(offs[g + 1] >= offs[g], MX_ERR_SHAPE);
   const int64_t M = offs[groups];
-  MX_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31, MX_ERR_SHAPE);
+  MX_REQUIRE(M <= (int64_t)1 << 31 && N <= (int64_t)1 << 31 && K <= INT32_MAX, MX_ERR_SHAPE);
   if (M == 0 || N == 0) return MX_OK;
   MX_REQUIRE(c, MX_ERR_NULL);
   if (K > 0) MX_REQUIRE(a_codes && a_scales && b_codes && b_scales, MX_ERR_NULL);

@@ -51,8 +51,8 @@ int gemm_pair_impl(const uint8_t* a0, const uint8_t* sa0, const uint8_t* b0, con
                    int64_t M1, int64_t N1, int64_t K1, float alpha1, float* c1, int64_t ldc1,
                    int64_t lds_a1, int64_t lds_b1, hipStream_t st);
 int gemm_ranges_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
-                     int64_t M, int64_t N, int64_t K, const int64_t* kbeg, int n, float alpha,
-                     float* c, int64_t lds_a, int64_t lds_b, hipStream_t st);
+                     int64_t M, int64_t N, int64_t K, const int64_t* kbeg, const int64_t* klen,
+                     int n, float alpha, float* c, int64_t lds_a, int64_t lds_b, hipStream_t st);
 int requantize_batched_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t batch,
                             int64_t rows, int64_t cols, int round, uint64_t seed, uint8_t* codes,
                             uint8_t* scales, hipStream_t st, int64_t s_pitch);
@@ -60,13 +60,13 @@ int quantize_dual_segments_impl(const void* x, int dtype, int64_t rows, int64_t 
                                 const int64_t* offs, int64_t groups, int round, uint64_t seed_row,
                                 uint64_t seed_col, uint8_t* codes_row, uint8_t* scales_row,
                                 uint8_t* codes_col, uint8_t* scales_col, hipStream_t st,
-                                int64_t sp_row, int64_t sp_col);
+                                int64_t sp_row, int64_t sp_col, int64_t pad);
 int requantize_segments_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
                              int64_t cols, const int64_t* offs, int64_t groups, int round,
                              uint64_t seed, uint8_t* codes, uint8_t* scales, hipStream_t st,
-                             int64_t s_pitch);
-int64_t segments_padded_rows(const int64_t* offs, int64_t groups);
-void segments_padded_offsets(const int64_t* offs, int64_t groups, int64_t* out);
+                             int64_t s_pitch, int64_t pad);
+int64_t segments_padded_rows(const int64_t* offs, int64_t groups, int64_t pad);
+void segments_padded_offsets(const int64_t* offs, int64_t groups, int64_t* out, int64_t pad);
 
 static size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -110,7 +110,13 @@ static BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K) {
 
 // Grouped (mixture-of-experts) backward workspace: Q3 [R][N], the experts'
 // Q4 [E][K][N], Q5 [N][P] and Q6 [K][P] packed, P = the padded token axis;
-// scale rows p3..p6 bytes apart.
+// scale rows p3..p6 bytes apart.  Each expert's token segment starts at a
+// multiple of 512 positions of P, so its dW product loads the scales of four
+// K-steps at once (16 bytes per row); the positions past the segment's rows
+// rounded up to the quantizers' tile height are never written, and the product
+// stops at its rows rounded up to 32.
+constexpr int64_t kExpertSegPad = 512;
+
 struct GroupedLayout {
   size_t q3c, q3s, q4c, q4s, q5c, q5s, q6c, q6s, total;
   int64_t P, p3, p4, p5, p6;
@@ -119,7 +125,7 @@ struct GroupedLayout {
 static GroupedLayout grouped_layout(const int64_t* offs, int64_t E, int64_t N, int64_t K) {
   GroupedLayout L;
   const int64_t R = offs[E];
-  L.P = segments_padded_rows(offs, E);
+  L.P = segments_padded_rows(offs, E, kExpertSegPad);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -300,18 +306,19 @@ extern "C" int mx_grouped_linear_bwd(const void* dy, int dtype, const int64_t* o
     // from one read of dY
     s = quantize_dual_segments_impl(dy, dtype, R, N, offs, E, MX_SR, seed + 3, seed + 5,
                                     ws + L.q3c, ws + L.q3s, ws + L.q5c, ws + L.q5s, st, L.p3,
-                                    L.p5);
+                                    L.p5, kExpertSegPad);
     if (s != MX_OK) return s;
     s = requantize_segments_impl(xq_codes, xq_scales, R, K, offs, E, MX_SR, seed + 6, ws + L.q6c,
-                                 ws + L.q6s, st, L.p6);
+                                 ws + L.q6s, st, L.p6, kExpertSegPad);
     if (s != MX_OK) return s;
     s = gemm_impl(ws + L.q3c, ws + L.q3s, ws + L.q4c, ws + L.q4s, offs, E, K, N, 1.0f, dx, K,
                   K * N / 2, K * L.p4, L.p3, L.p4, st);
     if (s != MX_OK) return s;
   }
-  int64_t kbeg[MX_MAX_GROUPS + 1];
-  segments_padded_offsets(offs, E, kbeg);
-  return gemm_ranges_impl(ws + L.q5c, ws + L.q5s, ws + L.q6c, ws + L.q6s, N, K, L.P, kbeg, (int)E,
+  int64_t kbeg[MX_MAX_GROUPS + 1], klen[MX_MAX_GROUPS];
+  segments_padded_offsets(offs, E, kbeg, kExpertSegPad);
+  for (int64_t e = 0; e < E; ++e) klen[e] = (offs[e + 1] - offs[e] + 31) / 32 * 32;
+  return gemm_ranges_impl(ws + L.q5c, ws + L.q5s, ws + L.q6c, ws + L.q6s, N, K, L.P, kbeg, klen, (int)E,
                           1.0f, dw, L.p5, L.p6, st);
 }
 

@@ -158,6 +158,9 @@ __global__ __launch_bounds__(256) void k_quant_row(const RowJobs<T> jobs, uint32
 // start at the segment's first row and its tail is zero-padded to a multiple
 // of kSegPad rows, so the transposed output has a padded row axis of out_len
 // positions, segment g's starting at out_off[g].  n == 0: one plain segment.
+// A caller may space the segments further apart (a multiple of kSegPad rows and
+// of the tile heights): the kernels then write each segment's first
+// round-up(rows, tile height) positions and leave the rest of its space alone.
 constexpr int kSegPad = 128;
 
 struct Segs {
@@ -716,7 +719,7 @@ static Segs plain_segs() {
 }
 
 // Segments of tile height TR over the row offsets offs[0..groups] (host array).
-static Segs make_segs(const int64_t* offs, int64_t groups, int TR) {
+static Segs make_segs(const int64_t* offs, int64_t groups, int TR, int64_t pad = kSegPad) {
   Segs s{};
   s.n = (int)groups;
   s.tile_start[0] = 0;
@@ -725,7 +728,7 @@ static Segs make_segs(const int64_t* offs, int64_t groups, int TR) {
     const int64_t n = offs[g + 1] - offs[g];
     s.row_off[g] = offs[g];
     s.tile_start[g + 1] = s.tile_start[g] + (int)cdiv(n, TR);
-    s.out_off[g + 1] = s.out_off[g] + cdiv(n, kSegPad) * kSegPad;
+    s.out_off[g + 1] = s.out_off[g] + cdiv(n, pad) * pad;
   }
   s.row_off[groups] = offs[groups];
   s.out_len = s.out_off[groups];
@@ -733,15 +736,16 @@ static Segs make_segs(const int64_t* offs, int64_t groups, int TR) {
 }
 
 // Start of each segment on the padded row axis (out[0..groups], out[groups] = total).
-void segments_padded_offsets(const int64_t* offs, int64_t groups, int64_t* out) {
+// pad: segment spacing, a multiple of 256 rows when not kSegPad.
+void segments_padded_offsets(const int64_t* offs, int64_t groups, int64_t* out,
+                             int64_t pad = kSegPad) {
   out[0] = 0;
-  for (int64_t g = 0; g < groups; ++g)
-    out[g + 1] = out[g] + cdiv(offs[g + 1] - offs[g], kSegPad) * kSegPad;
+  for (int64_t g = 0; g < groups; ++g) out[g + 1] = out[g] + cdiv(offs[g + 1] - offs[g], pad) * pad;
 }
 
-int64_t segments_padded_rows(const int64_t* offs, int64_t groups) {
+int64_t segments_padded_rows(const int64_t* offs, int64_t groups, int64_t pad = kSegPad) {
   int64_t p = 0;
-  for (int64_t g = 0; g < groups; ++g) p += cdiv(offs[g + 1] - offs[g], kSegPad) * kSegPad;
+  for (int64_t g = 0; g < groups; ++g) p += cdiv(offs[g + 1] - offs[g], pad) * pad;
   return p;
 }
 
@@ -902,9 +906,9 @@ int quantize_dual_segments_impl(const void* x, int dtype, int64_t rows, int64_t 
                                 const int64_t* offs, int64_t groups, int round, uint64_t seed_row,
                                 uint64_t seed_col, uint8_t* codes_row, uint8_t* scales_row,
                                 uint8_t* codes_col, uint8_t* scales_col, hipStream_t st,
-                                int64_t sp_row = 0, int64_t sp_col = 0) {
+                                int64_t sp_row = 0, int64_t sp_col = 0, int64_t pad = kSegPad) {
   if (rows == 0 || cols == 0) return MX_OK;
-  const Segs s = make_segs(offs, groups, kTileR);
+  const Segs s = make_segs(offs, groups, kTileR, pad);
   return dtype == MX_BF16
              ? launch_quant_tile<uint16_t, true>(static_cast<const uint16_t*>(x), rows, cols, round,
                                                  seed_row, seed_col, 0, 0, codes_row, scales_row,
@@ -917,10 +921,10 @@ int quantize_dual_segments_impl(const void* x, int dtype, int64_t rows, int64_t 
 int requantize_segments_impl(const uint8_t* codes_in, const uint8_t* scales_in, int64_t rows,
                              int64_t cols, const int64_t* offs, int64_t groups, int round,
                              uint64_t seed, uint8_t* codes, uint8_t* scales, hipStream_t st,
-                             int64_t s_pitch = 0) {
+                             int64_t s_pitch = 0, int64_t pad = kSegPad) {
   if (rows == 0 || cols == 0) return MX_OK;
   return launch_requant(codes_in, scales_in, rows, cols, round, seed, codes, scales, 1,
-                        make_segs(offs, groups, kRqR), st, s_pitch);
+                        make_segs(offs, groups, kRqR, pad), st, s_pitch);
 }
 
 // sp_row / sp_col: bytes between scale rows of the row-blocked [rows][cols/32]
