@@ -208,7 +208,8 @@ int mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int
  *  A: packed MX_ROW [M, K] (a_codes [M][K/2], a_scales [M][K/32]);
  *  B: packed MX_ROW [N, K] (b_codes [N][K/2], b_scales [N][K/32]);
  *  C: float32 row-major, leading dimension ldc >= N (ldc % 4 == 0), overwritten.
- *  K % 32 == 0; M, N >= 0 (M or N == 0: no-op; K == 0: C = 0).
+ *  K % 32 == 0; M, N >= 0 (M or N == 0: no-op; K == 0: C = 0); M, N <= 2^31 and
+ *  K < 2^31, else MX_ERR_SHAPE (the same bounds hold for every GEMM call below).
  *  Products of FP4 values and E8M0 scales are exact; sums are float32 in an
  *  unspecified order (error <= ~K/64 * 2^-24 * sum |a b|). */
 int mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales,

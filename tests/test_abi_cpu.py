@@ -103,6 +103,7 @@ def test_gemm_validation(L):
     assert g(GOOD, GOOD, GOOD, GOOD, 4, 6, 64, 1.0, GOOD, 6, None) == mx.MX_ERR_SHAPE   # ldc % 4
     assert g(GOOD, None, GOOD, GOOD, 4, 4, 64, 1.0, GOOD, 4, None) == mx.MX_ERR_NULL
     assert g(GOOD, GOOD, GOOD, GOOD, 4, 4, 64, 1.0, BAD, 4, None) == mx.MX_ERR_ALIGN
+    assert g(GOOD, GOOD, GOOD, GOOD, 4, 4, 1 << 31, 1.0, GOOD, 4, None) == mx.MX_ERR_SHAPE  # K > 2^31 - 1
     assert g(None, None, None, None, 0, 4, 64, 1.0, None, 4, None) == mx.MX_OK
 
 
@@ -114,6 +115,7 @@ def test_grouped_gemm_validation(L):
     assert gg(GOOD, GOOD, GOOD, GOOD, ctypes.addressof(ok), 0, 8, 64, 1.0, GOOD, None) == mx.MX_ERR_SHAPE
     assert gg(GOOD, GOOD, GOOD, GOOD, ctypes.addressof(ok), 2, 6, 64, 1.0, GOOD, None) == mx.MX_ERR_SHAPE
     assert gg(GOOD, GOOD, GOOD, GOOD, None, 2, 8, 64, 1.0, GOOD, None) == mx.MX_ERR_NULL
+    assert gg(GOOD, GOOD, GOOD, GOOD, ctypes.addressof(ok), 2, 8, 1 << 31, 1.0, GOOD, None) == mx.MX_ERR_SHAPE
     big = (ctypes.c_int64 * 200)(*range(200))
     assert gg(GOOD, GOOD, GOOD, GOOD, ctypes.addressof(big), 199, 8, 64, 1.0, GOOD, None) == mx.MX_ERR_SHAPE
 

@@ -96,6 +96,21 @@ def test_grouped_linear_bwd_matches_oracle(dtype):
     check_grouped_bwd(dy, dtype, xq, wq, OFFS, N, K, seed=9)
 
 
+def test_grouped_linear_bwd_long_segments_matches_oracle():
+    """Experts of 700, 0, 600, 783 and 33 tokens: each expert's dW contraction spans
+    several 512-position scale groups and ends inside one, the next expert's starts at
+    the following multiple of 512; every output checked."""
+    rng = np.random.default_rng(47)
+    offs = [0, 700, 700, 1300, 2083, 2116]
+    E, N, K = len(offs) - 1, 96, 160
+    R = offs[-1]
+    x = rng.standard_normal((R, K)).astype(np.float32)
+    w = (rng.standard_normal((E * N, K)) * 0.02).astype(np.float32)
+    dy = synth.f32_to_bf16_bits((rng.standard_normal((R, N)) * 1e-3).astype(np.float32))
+    xq, wq = O.quantize(x, O.ROW, O.RNE), O.quantize(w, O.ROW, O.RNE)
+    check_grouped_bwd(dy, "bf16", xq, wq, offs, N, K, seed=12)
+
+
 def test_grouped_linear_bwd_single_expert_equals_dense_backward():
     """One expert with a 32-aligned token count is the dense layer: the same bits."""
     rng = np.random.default_rng(45)
