@@ -125,58 +125,70 @@ def test_grouped_linear_bwd_single_expert_equals_dense_backward():
     assert torch.equal(dw1, dw2[0])
 
 
-def test_grouped_linear_bwd_moe_down_projection_sampled():
-    """32 experts, top-4 routing of 16384 tokens, down projection 2880 -> 2880: dY
-    [65536, 2880] bf16 N(0, 1e-3); dX checked on sampled rows, dW on sampled rows of
-    sampled experts, each against the oracle's operands for exactly those outputs."""
+def check_moe_bwd_sampled(xin, N, K, n_experts, rng, seed):
+    """32 experts, top-4 routing of 16384 tokens: X [65536, K] bf16 (the layer's
+    input), W [32 N, K] fp32 N(0, 0.02), dY [65536, N] bf16 N(0, 1e-3).  dX checked on
+    sampled rows and dW on sampled rows of sampled experts, each against the oracle's
+    operands for exactly those outputs."""
     cfg = synth.moe_config(with_weights=False)
-    E, H = cfg["E"], cfg["hidden"]
+    E = cfg["E"]
     offs = [int(o) for o in cfg["offs"]]
     R = offs[-1]
-    rng = np.random.default_rng(46)
-    w = (rng.standard_normal((E * H, H)) * 0.02).astype(np.float32)
-    dy = synth.f32_to_bf16_bits((rng.standard_normal((R, H)) * 1e-3).astype(np.float32))
-    xin = cfg["x_down"]
+    w = (rng.standard_normal((E * N, K)) * 0.02).astype(np.float32)
+    dy = synth.f32_to_bf16_bits((rng.standard_normal((R, N)) * 1e-3).astype(np.float32))
     xq_d = mx.quantize(upload(xin, "bf16"))
     wq_d = mx.quantize(upload(w, "f32"))
-    seed = 4
-    gx, gw = mx.grouped_linear_bwd(upload(dy, "bf16"), xq_d, wq_d, offs, H, H, seed)
+    gx, gw = mx.grouped_linear_bwd(upload(dy, "bf16"), xq_d, wq_d, offs, N, K, seed)
     gx, gw = host(gx), host(gw)
     xq = (host(xq_d[0]), host(xq_d[1]))
     dyf = O.bf16_bits_to_f32(dy)
-    for e in rng.choice(E, 4, replace=False):
+    for e in rng.choice(E, n_experts, replace=False):
         r0, r1 = offs[e], offs[e + 1]
-        # Q4 of expert e: 32x1 along N of its [H, H] weight, stacked index
-        wdeq = O.dequantize(host(wq_d[0])[e * H:(e + 1) * H], host(wq_d[1])[e * H:(e + 1) * H],
-                            H, H).astype(np.float32)
-        idx4 = (e * H + np.arange(H))[None, :] * H + np.arange(H)[:, None]  # [k][n] -> (eH+n)H+k
-        c4, s4 = O.quantize_blocks(wdeq.T.reshape(H, H // 32, 32), idx4.reshape(H, H // 32, 32),
+        # Q4 of expert e: 32x1 along N of its [N, K] weight, stacked index
+        wdeq = O.dequantize(host(wq_d[0])[e * N:(e + 1) * N], host(wq_d[1])[e * N:(e + 1) * N],
+                            N, K).astype(np.float32)
+        idx4 = (e * N + np.arange(N))[None, :] * K + np.arange(K)[:, None]  # [k][n] -> (eN+n)K+k
+        c4, s4 = O.quantize_blocks(wdeq.T.reshape(K, N // 32, 32), idx4.reshape(K, N // 32, 32),
                                    O.SR, seed + 4)
-        q4 = (O.pack_codes(c4.reshape(H, H)), s4)
+        q4 = (O.pack_codes(c4.reshape(K, N)), s4)
         rows = np.sort(rng.choice(np.arange(r0, r1), 6, replace=False))
-        idx3 = rows[:, None] * H + np.arange(H)[None, :]
-        c3, s3 = O.quantize_blocks(dyf[rows].reshape(6, H // 32, 32), idx3.reshape(6, H // 32, 32),
+        idx3 = rows[:, None] * N + np.arange(N)[None, :]
+        c3, s3 = O.quantize_blocks(dyf[rows].reshape(6, N // 32, 32), idx3.reshape(6, N // 32, 32),
                                    O.SR, seed + 3)
-        q3 = (O.pack_codes(c3.reshape(6, H)), s3)
-        assert_gemm_close(gx[rows], O.gemm(*q3, *q4, 6, H, H), O.gemm_abs(*q3, *q4, 6, H, H),
+        q3 = (O.pack_codes(c3.reshape(6, N)), s3)
+        assert_gemm_close(gx[rows], O.gemm(*q3, *q4, 6, K, N), O.gemm_abs(*q3, *q4, 6, K, N),
                           f"dX expert {e}")
         # dW_e rows n: Q5 column n of dY_e, Q6 of the expert's Q_D(X) over its tokens
-        ns = np.sort(rng.choice(H, 6, replace=False))
-        # the segment blocks of the sampled columns, with the [R, H] element indices
+        ns = np.sort(rng.choice(N, 6, replace=False))
+        # the segment blocks of the sampled columns, with the [R, N] / [R, K] element indices
         n = r1 - r0
         P = (n + 31) // 32 * 32
         v = np.zeros((6, P), np.float32)
         v[:, :n] = dyf[r0:r1][:, ns].T
-        idx5 = (r0 + np.arange(P))[None, :] * H + ns[:, None]
+        idx5 = (r0 + np.arange(P))[None, :] * N + ns[:, None]
         c5, s5 = O.quantize_blocks(v.reshape(6, P // 32, 32), idx5.reshape(6, P // 32, 32), O.SR,
                                    seed + 5)
         q5 = (O.pack_codes(c5.reshape(6, P)), s5)
-        xdeq = O.dequantize(xq[0][r0:r1], xq[1][r0:r1], n, H).astype(np.float32)
-        vx = np.zeros((H, P), np.float32)
+        xdeq = O.dequantize(xq[0][r0:r1], xq[1][r0:r1], n, K).astype(np.float32)
+        vx = np.zeros((K, P), np.float32)
         vx[:, :n] = xdeq.T
-        idx6 = (r0 + np.arange(P))[None, :] * H + np.arange(H)[:, None]
-        c6, s6 = O.quantize_blocks(vx.reshape(H, P // 32, 32), idx6.reshape(H, P // 32, 32), O.SR,
+        idx6 = (r0 + np.arange(P))[None, :] * K + np.arange(K)[:, None]
+        c6, s6 = O.quantize_blocks(vx.reshape(K, P // 32, 32), idx6.reshape(K, P // 32, 32), O.SR,
                                    seed + 6)
-        q6 = (O.pack_codes(c6.reshape(H, P)), s6)
-        assert_gemm_close(gw[e][ns], O.gemm(*q5, *q6, 6, H, P), O.gemm_abs(*q5, *q6, 6, H, P),
+        q6 = (O.pack_codes(c6.reshape(K, P)), s6)
+        assert_gemm_close(gw[e][ns], O.gemm(*q5, *q6, 6, K, P), O.gemm_abs(*q5, *q6, 6, K, P),
                           f"dW expert {e}")
+
+
+def test_grouped_linear_bwd_moe_down_projection_sampled():
+    """Down projection 2880 -> 2880 (input: the routed hidden activations)."""
+    cfg = synth.moe_config(with_weights=False)
+    H = cfg["hidden"]
+    check_moe_bwd_sampled(cfg["x_down"], H, H, 4, np.random.default_rng(46), seed=4)
+
+
+def test_grouped_linear_bwd_moe_up_projection_sampled():
+    """Up projection 2880 -> 5760 (input: the routed tokens)."""
+    cfg = synth.moe_config(with_weights=False)
+    check_moe_bwd_sampled(cfg["x_up"], cfg["ffn"], cfg["hidden"], 2, np.random.default_rng(48),
+                          seed=6)

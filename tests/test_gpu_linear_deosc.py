@@ -141,6 +141,25 @@ def test_moe_grouped_forward_sampled():
             want = O.gemm(hx[0][rows], hx[1][rows], *owq, len(rows), n_out, H)
             ab = O.gemm_abs(hx[0][rows], hx[1][rows], *owq, len(rows), n_out, H)
             assert_gemm_close(got[rows], want, ab, f"{name} expert {e}")
+        # the same product on operands whose scale rows are 96 bytes apart (16-byte
+        # scale-group loads, eight waves per tile): every output bit for bit
+        ld = (H // 32 + 15) // 16 * 16
+        xl = pitched_quantize(upload(xin, "bf16"), H, ld)
+        wl = pitched_quantize(w_dev[r0:r0 + E * n_out], H, ld)
+        assert torch.equal(xl[0], xq[0]) and torch.equal(wl[0], wc)
+        assert torch.equal(xl[1][:, :H // 32], xq[1]) and torch.equal(wl[1][:, :H // 32], ws)
+        c2 = torch.empty_like(c)
+        mx.mx_gemm_grouped_ld(xl[0], xl[1], ld, wl[0], wl[1], ld, offs, E, n_out, H, 1.0, c2)
+        assert torch.equal(c2, c), f"{name}: pitched operands"
+
+
+def pitched_quantize(x, cols, ld):
+    """1x32 nearest-rounding quantization with scale rows ld bytes apart."""
+    rows = x.shape[0]
+    c = torch.empty((rows, cols // 2), dtype=torch.uint8, device=DEV)
+    s = torch.empty((rows, ld), dtype=torch.uint8, device=DEV)
+    mx.mx_quantize_ld(x, mx.dtype_code(x), rows, cols, mx.MX_ROW, mx.MX_RNE, 0, 0, 0, c, s, ld)
+    return c, s
 
 
 # ------------------------------------------------------------------ de-oscillation

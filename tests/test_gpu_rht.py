@@ -97,3 +97,47 @@ def test_linear_rht_deit_fc1_full():
     dW product is split along its 12608-long contraction."""
     cfg = synth.deit_config()
     check_linear_rht(cfg["x"], cfg["w"], cfg["dy"], "bf16", 1, 0x9E37_79B9)
+
+
+def test_linear_rht_llama_up_proj_sampled():
+    """Llama-3-8B up-projection (M=8192, K=4096, N=14336, bf16) through the rotated
+    layer, as the benchmark times it: the rotated operands Q_D(H X), Q_D(H W) and the
+    double quantizations Q4, Q6 in full, bit for bit; Y, dX and dW on 48 sampled rows
+    each, against the oracle's operands for exactly those rows (global SR indices)."""
+    cfg = synth.llama_config()
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    mask, seed = 0x9E37_79B9, 2
+    rng = np.random.default_rng(5)
+    xf, wf, dyf = (oracle_input(cfg[k], "bf16") for k in ("x", "w", "dy"))
+    y, xq, wq = mx.linear_fwd_rht(upload(cfg["x"], "bf16"), upload(cfg["w"], "bf16"), mask)
+    gx, gw = mx.linear_bwd_rht(upload(cfg["dy"], "bf16"), xq, wq, M, N, K, seed, mask)
+    oxq = O.quantize(xf, O.ROW, O.RNE, 0, True, mask)
+    owq = O.quantize(wf, O.ROW, O.RNE, 0, True, mask)
+    for got, want, what in zip(xq + wq, oxq + owq, ["xq codes", "xq scales", "wq codes", "wq scales"]):
+        assert_bytes_equal(host(got), want, what)
+    q4 = O.requantize_rht(*owq, N, K, O.SR, seed + 4, mask)
+    q6 = O.requantize_rht(*oxq, M, K, O.SR, seed + 6, mask)
+    for (c, s), rows, (wc, ws), what in ((wq, N, q4, "Q4"), (xq, M, q6, "Q6")):
+        co = torch.empty((K, rows // 2), dtype=torch.uint8, device=DEV)
+        so = torch.empty((K, rows // 32), dtype=torch.uint8, device=DEV)
+        sd = seed + (4 if what == "Q4" else 6)
+        mx.mx_requantize_rht(c, s, rows, K, mx.MX_SR, sd, mask, co, so)
+        assert_bytes_equal(host(co), wc, f"{what} codes")
+        assert_bytes_equal(host(so), ws, f"{what} scales")
+    a = O.HADAMARD_ALPHA
+    rows = np.sort(rng.choice(M, 48, replace=False))
+    nrows = np.sort(rng.choice(N, 48, replace=False))
+    ya = (oxq[0][rows], oxq[1][rows])
+    assert_gemm_close(host(y)[rows], O.gemm(*ya, *owq, 48, N, K, a),
+                      O.gemm_abs(*ya, *owq, 48, N, K, a), "Y")
+    idx3 = O.block_indices(M, N, O.ROW)[rows]
+    c3, s3 = O.quantize_blocks(dyf[rows].reshape(48, N // 32, 32), idx3, O.SR, seed + 3, True, mask)
+    q3 = (O.pack_codes(c3.reshape(48, N)), s3)
+    assert_gemm_close(host(gx)[rows], O.gemm(*q3, *q4, 48, K, N, a),
+                      O.gemm_abs(*q3, *q4, 48, K, N, a), "dX")
+    idx5 = O.block_indices(M, N, O.COL)[nrows]
+    c5, s5 = O.quantize_blocks(dyf.T[nrows].reshape(48, M // 32, 32), idx5, O.SR, seed + 5, True,
+                               mask)
+    q5 = (O.pack_codes(c5.reshape(48, M)), s5)
+    assert_gemm_close(host(gw)[nrows], O.gemm(*q5, *q6, 48, K, M, a),
+                      O.gemm_abs(*q5, *q6, 48, K, M, a), "dW")
