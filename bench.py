@@ -38,8 +38,8 @@ PEAK_FP4_TFLOPS = 10100.0
 # from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB copy, valid for
 # the GEMM code with this sha256 only (of the source with comments and blank
 # lines removed; the per-launch table is kept with the committed profiles).
-GEMM_TRAFFIC = {"sha256": "5fe42b3fe449f8c69407895eef918a1614c2ad7667658aa1de260c97ddd3bda6",
-                "bytes_per_launch": 676972389}
+GEMM_TRAFFIC = {"sha256": "765fa4d8343c4c33e630c12dd96af4cf19aafb89b7071a77624161b0642e7bb8",
+                "bytes_per_launch": 685656425}
 
 
 def gemm_code_sha256(path):
