@@ -273,7 +273,8 @@ int mx_requantize_segments(const uint8_t* codes_in, const uint8_t* scales_in, in
  * ([TJ] Question 2 (1)); X [M, K], W [N, K] (nn.Linear layout), both `dtype`;
  * Q_D is MX_ROW + MX_RNE along K.  Writes y [M][N] float32 and the packed
  * operands kept for the backward pass: xq_codes [M][K/2], xq_scales [M][K/32],
- * wq_codes [N][K/2], wq_scales [N][K/32].  M, N, K multiples of 32, N % 4 == 0. */
+ * wq_codes [N][K/2], wq_scales [N][K/32].  M, N, K multiples of 32 and below 2^31,
+ * N % 4 == 0 (else MX_ERR_SHAPE, before any launch). */
 int mx_linear_fwd(const void* x, const void* w, int dtype, int64_t M, int64_t N, int64_t K,
                   float* y, uint8_t* xq_codes, uint8_t* xq_scales,
                   uint8_t* wq_codes, uint8_t* wq_scales, void* stream);
@@ -291,7 +292,7 @@ size_t mx_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K);
  * the saved operands are mx_linear_fwd's outputs; writes dx [M][K] and
  * dw [N][K] float32.  workspace: device buffer of at least
  * mx_linear_bwd_workspace_size(M, N, K) bytes, 16-byte aligned.
- * M, N, K multiples of 32, K % 4 == 0. */
+ * M, N, K multiples of 32 and below 2^31, K % 4 == 0. */
 int mx_linear_bwd(const void* dy, int dtype, int64_t M, int64_t N, int64_t K,
                   const uint8_t* xq_codes, const uint8_t* xq_scales,
                   const uint8_t* wq_codes, const uint8_t* wq_scales,
@@ -332,7 +333,9 @@ int mx_linear_bwd_rht(const void* dy, int dtype, int64_t M, int64_t N, int64_t K
  * rounding, quantizer q uses seed + q.  dy [R][N] (`dtype`, R = offs[groups]);
  * xq: Q_D(X) [R][K/2] + [R][K/32]; wq: the stacked Q_D(W) [groups*N][K/2] +
  * [groups*N][K/32].  Writes dx [R][K] and dw [groups][N][K] float32 (an expert
- * without tokens gets dW_e = 0).  N, K multiples of 32.  workspace: at least
+ * without tokens gets dW_e = 0).  N, K multiples of 32 and below 2^31, and the
+ * workspace's token axis (each expert's tokens padded to a multiple of 512) below
+ * 2^31 (else MX_ERR_SHAPE).  workspace: at least
  * mx_grouped_linear_bwd_workspace_size(offs, groups, N, K) bytes, 16-byte
  * aligned. */
 size_t mx_grouped_linear_bwd_workspace_size(const int64_t* offs, int64_t groups, int64_t N,

@@ -158,6 +158,7 @@ static int linear_fwd_impl(const void* x, const void* w, int dtype, int64_t M, i
                            hipStream_t st) {
   MX_REQUIRE(dtype == MX_F32 || dtype == MX_BF16, MX_ERR_ENUM);
   MX_REQUIRE(M >= 0 && N >= 0 && K >= 0, MX_ERR_SHAPE);
+  MX_REQUIRE(M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX, MX_ERR_SHAPE);  // GEMM bounds
   MX_REQUIRE(M % 32 == 0 && N % 32 == 0 && K % 32 == 0, MX_ERR_SHAPE);
   if (M == 0 || N == 0 || K == 0) {
     if (M > 0 && N > 0 && K == 0) MX_REQUIRE(y, MX_ERR_NULL);
@@ -182,6 +183,7 @@ static int linear_bwd_impl(const void* dy, int dtype, int64_t M, int64_t N, int6
                            size_t workspace_bytes, hipStream_t st) {
   MX_REQUIRE(dtype == MX_F32 || dtype == MX_BF16, MX_ERR_ENUM);
   MX_REQUIRE(M >= 0 && N >= 0 && K >= 0, MX_ERR_SHAPE);
+  MX_REQUIRE(M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX, MX_ERR_SHAPE);  // GEMM bounds
   MX_REQUIRE(M % 32 == 0 && N % 32 == 0 && K % 32 == 0, MX_ERR_SHAPE);
   if (M == 0 || N == 0 || K == 0) return MX_OK;
   MX_REQUIRE(dy && xq_codes && xq_scales && wq_codes && wq_scales && dx && dw, MX_ERR_NULL);
@@ -282,6 +284,7 @@ extern "C" int mx_grouped_linear_bwd(const void* dy, int dtype, const int64_t* o
   MX_REQUIRE(dtype == MX_F32 || dtype == MX_BF16, MX_ERR_ENUM);
   MX_REQUIRE(valid_offsets(offs, groups), MX_ERR_SHAPE);
   MX_REQUIRE(N >= 0 && K >= 0 && N % 32 == 0 && K % 32 == 0, MX_ERR_SHAPE);
+  MX_REQUIRE(N <= INT32_MAX && K <= INT32_MAX, MX_ERR_SHAPE);
   const int64_t E = groups, R = offs[groups];
   if (N == 0 || K == 0) return MX_OK;
   MX_REQUIRE(dw, MX_ERR_NULL);
@@ -293,6 +296,7 @@ extern "C" int mx_grouped_linear_bwd(const void* dy, int dtype, const int64_t* o
   MX_REQUIRE(wq_codes && wq_scales, MX_ERR_NULL);
   MX_REQUIRE(aligned16(wq_codes), MX_ERR_ALIGN);
   const GroupedLayout L = grouped_layout(offs, E, N, K);
+  MX_REQUIRE(L.P <= INT32_MAX, MX_ERR_SHAPE);  // the dW contraction axis
   MX_REQUIRE(workspace && workspace_bytes >= L.total, MX_ERR_WORKSPACE);
   MX_REQUIRE(aligned16(workspace), MX_ERR_ALIGN);
   uint8_t* ws = static_cast<uint8_t*>(workspace);

@@ -153,6 +153,13 @@ def test_linear_validation_and_workspace_size(L):
     assert L.mx_linear_bwd_workspace_size(-1, 2, 3) == 0
     assert L.mx_linear_fwd(GOOD, GOOD, 0, 64, 64, 48, GOOD, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_SHAPE
     assert L.mx_linear_fwd(GOOD, GOOD, 3, 64, 64, 64, GOOD, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_ENUM
+    # dimensions past the GEMM's 32-bit contraction bound fail before any launch
+    assert L.mx_linear_fwd(GOOD, GOOD, 0, 64, 64, 1 << 31, GOOD, GOOD, GOOD, GOOD, GOOD, None) == mx.MX_ERR_SHAPE
+    big = [GOOD, 0, 1 << 31, 64, 64, GOOD, GOOD, GOOD, GOOD, 0, GOOD, GOOD]
+    assert L.mx_linear_bwd(*big, GOOD, 1 << 30, None) == mx.MX_ERR_SHAPE
+    offs = (ctypes.c_int64 * 2)(0, 64)
+    assert L.mx_grouped_linear_bwd(GOOD, 0, ctypes.addressof(offs), 1, 1 << 31, 64, GOOD, GOOD,
+                                   GOOD, GOOD, 0, GOOD, GOOD, GOOD, 1 << 30, None) == mx.MX_ERR_SHAPE
     args = [GOOD, 0, 64, 64, 64, GOOD, GOOD, GOOD, GOOD, 0, GOOD, GOOD]
     small = L.mx_linear_bwd_workspace_size(64, 64, 64) - 16
     assert L.mx_linear_bwd(*args, GOOD, small, None) == mx.MX_ERR_WORKSPACE
