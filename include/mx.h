@@ -192,12 +192,17 @@ int mx_requantize_rht(const uint8_t* codes_in, const uint8_t* scales_in, int64_t
                       int64_t cols, int round, uint64_t seed, uint32_t sign_mask,
                       uint8_t* codes_out, uint8_t* scales_out, void* stream);
 
-/* mx_dequantize: exact values of a packed matrix of logical shape [rows, cols]
+/* mx_dequantize: exact values of a packed matrix -- [ALTO] Jargon "MXFP4" (each
+ * block of 32 values shares one power-of-two scale, and an element's value is
+ * its 4-bit E2M1 number times that scale) and "E2M1"; it is the deq(.) inside
+ * every product of [TJ] Question 2 and the bin value q(w) of the
+ * de-oscillation pass.  Input: a packed matrix of logical shape [rows, cols]
  * quantized along `axis` (the inverse layout of mx_quantize), written row-major
  * [rows, cols] as float32 or bf16 (out_dtype).  value = sign * E2M1[code & 7]
  * * 2^(byte - 127) (exact in both types), byte 0xFF gives NaN.  hadamard != 0
  * undoes the rotation: x = s . (H32 y) 2^-5 per block in float32 (bf16 output
- * then rounds to nearest even). */
+ * then rounds to nearest even).  rows (MX_COL) or cols (MX_ROW) % 32 == 0;
+ * rows or cols == 0 is a no-op.  Errors as for mx_quantize. */
 int mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                   int axis, int hadamard, uint32_t sign_mask, void* out, int out_dtype,
                   void* stream);
@@ -274,7 +279,9 @@ int mx_requantize_segments(const uint8_t* codes_in, const uint8_t* scales_in, in
  * Q_D is MX_ROW + MX_RNE along K.  Writes y [M][N] float32 and the packed
  * operands kept for the backward pass: xq_codes [M][K/2], xq_scales [M][K/32],
  * wq_codes [N][K/2], wq_scales [N][K/32].  M, N, K multiples of 32 and below 2^31,
- * N % 4 == 0 (else MX_ERR_SHAPE, before any launch). */
+ * N % 4 == 0 (else MX_ERR_SHAPE, before any launch).  M or N == 0: no-op;
+ * K == 0: Y = 0 and nothing else is read or written (x, w and the packed
+ * operands may then be NULL). */
 int mx_linear_fwd(const void* x, const void* w, int dtype, int64_t M, int64_t N, int64_t K,
                   float* y, uint8_t* xq_codes, uint8_t* xq_scales,
                   uint8_t* wq_codes, uint8_t* wq_scales, void* stream);
@@ -292,7 +299,10 @@ size_t mx_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K);
  * the saved operands are mx_linear_fwd's outputs; writes dx [M][K] and
  * dw [N][K] float32.  workspace: device buffer of at least
  * mx_linear_bwd_workspace_size(M, N, K) bytes, 16-byte aligned.
- * M, N, K multiples of 32 and below 2^31, K % 4 == 0. */
+ * M, N, K multiples of 32 and below 2^31, K % 4 == 0.  K == 0: no-op.  M == 0 or
+ * N == 0 (an empty contraction for one of the products): dx = 0 and dw = 0 are
+ * written and nothing else is read (only dx, when M > 0, and dw, when N > 0,
+ * are required). */
 int mx_linear_bwd(const void* dy, int dtype, int64_t M, int64_t N, int64_t K,
                   const uint8_t* xq_codes, const uint8_t* xq_scales,
                   const uint8_t* wq_codes, const uint8_t* wq_scales,

@@ -379,7 +379,9 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  issue_scales(0);
+  // an empty contraction range (an expert without tokens) loads nothing and
+  // writes zeros
+  if (0 < KT) issue_scales(0);
   if (0 < KT) issue(0, I0{});
   if (1 < KT) issue(1, I1{});
   if (2 < KT) issue(2, I2{});
@@ -730,12 +732,38 @@ static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
 #undef MX_GEMM_ARGS
 }
 
+// C[m][n] = 0 for m < M, n < N (row pitch ldc): the product of an empty
+// contraction, written without touching the operands.
+__global__ __launch_bounds__(256) void k_zero_c(float* __restrict__ c, int64_t M, int64_t N,
+                                                int64_t ldc) {
+  const int64_t n4 = (N + 3) / 4, total = M * n4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / n4, q = (i % n4) * 4;
+    float* p = c + r * ldc + q;
+    if (q + 3 < N) {
+      store_c4(p, make_float4(0.f, 0.f, 0.f, 0.f), true);
+    } else {
+      for (int64_t j = q; j < N; ++j) c[r * ldc + j] = 0.f;
+    }
+  }
+}
+
+int zero_c_impl(float* c, int64_t M, int64_t N, int64_t ldc, hipStream_t st) {
+  if (M == 0 || N == 0) return MX_OK;
+  const int64_t n4 = M * ((N + 3) / 4);
+  k_zero_c<<<dim3((unsigned)hmin(cdiv(n4, 256), 4096)), dim3(256), 0, st>>>(c, M, N, ldc);
+  return launch_status();
+}
+
 // lds_a, lds_b: bytes between the scale rows of A and of B (K / 32 when
 // packed; the backward layers pad their own operands' rows to 16 bytes).
+// K == 0: C = 0 by a fill kernel; the operands are not read.
 int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
               const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha, float* c,
               int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, int64_t lds_a,
               int64_t lds_b, hipStream_t st) {
+  if (K == 0) return zero_c_impl(c, offs[groups], N, ldc, st);
   GemmSplit one{};
   one.n = 1;
   one.stream_c = 1;

@@ -34,6 +34,7 @@ int requantize_rht_pair_impl(const uint8_t* codes_in0, const uint8_t* scales_in0
                              int64_t cols, int round, uint64_t seed0, uint64_t seed1,
                              uint32_t mask, uint8_t* codes0, uint8_t* scales0, uint8_t* codes1,
                              uint8_t* scales1, hipStream_t st);
+int zero_c_impl(float* c, int64_t M, int64_t N, int64_t ldc, hipStream_t st);
 int gemm_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
               const int64_t* offs, int64_t groups, int64_t N, int64_t K, float alpha, float* c,
               int64_t ldc, int64_t b_stride_codes, int64_t b_stride_scales, int64_t lds_a,
@@ -160,9 +161,11 @@ static int linear_fwd_impl(const void* x, const void* w, int dtype, int64_t M, i
   MX_REQUIRE(M >= 0 && N >= 0 && K >= 0, MX_ERR_SHAPE);
   MX_REQUIRE(M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX, MX_ERR_SHAPE);  // GEMM bounds
   MX_REQUIRE(M % 32 == 0 && N % 32 == 0 && K % 32 == 0, MX_ERR_SHAPE);
-  if (M == 0 || N == 0 || K == 0) {
-    if (M > 0 && N > 0 && K == 0) MX_REQUIRE(y, MX_ERR_NULL);
-    if (M == 0 || N == 0) return MX_OK;
+  if (M == 0 || N == 0) return MX_OK;
+  if (K == 0) {  // Y = 0; the packed operands are empty
+    MX_REQUIRE(y, MX_ERR_NULL);
+    MX_REQUIRE(aligned16(y), MX_ERR_ALIGN);
+    return zero_c_impl(y, M, N, N, st);
   }
   MX_REQUIRE(x && w && y && xq_codes && xq_scales && wq_codes && wq_scales, MX_ERR_NULL);
   MX_REQUIRE(aligned16(x) && aligned16(w) && aligned16(y) && aligned16(xq_codes) &&
@@ -185,7 +188,15 @@ static int linear_bwd_impl(const void* dy, int dtype, int64_t M, int64_t N, int6
   MX_REQUIRE(M >= 0 && N >= 0 && K >= 0, MX_ERR_SHAPE);
   MX_REQUIRE(M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX, MX_ERR_SHAPE);  // GEMM bounds
   MX_REQUIRE(M % 32 == 0 && N % 32 == 0 && K % 32 == 0, MX_ERR_SHAPE);
-  if (M == 0 || N == 0 || K == 0) return MX_OK;
+  if (K == 0) return MX_OK;  // dX [M][0] and dW [N][0] are empty
+  if (M == 0 || N == 0) {
+    // an empty contraction: dX = 0 (over N == 0) and dW = 0 (over M == 0)
+    if (M > 0) MX_REQUIRE(dx && aligned16(dx), dx ? MX_ERR_ALIGN : MX_ERR_NULL);
+    if (N > 0) MX_REQUIRE(dw && aligned16(dw), dw ? MX_ERR_ALIGN : MX_ERR_NULL);
+    int s = zero_c_impl(dx, M, K, K, st);
+    if (s != MX_OK) return s;
+    return zero_c_impl(dw, N, K, K, st);
+  }
   MX_REQUIRE(dy && xq_codes && xq_scales && wq_codes && wq_scales && dx && dw, MX_ERR_NULL);
   MX_REQUIRE(aligned16(dy) && aligned16(xq_codes) && aligned16(wq_codes) && aligned16(dx) &&
                  aligned16(dw), MX_ERR_ALIGN);

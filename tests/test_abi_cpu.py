@@ -165,6 +165,21 @@ def test_linear_validation_and_workspace_size(L):
     assert L.mx_linear_bwd(*args, GOOD, small, None) == mx.MX_ERR_WORKSPACE
     assert L.mx_linear_bwd(*args, None, 1 << 30, None) == mx.MX_ERR_WORKSPACE
     assert L.mx_linear_bwd(*args, BAD, 1 << 30, None) == mx.MX_ERR_ALIGN
+    # empty contractions: only the zero-filled output is required (validated
+    # before the fill kernel; a NULL operand is fine)
+    assert L.mx_linear_fwd(None, None, 0, 64, 64, 0, None, None, None, None, None, None) == mx.MX_ERR_NULL
+    assert L.mx_linear_fwd(None, None, 0, 64, 64, 0, BAD, None, None, None, None, None) == mx.MX_ERR_ALIGN
+    assert L.mx_linear_fwd(None, None, 0, 0, 64, 0, None, None, None, None, None, None) == mx.MX_OK
+    assert L.mx_linear_bwd(None, 0, 0, 64, 64, None, None, None, None, 0, None, None, None, 0,
+                           None) == mx.MX_ERR_NULL                     # dW required when N > 0
+    assert L.mx_linear_bwd(None, 0, 0, 64, 64, None, None, None, None, 0, None, BAD, None, 0,
+                           None) == mx.MX_ERR_ALIGN
+    assert L.mx_linear_bwd(None, 0, 64, 0, 64, None, None, None, None, 0, None, None, None, 0,
+                           None) == mx.MX_ERR_NULL                     # dX required when M > 0
+    assert L.mx_linear_bwd(None, 0, 64, 64, 0, None, None, None, None, 0, None, None, None, 0,
+                           None) == mx.MX_OK                           # K == 0: nothing to write
+    assert L.mx_linear_bwd(None, 0, 0, 0, 64, None, None, None, None, 0, None, None, None, 0,
+                           None) == mx.MX_OK
 
 
 def test_rotated_entry_points_validation(L):

@@ -69,6 +69,39 @@ def test_gemm_k_zero_writes_zeros():
     assert np.all(host(c) == 0)
 
 
+def test_empty_contraction_with_null_operands_writes_zeros():
+    """K == 0 is a valid product (C = 0) and reads no operand, so NULL operand
+    pointers are accepted: every GEMM entry point, and the linear layer's forward
+    (Y = 0) and backward over an empty token or output axis (dW = 0, dX = 0)."""
+    M, N = 300, 72
+    c = torch.full((M, 76), 5.0, device=DEV)
+    mx.mx_gemm(None, None, None, None, M, N, 0, 1.0, c, 76)
+    got = host(c)
+    assert np.all(got[:, :N] == 0) and np.all(got[:, N:] == 5.0)
+    c.fill_(5.0)
+    mx.mx_gemm_ld(None, None, 16, None, None, 16, M, N, 0, 1.0, c, 76)
+    got = host(c)
+    assert np.all(got[:, :N] == 0) and np.all(got[:, N:] == 5.0)
+    offs = [0, 100, 100, 300]
+    for fn in ("grouped", "grouped_ld"):
+        c = torch.full((M, N), 5.0, device=DEV)
+        if fn == "grouped":
+            mx.mx_gemm_grouped(None, None, None, None, offs, 3, N, 0, 1.0, c)
+        else:
+            mx.mx_gemm_grouped_ld(None, None, 16, None, None, 16, offs, 3, N, 0, 1.0, c)
+        assert np.all(host(c) == 0), fn
+    y = torch.full((64, 96), 5.0, device=DEV)
+    mx.mx_linear_fwd(None, None, mx.MX_BF16, 64, 96, 0, y, None, None, None, None)
+    assert np.all(host(y) == 0)
+    # backward with M == 0 tokens: dW [N][K] = 0; with N == 0 outputs: dX [M][K] = 0
+    dw = torch.full((96, 128), 5.0, device=DEV)
+    mx.mx_linear_bwd(None, mx.MX_BF16, 0, 96, 128, None, None, None, None, 1, None, dw, None, 0)
+    assert np.all(host(dw) == 0)
+    dx = torch.full((64, 128), 5.0, device=DEV)
+    mx.mx_linear_bwd(None, mx.MX_BF16, 64, 0, 128, None, None, None, None, 1, dx, None, None, 0)
+    assert np.all(host(dx) == 0)
+
+
 def test_gemm_tiny_config_end_to_end():
     """256^3: X, W float32 N(0,1) seed 0 -> MXFP4 row RNE -> GEMM; codes, scales and Y."""
     cfg = synth.tiny_config(0)

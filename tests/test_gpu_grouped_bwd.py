@@ -111,6 +111,21 @@ def test_grouped_linear_bwd_long_segments_matches_oracle():
     check_grouped_bwd(dy, "bf16", xq, wq, offs, N, K, seed=12)
 
 
+def test_grouped_linear_bwd_empty_trailing_expert():
+    """The last expert gets no tokens: its dW contraction range is empty and
+    starts at the end of the padded token axis, so it must load nothing (no scale
+    read past the workspace) and write dW_e = 0; the other experts as usual."""
+    rng = np.random.default_rng(48)
+    offs = [0, 37, 100, 100, 261, 400, 400]
+    E, N, K = len(offs) - 1, 64, 96
+    R = offs[-1]
+    x = rng.standard_normal((R, K)).astype(np.float32)
+    w = (rng.standard_normal((E * N, K)) * 0.02).astype(np.float32)
+    dy = synth.f32_to_bf16_bits((rng.standard_normal((R, N)) * 1e-3).astype(np.float32))
+    xq, wq = O.quantize(x, O.ROW, O.RNE), O.quantize(w, O.ROW, O.RNE)
+    check_grouped_bwd(dy, "bf16", xq, wq, offs, N, K, seed=13)
+
+
 def test_grouped_linear_bwd_single_expert_equals_dense_backward():
     """One expert with a 32-aligned token count is the dense layer: the same bits."""
     rng = np.random.default_rng(45)

@@ -37,6 +37,52 @@ def test_gemm_equals_exact_rational_sum(M, N, K):
             assert C[m, n] == float(tot)      # exact: every partial sum is a short dyadic
 
 
+@pytest.mark.parametrize("M,N,K,alpha", [(1, 1, 32, -0.75), (3, 5, 64, -2.0 ** -5),
+                                         (4, 2, 96, 1.5), (2, 3, 128, -3.0)])
+def test_gemm_abs_equals_exact_rational_sum_of_magnitudes(M, N, K, alpha):
+    """The tolerance scale of every GEMM parity check, sum_k |alpha a_k b_k|, against
+    exact rationals: mixed signs (a dropped absolute value would cancel terms),
+    negative alpha (a sign slip gives a negative scale), signed-zero codes (8) and
+    scale bytes at both ends of the E8M0 range (0, 1, 254) next to ordinary ones."""
+    rng = np.random.default_rng(M * 1000 + N * 100 + K)
+    ac, as_, acu = random_packed(rng, M, K)
+    bc, bs, bcu = random_packed(rng, N, K)
+    acu[:, 3] = 8                                   # -0 in every row of A
+    bcu[:, 5] = 8
+    ac, bc = O.pack_codes(acu), O.pack_codes(bcu)
+    extremes = np.array([0, 1, 254, 127], np.uint8)
+    as_[:, 0] = extremes[np.arange(M) % 4]
+    bs[:, -1] = extremes[(np.arange(N) + 1) % 4]
+    got = O.gemm_abs(ac, as_, bc, bs, M, N, K, alpha)
+    a = Fraction(alpha)
+    for m in range(M):
+        for n in range(N):
+            terms = [abs(a * exact_value(acu[m, k], as_[m, k // 32]) *
+                         exact_value(bcu[n, k], bs[n, k // 32])) for k in range(K)]
+            want = sum(terms)
+            assert got[m, n] >= 0
+            # the float64 sum of K non-negative terms is within K ulps of the exact sum
+            assert abs(Fraction(float(got[m, n])) - want) <= want * K * Fraction(2) ** -52, (m, n)
+    # and it bounds the product itself (triangle inequality), with equality when
+    # every term has one sign
+    C = O.gemm(ac, as_, bc, bs, M, N, K, alpha)
+    assert np.all(np.abs(C) <= got * (1 + K * 2.0 ** -52))
+    pos_a = O.pack_codes(acu & 7)
+    pos_b = O.pack_codes(bcu & 7)
+    assert np.array_equal(O.gemm_abs(pos_a, as_, pos_b, bs, M, N, K, alpha),
+                          np.abs(O.gemm(pos_a, as_, pos_b, bs, M, N, K, alpha)))
+
+
+def test_gemm_abs_scales_with_the_magnitude_of_alpha():
+    rng = np.random.default_rng(31)
+    ac, as_, _ = random_packed(rng, 6, 64)
+    bc, bs, _ = random_packed(rng, 7, 64)
+    one = O.gemm_abs(ac, as_, bc, bs, 6, 7, 64, 1.0)
+    assert np.all(one > 0)
+    for alpha in (-1.0, 2.0 ** -5, -8.0):
+        assert np.array_equal(O.gemm_abs(ac, as_, bc, bs, 6, 7, 64, alpha), abs(alpha) * one)
+
+
 def test_gemm_with_unit_scales_is_an_integer_matmul():
     # With every scale byte 127 (2^0), 2 * deq(code) is an integer in [-12, 12]:
     # the GEMM must equal a textbook int64 matrix product divided by 4.

@@ -282,6 +282,42 @@ def test_sr_is_unbiased_for_in_range_values():
     assert np.all(np.abs(mean - vals) <= 5 * np.maximum(sd, 1e-12) / math.sqrt(n) + 1e-12)
 
 
+def test_sr_decisions_of_a_pair_are_independent():
+    """Elements 2i and 2i+1 of a block draw from one generator output (disjoint
+    bits).  Over 100,000 seeds, each pair's two round-up indicators must be
+    uncorrelated: the sample covariance within 5 standard errors of 0, and
+    P(both up) = P(up 2i) P(up 2i+1).  The pairs take different probabilities
+    (dyadic t = 1/2, 1/4, 3/4, 1/8 ..., exact in float32), so a shared or overlapping random field would
+    show as a positive covariance, a complementary one as a negative one."""
+    t = np.array([0.5, 0.5, 0.25, 0.75, 0.75, 0.25, 0.125, 0.875, 0.5, 0.125, 0.875, 0.5,
+                  0.3125, 0.5625, 0.90625, 0.09375, 0.5, 0.25, 0.625, 0.375, 0.0625, 0.5, 0.5,
+                  0.9375, 0.25, 0.25, 0.75, 0.75, 0.40625, 0.6875, 0.1875, 0.0], np.float64)
+    blk = (t * 0.5).astype(np.float32)   # a in [0, 0.5): neighbours 0 and 0.5, P(up) = t
+    blk[31] = 6.0                        # anchor: scale byte 127
+    assert np.array_equal(blk[:31].astype(np.float64), t[:31] * 0.5)
+    n = 100_000
+    idx = np.arange(32, dtype=np.int64) + 4096
+    up = np.empty((n, 32), np.float64)
+    rng = np.random.default_rng(2025)
+    seeds = rng.integers(0, 2 ** 63, n, dtype=np.int64).astype(np.uint64) * np.uint64(2) + \
+        rng.integers(0, 2, n).astype(np.uint64)
+    for j, sd in enumerate(seeds):
+        c, s = O.quantize_blocks(blk, idx, O.SR, seed=int(sd))
+        up[j] = c & 7
+    assert np.all((up[:, :31] == 0) | (up[:, :31] == 1))
+    p = up.mean(axis=0)
+    se_p = np.sqrt(t * (1 - t) / n)
+    assert np.all(np.abs(p[:31] - t[:31]) <= 5 * se_p[:31] + 1e-12)     # the odds themselves
+    for i in range(15):                                                  # pairs (2i, 2i+1), i < 15
+        u0, u1 = up[:, 2 * i], up[:, 2 * i + 1]
+        cov = np.mean(u0 * u1) - u0.mean() * u1.mean()
+        se = math.sqrt(t[2 * i] * (1 - t[2 * i]) * t[2 * i + 1] * (1 - t[2 * i + 1]) / n)
+        assert abs(cov) <= 5 * se, (i, cov, se)
+    # across pairs as well (outputs for different pair indices)
+    cov = np.mean(up[:, 1] * up[:, 2]) - up[:, 1].mean() * up[:, 2].mean()
+    assert abs(cov) <= 5 * math.sqrt(0.25 * 0.25 * 0.75 / n)
+
+
 def test_sr_saturation_is_biased_above_six():
     # Reading: values in (6, 8) * 2^e saturate to 6 under SR as under RNE.
     blk = np.zeros(32, np.float32)
