@@ -309,6 +309,27 @@ int mx_linear_bwd(const void* dy, int dtype, int64_t M, int64_t N, int64_t K,
                   uint64_t seed, float* dx, float* dw,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* mx_linear_bwd_noalloc: mx_linear_bwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): no workspace argument and no allocation of any kind; the
+ * workspace is a file-scope device array of mx_linear_bwd_noalloc_max_workspace()
+ * bytes (64 MiB) that each GPU the library runs on holds from library load until
+ * the process ends.  Layers whose workspace (mx_linear_bwd_workspace_size) is
+ * larger are rejected with MX_ERR_WORKSPACE before anything is enqueued (the
+ * DeiT-S MLP layers need 36-43 MiB; the Llama-3-8B up-projection needs 166 MiB
+ * and must use mx_linear_bwd).  Every call on one GPU shares that GPU's array,
+ * so calls that may overlap on one GPU (on different streams, or from different
+ * threads without ordering) race and give wrong results; calls on one stream are
+ * ordered and safe.  Nothing in the array needs to start at zero.  The first call
+ * on a device looks up the array's device address (MX_ERR_HIP if the runtime
+ * cannot give it).  Arguments, results and other errors as mx_linear_bwd, bit
+ * for bit. */
+int mx_linear_bwd_noalloc(const void* dy, int dtype, int64_t M, int64_t N, int64_t K,
+                          const uint8_t* xq_codes, const uint8_t* xq_scales,
+                          const uint8_t* wq_codes, const uint8_t* wq_scales,
+                          uint64_t seed, float* dx, float* dw, void* stream);
+size_t mx_linear_bwd_noalloc_max_workspace(void);
+
 /* mx_linear_fwd_rht / mx_linear_bwd_rht: the same layer with the random-sign
  * block Hadamard on every product ([ALTO] Jargon "Randomized Hadamard
  * transform", the "MXFP4 + RHT + stochastic rounding" rows of its steps

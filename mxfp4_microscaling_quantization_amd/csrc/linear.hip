@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "mx_host.h"
 
 namespace mx {
@@ -235,9 +237,55 @@ static int linear_bwd_impl(const void* dy, int dtype, int64_t M, int64_t N, int6
                          L.dw, part, p5, p6, st);
 }
 
+// ---------------------------------------------------------------- no-allocation backward
+// Workspace of mx_linear_bwd_noalloc: one file-scope device array, present on
+// every GPU the library runs on from module load to process end.  Its name is a
+// host-side stand-in in host code: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch array (nullptr and an error status
+// when the runtime cannot give it).
+static int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MX_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MX_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MX_OK;
+}
+
 }  // namespace mx
 
 using namespace mx;
+
+extern "C" size_t mx_linear_bwd_noalloc_max_workspace(void) { return kScratchBytes; }
+
+extern "C" int mx_linear_bwd_noalloc(const void* dy, int dtype, int64_t M, int64_t N, int64_t K,
+                                     const uint8_t* xq_codes, const uint8_t* xq_scales,
+                                     const uint8_t* wq_codes, const uint8_t* wq_scales,
+                                     uint64_t seed, float* dx, float* dw, void* stream) {
+  // sizes first, so an oversized layer is rejected before any runtime call
+  MX_REQUIRE(M >= 0 && N >= 0 && K >= 0, MX_ERR_SHAPE);
+  MX_REQUIRE(M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX, MX_ERR_SHAPE);
+  MX_REQUIRE(M % 32 == 0 && N % 32 == 0 && K % 32 == 0, MX_ERR_SHAPE);
+  const size_t need = bwd_layout(M, N, K).total;
+  MX_REQUIRE(need <= kScratchBytes, MX_ERR_WORKSPACE);
+  void* ws = nullptr;
+  const int s = scratch_for_current_device(&ws);
+  if (s != MX_OK) return s;
+  return linear_bwd_impl(dy, dtype, M, N, K, xq_codes, xq_scales, wq_codes, wq_scales, seed, 0,
+                         0, dx, dw, ws, kScratchBytes, as_stream(stream));
+}
 
 extern "C" int mx_linear_fwd(const void* x, const void* w, int dtype, int64_t M, int64_t N,
                              int64_t K, float* y, uint8_t* xq_codes, uint8_t* xq_scales,

@@ -49,6 +49,8 @@ SIGNATURES = {
     "mx_linear_fwd": ([_P, _P, _i32, _i64, _i64, _i64, _P, _P, _P, _P, _P, _P], _i32),
     "mx_linear_bwd_workspace_size": ([_i64, _i64, _i64], _sz),
     "mx_linear_bwd": ([_P, _i32, _i64, _i64, _i64, _P, _P, _P, _P, _u64, _P, _P, _P, _sz, _P], _i32),
+    "mx_linear_bwd_noalloc": ([_P, _i32, _i64, _i64, _i64, _P, _P, _P, _P, _u64, _P, _P, _P], _i32),
+    "mx_linear_bwd_noalloc_max_workspace": ([], _sz),
     "mx_grouped_linear_bwd_workspace_size": ([_P, _i64, _i64, _i64], _sz),
     "mx_grouped_linear_bwd": ([_P, _i32, _P, _i64, _i64, _i64, _P, _P, _P, _P, _u64, _P, _P, _P, _sz,
                                _P], _i32),
@@ -276,6 +278,17 @@ def mx_linear_bwd(dy, dtype, M, N, K, xq_codes, xq_scales, wq_codes, wq_scales, 
         _ptr(dy), dtype, M, N, K, _ptr(xq_codes), _ptr(xq_scales), _ptr(wq_codes),
         _ptr(wq_scales), seed, _ptr(dx), _ptr(dw), _ptr(workspace), workspace_bytes,
         _stream(stream)))
+
+
+def mx_linear_bwd_noalloc(dy, dtype, M, N, K, xq_codes, xq_scales, wq_codes, wq_scales, seed, dx,
+                          dw, stream=None):
+    _check("mx_linear_bwd_noalloc", lib().mx_linear_bwd_noalloc(
+        _ptr(dy), dtype, M, N, K, _ptr(xq_codes), _ptr(xq_scales), _ptr(wq_codes),
+        _ptr(wq_scales), seed, _ptr(dx), _ptr(dw), _stream(stream)))
+
+
+def mx_linear_bwd_noalloc_max_workspace():
+    return int(lib().mx_linear_bwd_noalloc_max_workspace())
 
 
 def mx_linear_bwd_rht(dy, dtype, M, N, K, xq_codes, xq_scales, wq_codes, wq_scales, seed,
