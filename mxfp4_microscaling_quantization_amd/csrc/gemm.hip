@@ -136,6 +136,16 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) {
                : "s"(lds_addr(lds)), "v"(g)
                : "memory", "m0");
 }
+// The same load from an SGPR base plus a 32-bit per-lane offset: the wave
+// hands the address unit half the address data, and the instruction issues
+// in about a third of the cycles between MFMAs (measured interleaved with
+// scaled FP4 MFMAs).
+__device__ __forceinline__ void dma16s(const uint8_t* base, uint32_t voff, void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_addr(lds)), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void* g, void* lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                :
@@ -192,6 +202,153 @@ struct ScaleGroupLds {
   uint4 b[BN];
 };
 
+// The work of one workgroup: which problem (first or paired second), group,
+// contraction range and output tile, and where its operands and output live.
+// The first problem's workgroups come first in dispatch order.  Within a
+// problem, consecutive logical tiles are spread over one XCD (workgroups are
+// dealt round-robin to the 8 XCDs), then tile rows are walked kGroupM at a time.
+struct TileWork {
+  const uint8_t* A;
+  const uint8_t* SA;
+  const uint8_t* B;
+  const uint8_t* SB;
+  float* C;
+  int64_t N, ldc, ldk, lds_a, lds_b, a_last, m0, n0, k0, kc_bytes, kc_blocks;
+  float alpha;
+  bool stream_c;
+  int rows_valid, cols_valid, KT, tail_kb;
+};
+
+template <int BM, int BN, bool PAIR>
+__device__ __forceinline__ TileWork tile_work(const uint8_t* A0, const uint8_t* SA0,
+                                              const uint8_t* B0, const uint8_t* SB0, int64_t N0,
+                                              int64_t K0, float alpha0, float* C0, int64_t ldc0,
+                                              int64_t b_stride_codes, int64_t b_stride_scales,
+                                              const GemmGroups& gg, const GemmSplit& sp,
+                                              const GemmPlain& p1) {
+  const int tiles0 = gg.tile_start[gg.ngroups];
+  const int total0 = tiles0 * sp.n;
+  const bool second = PAIR && (int)blockIdx.x >= total0;  // uniform over the workgroup
+  const int total = second ? p1.tiles : total0;
+  int id = (int)blockIdx.x - (second ? total0 : 0);
+  {
+    const int q = total / 8, r = total % 8, x = id % 8;
+    id = x * q + min(x, r) + id / 8;
+  }
+  int split = 0, g = 0, tiles_n = p1.tiles_n;
+  int64_t grow0 = 0, grows = p1.M, a_last = p1.M - 1, k0 = 0, k1 = p1.K;
+  if (!second) {
+    split = id / tiles0;
+    id -= split * tiles0;
+    while (g + 1 < gg.ngroups && gg.tile_start[g + 1] <= id) ++g;
+    id -= gg.tile_start[g];
+    tiles_n = gg.tiles_n;
+    grow0 = gg.row_off[g];
+    grows = gg.row_off[g + 1] - grow0;
+    a_last = gg.row_off[gg.ngroups] - 1;  // last row of A in memory
+    k0 = sp.kbeg[split];
+    k1 = k0 + sp.klen[split];
+  }
+  TileWork w;
+  w.A = second ? p1.A : A0;
+  w.SA = second ? p1.SA : SA0;
+  w.N = second ? p1.N : N0;
+  const int64_t K = second ? p1.K : K0;
+  w.alpha = second ? p1.alpha : alpha0;
+  w.ldc = second ? p1.ldc : ldc0;
+  w.stream_c = second || sp.stream_c != 0;
+  w.C = second ? p1.C : C0 + split * sp.c_stride;
+  w.B = second ? p1.B : B0 + (int64_t)g * b_stride_codes;
+  w.SB = second ? p1.SB : SB0 + (int64_t)g * b_stride_scales;
+  const int lt = id;
+  const int tiles_m = (int)((grows + BM - 1) / BM);
+  const int span = kGroupM * tiles_n;
+  const int first_m = (lt / span) * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int tm_idx = first_m + (lt % span) % gm;
+  const int tn_idx = (lt % span) / gm;
+
+  w.m0 = grow0 + (int64_t)tm_idx * BM;
+  w.rows_valid = (int)min<int64_t>(BM, grow0 + grows - w.m0);
+  w.n0 = (int64_t)tn_idx * BN;
+  w.cols_valid = (int)min<int64_t>(BN, w.N - w.n0);
+  w.a_last = a_last;
+  w.k0 = k0;
+  w.ldk = K / 2;   // code bytes per row
+  w.lds_a = second ? p1.lds_a : gg.lds_a;  // bytes between scale rows
+  w.lds_b = second ? p1.lds_b : gg.lds_b;
+  const int64_t kc_len = k1 - k0;  // K-values of this range
+  w.kc_bytes = kc_len / 2;
+  w.kc_blocks = kc_len / 32;
+  w.KT = (int)((kc_len + 127) / 128);
+  w.tail_kb = (int)(w.kc_blocks - (int64_t)(w.KT - 1) * 4);  // valid 32-blocks in the last step
+  return w;
+}
+
+// Epilogue of a BM x BN tile held by WM x WN waves in acc[TN][TM] (lane holds
+// D[n = 8 g + 4 lh + v][m = lr], g, v = 0..3, of each 32x32 tile).  The LDS ring
+// is idle by then: each wave stages its sub-tile there, 64 rows per pass (32
+// when the ring is too small for that; row pitch CH 16-byte chunks, chunk index
+// XORed with row & 15, so the 16-row writes and the row reads are free of bank
+// conflicts), and reads it back so that every store instruction writes whole
+// row segments of C (two rows of 512 bytes for 256 x 256 tiles, four of 256 for
+// 128 x 128) instead of 32-byte pieces of 32 rows.
+template <int BM, int BN, int WM, int WN, int TM, int TN, int RING>
+__device__ __forceinline__ void store_tile_impl(v16f (&acc)[TN][TM], char* ring,
+                                                const TileWork& tw) {
+  constexpr int NW = WM * WN;
+  constexpr int CH = TN * 8;      // 16-byte chunks per staged row
+  constexpr int RB = CH * 16;     // bytes per staged row
+  constexpr int RPI = 64 / CH;    // rows per read (one chunk per lane)
+  constexpr int PR = RING >= NW * 64 * RB ? 64 : 32;  // rows per pass
+  constexpr int PB = PR / 32;     // 32-row MFMA tiles per pass
+  static_assert(TM % PB == 0 && CH >= 16 && 64 % CH == 0, "staging shape");
+  static_assert(RING >= NW * PR * RB, "staging space");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm_off = (wave / WN) * (BM / WM);
+  const int wn_off = (wave % WN) * (BN / WN);
+  const int lr = lane & 31, lh = lane >> 5;
+  const float alpha = tw.alpha;
+  __syncthreads();  // every wave is done reading the ring
+  char* stg = ring + wave * PR * RB;
+#pragma unroll
+  for (int p = 0; p < TM / PB; ++p) {
+#pragma unroll
+    for (int bb = 0; bb < PB; ++bb) {
+      const int b = PB * p + bb;
+      const int rl = bb * 32 + lr;
+#pragma unroll
+      for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int ch = a * 8 + gq * 2 + lh;
+          *reinterpret_cast<float4*>(stg + rl * RB + ((ch ^ (rl & 15)) * 16)) =
+              make_float4(acc[a][b][4 * gq] * alpha, acc[a][b][4 * gq + 1] * alpha,
+                          acc[a][b][4 * gq + 2] * alpha, acc[a][b][4 * gq + 3] * alpha);
+        }
+    }
+#pragma unroll 4
+    for (int it = 0; it < PR / RPI; ++it) {
+      const int rl = it * RPI + lane / CH, ch = lane % CH;
+      const float4 v = *reinterpret_cast<const float4*>(stg + rl * RB + ((ch ^ (rl & 15)) * 16));
+      const int mrow = wm_off + p * PR + rl;
+      const int ncol = wn_off + ch * 4;
+      if (mrow < tw.rows_valid) {
+        float* crow = tw.C + (tw.m0 + mrow) * tw.ldc + tw.n0;
+        if (ncol + 3 < tw.cols_valid) {
+          store_c4(crow + ncol, v, tw.stream_c);
+        } else {
+          if (ncol + 0 < tw.cols_valid) crow[ncol + 0] = v.x;
+          if (ncol + 1 < tw.cols_valid) crow[ncol + 1] = v.y;
+          if (ncol + 2 < tw.cols_valid) crow[ncol + 2] = v.z;
+        }
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int STAGES, int SC, bool PAIR>
 __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
     const uint8_t* __restrict__ A0, const uint8_t* __restrict__ SA0, const uint8_t* __restrict__ B0,
@@ -225,63 +382,15 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
   auto bufA = [&](auto S) -> TileLds<BM, SC>& { return stage(S).a; };
   auto bufB = [&](auto S) -> TileLds<BN, SC>& { return stage(S).b; };
 
-  // ---- which problem and tile: the first problem's workgroups come first in
-  // dispatch order.  Within a problem, consecutive logical tiles are spread
-  // over one XCD (workgroups are dealt round-robin to the 8 XCDs), then tile
-  // rows are walked kGroupM at a time.
-  const int tiles0 = gg.tile_start[gg.ngroups];
-  const int total0 = tiles0 * sp.n;
-  const bool second = PAIR && (int)blockIdx.x >= total0;  // uniform over the workgroup
-  const int total = second ? p1.tiles : total0;
-  int id = (int)blockIdx.x - (second ? total0 : 0);
-  {
-    const int q = total / 8, r = total % 8, x = id % 8;
-    id = x * q + min(x, r) + id / 8;
-  }
-  int split = 0, g = 0, tiles_n = p1.tiles_n;
-  int64_t grow0 = 0, grows = p1.M, a_last = p1.M - 1, k0 = 0, k1 = p1.K;
-  if (!second) {
-    split = id / tiles0;
-    id -= split * tiles0;
-    while (g + 1 < gg.ngroups && gg.tile_start[g + 1] <= id) ++g;
-    id -= gg.tile_start[g];
-    tiles_n = gg.tiles_n;
-    grow0 = gg.row_off[g];
-    grows = gg.row_off[g + 1] - grow0;
-    a_last = gg.row_off[gg.ngroups] - 1;  // last row of A in memory
-    k0 = sp.kbeg[split];
-    k1 = k0 + sp.klen[split];
-  }
-  const uint8_t* __restrict__ A = second ? p1.A : A0;
-  const uint8_t* __restrict__ SA = second ? p1.SA : SA0;
-  const int64_t N = second ? p1.N : N0;
-  const int64_t K = second ? p1.K : K0;
-  const float alpha = second ? p1.alpha : alpha0;
-  const int64_t ldc = second ? p1.ldc : ldc0;
-  const bool stream_c = second || sp.stream_c != 0;
-  float* __restrict__ C = second ? p1.C : C0 + split * sp.c_stride;
-  const uint8_t* Bg = second ? p1.B : B0 + (int64_t)g * b_stride_codes;
-  const uint8_t* SBg = second ? p1.SB : SB0 + (int64_t)g * b_stride_scales;
-  const int lt = id;
-  const int tiles_m = (int)((grows + BM - 1) / BM);
-  const int span = kGroupM * tiles_n;
-  const int first_m = (lt / span) * kGroupM;
-  const int gm = min(tiles_m - first_m, kGroupM);
-  const int tm_idx = first_m + (lt % span) % gm;
-  const int tn_idx = (lt % span) / gm;
-
-  const int64_t m0 = grow0 + (int64_t)tm_idx * BM;
-  const int rows_valid = (int)min<int64_t>(BM, grow0 + grows - m0);
-  const int64_t n0 = (int64_t)tn_idx * BN;
-  const int cols_valid = (int)min<int64_t>(BN, N - n0);
-
-  const int64_t ldk = K / 2;   // code bytes per row
-  const int64_t lds_a = second ? p1.lds_a : gg.lds_a;  // bytes between scale rows
-  const int64_t lds_b = second ? p1.lds_b : gg.lds_b;
-  const int64_t kc_len = k1 - k0;  // K-values of this split
-  const int64_t kc_bytes = kc_len / 2, kc_blocks = kc_len / 32;
-  const int KT = (int)((kc_len + 127) / 128);
-  const int tail_kb = (int)(kc_blocks - (int64_t)(KT - 1) * 4);  // valid 32-blocks in the last step
+  const TileWork tw = tile_work<BM, BN, PAIR>(A0, SA0, B0, SB0, N0, K0, alpha0, C0, ldc0,
+                                              b_stride_codes, b_stride_scales, gg, sp, p1);
+  const uint8_t* __restrict__ A = tw.A;
+  const uint8_t* __restrict__ SA = tw.SA;
+  const uint8_t* Bg = tw.B;
+  const uint8_t* SBg = tw.SB;
+  const int64_t N = tw.N, ldk = tw.ldk, lds_a = tw.lds_a, lds_b = tw.lds_b, a_last = tw.a_last;
+  const int64_t m0 = tw.m0, n0 = tw.n0, k0 = tw.k0, kc_bytes = tw.kc_bytes, kc_blocks = tw.kc_blocks;
+  const int KT = tw.KT, tail_kb = tw.tail_kb;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -554,60 +663,300 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
     if (kt + 3 < KT) step(kt + 3, I3{}, Part{});
   }
 
-  // ---- epilogue: lane holds D[n = 8 g + 4 lh + v][m = lr], g, v = 0..3, of each 32x32 tile
-  // The LDS ring is idle now: each wave stages its sub-tile there, 64 rows per
-  // pass (32 when the ring is too small for that; row pitch CH 16-byte chunks,
-  // chunk index XORed with row & 15, so the 16-row writes and the row reads
-  // are free of bank conflicts), and reads it back so that every store
-  // instruction writes whole row segments of C (two rows of 512 bytes for
-  // 256 x 256 tiles, four of 256 for 128 x 128) instead of 32-byte pieces of
-  // 32 rows.
-  {
-    constexpr int CH = TN * 8;      // 16-byte chunks per staged row
-    constexpr int RB = CH * 16;     // bytes per staged row
-    constexpr int RPI = 64 / CH;    // rows per read (one chunk per lane)
-    constexpr int PR = sizeof(ring) >= NW * 64 * RB ? 64 : 32;  // rows per pass
-    constexpr int PB = PR / 32;     // 32-row MFMA tiles per pass
-    static_assert(TM % PB == 0 && CH >= 16 && 64 % CH == 0, "staging shape");
-    static_assert(sizeof(ring) >= NW * PR * RB, "staging space");
-    __syncthreads();  // every wave is done reading the ring
-    char* stg = reinterpret_cast<char*>(ring) + wave * PR * RB;
+  store_tile_impl<BM, BN, WM, WN, TM, TN, (int)sizeof(ring)>(
+      acc, reinterpret_cast<char*>(ring), tw);
+}
+
+// Ping-pong variant for 256 x 256 tiles with 16-byte scale-group loads: eight
+// waves, two per SIMD (waves w and w + 4), in two groups: waves 0-3 own rows
+// 0-127 of the tile, waves 4-7 rows 128-255, each wave 128 x 64 of C.  Every
+// K-step is a load phase L (read the step's fragments of both K-halves and its
+// scales into registers, wait for them) and a compute phase C (the step's 16
+// MFMAs, with this wave's share of the global -> LDS loads three steps ahead
+// issued between them, one per four MFMAs), each ended by a workgroup barrier.
+// Group 1 starts one barrier late, so while one wave of a SIMD runs its MFMAs
+// the other reads its fragments: the MFMA pipe alternates between the two
+// waves' bursts, and no wave needs a second set of fragment registers.  The
+// loads are spread over the MFMA bursts because the address unit moves about
+// 64 bytes per clock per CU (a 1 KB load takes ~16 of the 32 clocks of an
+// MFMA): issued all at once they stall the issuing waves for hundreds of
+// clocks (measured), spread out they cost a few clocks each.
+// Barriers: 0 ends the prologue; group 0's L(j) runs between barriers 2j and
+// 2j+1 and its C(j) between 2j+1 and 2j+2, group 1 one barrier later.  Stage j
+// of the ring is read in L(j) by both groups, so by barrier 2j+2; the load of
+// step j+3 into the stage of step j-1 is issued in C(j), after barrier 2j+1.
+// Each wave waits for its own share of step j+1 at the end of its L(j), by
+// barrier 2j+2 at the latest, before any wave reads that stage.
+__global__ __launch_bounds__(512) void k_gemm_pp(
+    const uint8_t* __restrict__ A0, const uint8_t* __restrict__ SA0, const uint8_t* __restrict__ B0,
+    const uint8_t* __restrict__ SB0, int64_t N0, int64_t K0, float alpha0, float* __restrict__ C0,
+    int64_t ldc0, int64_t b_stride_codes, int64_t b_stride_scales, GemmGroups gg, GemmSplit sp) {
+  constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NW = 8;
+  constexpr int TM = 4, TN = 2;  // 32 x 32 MFMA tiles per wave along m and n
+  constexpr int LA = 2, LB = 2;  // code DMAs per wave per step (16 rows each)
+  constexpr int LC = LA + LB;
+  static_assert(LA * NW * 16 == BM && LB * NW * 16 == BN, "tile/wave mismatch");
+  __shared__ StageLds<BM, BN, kScGroup> ring[4];
+  __shared__ ScaleGroupLds<BM, BN> sg[2];
+
+  const TileWork tw = tile_work<BM, BN, false>(A0, SA0, B0, SB0, N0, K0, alpha0, C0, ldc0,
+                                               b_stride_codes, b_stride_scales, gg, sp,
+                                               GemmPlain{});
+  const int64_t kc_bytes = tw.kc_bytes;
+  const int KT = tw.KT, tail_kb = tw.tail_kb;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;           // 0: rows 0-127, 1: rows 128-255
+  const int wm_off = grp * (BM / WM);
+  const int wn_off = (wave & 3) * (BN / WN);
+  const int lr = lane & 31;            // MFMA operand row of this lane
+  const int lh = lane >> 5;            // which 32-block of the instruction's 64 K-values
+
+  // DMA sources: rows clamped into memory (rows past the tile feed outputs
+  // that are never stored)
+  const int dr = lane >> 2;
+  const int dc = (lane & 3) ^ ((dr >> 2) & 3);
+  const uint8_t* a_src[LA];
+  const uint8_t* b_src[LB];
 #pragma unroll
-    for (int p = 0; p < TM / PB; ++p) {
+  for (int j = 0; j < LA; ++j) {
+    const int64_t row = lmin(tw.m0 + (wave * LA + j) * 16 + dr, tw.a_last);
+    a_src[j] = tw.A + row * tw.ldk + tw.k0 / 2 + dc * 16;
+  }
 #pragma unroll
-      for (int bb = 0; bb < PB; ++bb) {
-        const int b = PB * p + bb;
-        const int rl = bb * 32 + lr;
+  for (int j = 0; j < LB; ++j) {
+    const int64_t row = lmin(tw.n0 + (wave * LB + j) * 16 + dr, tw.N - 1);
+    b_src[j] = tw.B + row * tw.ldk + tw.k0 / 2 + dc * 16;
+  }
+  // the same sources as 32-bit offsets from the tile's first row at the range's
+  // first K byte (the host guarantees 256 rows of either operand span < 2^31 B)
+  const uint8_t* a_base = tw.A + tw.m0 * tw.ldk + tw.k0 / 2;
+  const uint8_t* b_base = tw.B + tw.n0 * tw.ldk + tw.k0 / 2;
+  uint32_t a_off[LA], b_off[LB];
 #pragma unroll
-        for (int a = 0; a < TN; ++a)
+  for (int j = 0; j < LA; ++j)
+    a_off[j] = (uint32_t)(a_src[j] - a_base);
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int ch = a * 8 + gq * 2 + lh;
-            *reinterpret_cast<float4*>(stg + rl * RB + ((ch ^ (rl & 15)) * 16)) =
-                make_float4(acc[a][b][4 * gq] * alpha, acc[a][b][4 * gq + 1] * alpha,
-                            acc[a][b][4 * gq + 2] * alpha, acc[a][b][4 * gq + 3] * alpha);
-          }
+  for (int j = 0; j < LB; ++j)
+    b_off[j] = (uint32_t)(b_src[j] - b_base);
+  // scale group job of this wave: 64 rows (lane = row) of A (waves 0-3) or B
+  const bool s_isA = wave < 4;
+  const int s_r0 = (wave & 3) * 64;
+  const uint8_t* s_src =
+      s_isA ? tw.SA + lmin(tw.m0 + s_r0 + lane, tw.a_last) * tw.lds_a + tw.k0 / 32
+            : tw.SB + lmin(tw.n0 + s_r0 + lane, tw.N - 1) * tw.lds_b + tw.k0 / 32;
+
+  auto issue = [&](int kt, auto S) {
+    constexpr int P = decltype(S)::value;
+    const int64_t kc = (int64_t)kt * 64;
+    const int64_t coff = lmin(kc, lmax(kc_bytes - 16 - dc * 16, -dc * 16));
+#pragma unroll
+    for (int j = 0; j < LA; ++j) dma16(a_src[j] + coff, &ring[P].a.codes[((wave * LA + j) * 16) * 4]);
+#pragma unroll
+    for (int j = 0; j < LB; ++j) dma16(b_src[j] + coff, &ring[P].b.codes[((wave * LB + j) * 16) * 4]);
+  };
+  auto issue_scales = [&](int g) {
+    ScaleGroupLds<BM, BN>& t = sg[g & 1];
+    dma16(s_src + (int64_t)g * 16, s_isA ? &t.a[s_r0] : &t.b[s_r0]);
+  };
+
+  v16f acc[TN][TM];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  // fragments of the current step (both K-halves), the scale groups of the
+  // current four steps and the current step's scale dwords
+  uint4 fa[2][TM], fb[2][TN], ga[TM], gb[TN];
+  uint32_t sa[TM], sb[TN];
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  auto barrier_lds = [&]() {  // this wave's LDS reads landed, then barrier
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // phase L(j), j % 4 == P: fragments and scales of step j, then the waits
+  auto load_phase = [&](int kt, auto S, auto FULL) {
+    constexpr int P = decltype(S)::value;
+    constexpr bool F = decltype(FULL)::value;
+    if (P == 0) {
+      const ScaleGroupLds<BM, BN>& t = sg[(kt >> 2) & 1];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) ga[i] = t.a[wm_off + i * 32 + lr];
+#pragma unroll
+      for (int i = 0; i < TN; ++i) gb[i] = t.b[wn_off + i * 32 + lr];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kb = 2 * h + lh;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm_off + i * 32 + lr;
+        fa[h][i] = ring[P].a.codes[row * 4 + (kb ^ ((row >> 2) & 3))];
       }
-#pragma unroll 4
-      for (int it = 0; it < PR / RPI; ++it) {
-        const int rl = it * RPI + lane / CH, ch = lane % CH;
-        const float4 v =
-            *reinterpret_cast<const float4*>(stg + rl * RB + ((ch ^ (rl & 15)) * 16));
-        const int mrow = wm_off + p * PR + rl;
-        const int ncol = wn_off + ch * 4;
-        if (mrow < rows_valid) {
-          float* crow = C + (m0 + mrow) * ldc + n0;
-          if (ncol + 3 < cols_valid) {
-            store_c4(crow + ncol, v, stream_c);
-          } else {
-            if (ncol + 0 < cols_valid) crow[ncol + 0] = v.x;
-            if (ncol + 1 < cols_valid) crow[ncol + 1] = v.y;
-            if (ncol + 2 < cols_valid) crow[ncol + 2] = v.z;
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        const int row = wn_off + i * 32 + lr;
+        fb[h][i] = ring[P].b.codes[row * 4 + (kb ^ ((row >> 2) & 3))];
+      }
+    }
+    // this wave's share of step kt + 1 (issued in C(kt - 2), or by the
+    // prologue) has landed, and with it the scale group issued before it;
+    // vector-memory instructions issued after it: the loads of step kt + 2
+    // (in C(kt - 1)) and the scale groups issued in C(kt - 2) after that
+    // step's loads and in C(kt - 1) (one per four steps)
+    if constexpr (F) {
+      wait_vmcnt<LC + ((P == 1 || P == 2) ? 1 : 0)>();
+    } else {
+      if (kt + 2 < KT) wait_vmcnt<LC>();
+      else wait_vmcnt<0>();
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa[i] = reinterpret_cast<const uint32_t*>(&ga[i])[P] >> (8 * lh);
+#pragma unroll
+    for (int i = 0; i < TN; ++i) sb[i] = reinterpret_cast<const uint32_t*>(&gb[i])[P] >> (8 * lh);
+    if (!F && kt == KT - 1) {
+      // 32-blocks past K in the last step: zero A's codes, neutral scales (127)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (2 * h + lh >= tail_kb) {
+          const uint32_t keep = h ? 0x0000FFFFu : 0xFFFF0000u;
+          const uint32_t neutral = h ? 0x007F0000u : 0x0000007Fu;
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            fa[h][i] = make_uint4(0, 0, 0, 0);
+            sa[i] = (sa[i] & keep) | neutral;
           }
+#pragma unroll
+          for (int i = 0; i < TN; ++i) sb[i] = (sb[i] & keep) | neutral;
         }
       }
     }
+    barrier_lds();
+  };
+  // MFMA i of a step: K-half i / 8, tile (a, b) = ((i % 8) / TM, i % TM)
+  auto mfma_i = [&](auto I) {
+    constexpr int i = decltype(I)::value;
+    constexpr int h = i / (TM * TN), a = (i % (TM * TN)) / TM, b = i % TM;
+    acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        as_v8i(fb[h][a]), as_v8i(fa[h][b]), acc[a][b], kFmtFp4, kFmtFp4, h ? 2 : 0,
+        (int)sb[a], h ? 2 : 0, (int)sa[b]);
+  };
+  // phase C(j): the 16 MFMAs of step j with this wave's loads of step j + 3
+  // after MFMAs 0, 4, 8 and 12 and, every four steps, its scale-group load
+  // after MFMA 14.  FULL steps load at a uniform K offset from SGPR bases; the
+  // last steps clamp each lane's column into the row.
+  auto compute_phase = [&](int kt, auto S, auto FULL) {
+    constexpr int P = decltype(S)::value;
+    constexpr bool F = decltype(FULL)::value;
+    constexpr int S3 = (P + 3) % 4;
+    const bool load = F || kt + 3 < KT;
+    const int64_t kc = (int64_t)(kt + 3) * 64;
+    const int64_t coff = lmin(kc, lmax(kc_bytes - 16 - dc * 16, -dc * 16));
+    const uint8_t* ak = a_base + kc;
+    const uint8_t* bk = b_base + kc;
+    auto load_a = [&](int j) {
+      if (F) dma16s(ak, a_off[j], &ring[S3].a.codes[((wave * LA + j) * 16) * 4]);
+      else if (load) dma16(a_src[j] + coff, &ring[S3].a.codes[((wave * LA + j) * 16) * 4]);
+    };
+    auto load_b = [&](int j) {
+      if (F) dma16s(bk, b_off[j], &ring[S3].b.codes[((wave * LB + j) * 16) * 4]);
+      else if (load) dma16(b_src[j] + coff, &ring[S3].b.codes[((wave * LB + j) * 16) * 4]);
+    };
+    auto one = [&](auto I) {
+      constexpr int i = decltype(I)::value;
+      mfma_i(I);
+      if constexpr (i % 4 == 0 || i == 14) {
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (i == 0 || i == 4) load_a(i / 4);
+        if constexpr (i == 8 || i == 12) load_b(i / 4 - 2);
+        if constexpr (i == 14) {
+          if (P == 0 && (F || kt + 4 < KT)) issue_scales((kt >> 2) + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    static_assert(TM * TN * 2 == 16 && LA == 2 && LB == 2, "load placement");
+    using std::integral_constant;
+    one(integral_constant<int, 0>{});
+    one(integral_constant<int, 1>{});
+    one(integral_constant<int, 2>{});
+    one(integral_constant<int, 3>{});
+    one(integral_constant<int, 4>{});
+    one(integral_constant<int, 5>{});
+    one(integral_constant<int, 6>{});
+    one(integral_constant<int, 7>{});
+    one(integral_constant<int, 8>{});
+    one(integral_constant<int, 9>{});
+    one(integral_constant<int, 10>{});
+    one(integral_constant<int, 11>{});
+    one(integral_constant<int, 12>{});
+    one(integral_constant<int, 13>{});
+    one(integral_constant<int, 14>{});
+    one(integral_constant<int, 15>{});
+    barrier();
+  };
+
+  // prologue: scale group 0 and steps 0-2 issued; step 0 and the group landed
+  if (0 < KT) issue_scales(0);
+  if (0 < KT) issue(0, I0{});
+  if (1 < KT) issue(1, I1{});
+  if (2 < KT) issue(2, I2{});
+  if (2 < KT) wait_vmcnt<2 * LC>();
+  else if (1 < KT) wait_vmcnt<LC>();
+  else wait_vmcnt<0>();
+  barrier();
+  if (grp == 1) barrier();  // group 1 runs one phase behind group 0
+
+  using Full = std::true_type;
+  using Part = std::false_type;
+  int kt = 0;
+  for (; kt + 7 < KT; kt += 4) {
+    load_phase(kt, I0{}, Full{});
+    compute_phase(kt, I0{}, Full{});
+    load_phase(kt + 1, I1{}, Full{});
+    compute_phase(kt + 1, I1{}, Full{});
+    load_phase(kt + 2, I2{}, Full{});
+    compute_phase(kt + 2, I2{}, Full{});
+    load_phase(kt + 3, I3{}, Full{});
+    compute_phase(kt + 3, I3{}, Full{});
   }
+  for (; kt < KT; kt += 4) {
+    load_phase(kt, I0{}, Part{});
+    compute_phase(kt, I0{}, Part{});
+    if (kt + 1 < KT) {
+      load_phase(kt + 1, I1{}, Part{});
+      compute_phase(kt + 1, I1{}, Part{});
+    }
+    if (kt + 2 < KT) {
+      load_phase(kt + 2, I2{}, Part{});
+      compute_phase(kt + 2, I2{}, Part{});
+    }
+    if (kt + 3 < KT) {
+      load_phase(kt + 3, I3{}, Part{});
+      compute_phase(kt + 3, I3{}, Part{});
+    }
+  }
+  if (grp == 0) barrier();  // both groups have now passed 2 KT + 2 barriers
+
+  store_tile_impl<BM, BN, WM, WN, TM, TN, (int)sizeof(ring)>(acc, reinterpret_cast<char*>(ring),
+                                                              tw);
 }
 
 // ---------------------------------------------------------------- host side
@@ -653,6 +1002,35 @@ static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
   if (total == 0) return MX_OK;
   k_gemm_mx<BM, BN, WM, WN, STAGES, SC, false><<<dim3(total), dim3(WM * WN * 64), 0, st>>>(
       a, sa, b, sb, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, gg, sp, GemmPlain{});
+  return launch_status();
+}
+
+// The ping-pong kernel for 256 x 256 tiles with group scale loads (no paired
+// second product).
+static int launch_gemm_pp(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
+                          const uint8_t* sb, const int64_t* offs, int64_t groups, int64_t N,
+                          int64_t K, float alpha, float* c, int64_t ldc, int64_t b_stride_codes,
+                          int64_t b_stride_scales, int64_t lds_a, int64_t lds_b, GemmSplit sp,
+                          hipStream_t st) {
+  constexpr int64_t kMaxWg = 0xFFFFFFFFll / 512;
+  int64_t t64 = 0;
+  for (int64_t g = 0; g < groups; ++g) t64 += cdiv(offs[g + 1] - offs[g], 256) * cdiv(N, 256);
+  if (t64 * sp.n > kMaxWg) return MX_ERR_SHAPE;
+  GemmGroups gg;
+  gg.ngroups = (int)groups;
+  gg.tiles_n = (int)cdiv(N, 256);
+  gg.lds_a = lds_a;
+  gg.lds_b = lds_b;
+  gg.tile_start[0] = 0;
+  for (int64_t g = 0; g < groups; ++g) {
+    gg.row_off[g] = offs[g];
+    gg.tile_start[g + 1] = gg.tile_start[g] + (int)(cdiv(offs[g + 1] - offs[g], 256) * gg.tiles_n);
+  }
+  gg.row_off[groups] = offs[groups];
+  const int total = gg.tile_start[groups] * sp.n;
+  if (total == 0) return MX_OK;
+  k_gemm_pp<<<dim3(total), dim3(512), 0, st>>>(a, sa, b, sb, N, K, alpha, c, ldc, b_stride_codes,
+                                                b_stride_scales, gg, sp);
   return launch_status();
 }
 
@@ -711,6 +1089,10 @@ static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
     // group-mode scale loads leave registers for eight waves (two per SIMD, 128 x 64
     // per wave: one wave's LDS waits and barrier overlap the other's MFMAs); the
     // other modes keep four waves, where eight would spill in the K loop
+    // the ping-pong kernel addresses 256 rows of an operand with 32-bit offsets
+    if (sc == kScGroup && 256 * (K / 2) < ((int64_t)1 << 31))
+      return launch_gemm_pp(a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes,
+                            b_stride_scales, lds_a, lds_b, sp, st);
     if (sc == kScGroup) return launch_gemm<256, 256, 2, 4, kScGroup>(MX_GEMM_ARGS);
     if (sc == kScDword) return launch_gemm<256, 256, 2, 2, kScDword>(MX_GEMM_ARGS);
     if (sc == kScShort) return launch_gemm<256, 256, 2, 2, kScShort>(MX_GEMM_ARGS);
