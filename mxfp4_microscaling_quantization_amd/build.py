@@ -34,6 +34,25 @@ HIP_FLAGS = [
 ]
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the same
+# sources (device code untouched): the CPU ABI tests run the argument checks
+# of every entry point against it.  It is loaded with the sanitizer runtime
+# preloaded, never by the product path.
+SAN_BUILD = BUILD / "san"
+SAN_LIB = SAN_BUILD / "libmx355_san.so"
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def sanitizer_runtime() -> Path:
+    """The clang AddressSanitizer runtime that a sanitized library needs preloaded."""
+    res = subprocess.run([hipcc(), "-print-resource-dir"], capture_output=True, text=True)
+    rt = Path(res.stdout.strip()) / "lib" / "linux" / "libclang_rt.asan-x86_64.so"
+    if not rt.exists():
+        raise RuntimeError(f"sanitizer runtime not found at {rt}")
+    return rt
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -41,9 +60,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the MXFP4 HIP library cannot be built")
 
 
-def _compile(src: str) -> Path:
-    obj = BUILD / (Path(src).stem + ".o")
-    cmd = [hipcc(), *HIP_FLAGS, "-c", str(CSRC / src), "-o", str(obj)]
+def _compile(src: str, sanitize: bool = False) -> Path:
+    out = SAN_BUILD if sanitize else BUILD
+    obj = out / (Path(src).stem + ".o")
+    cmd = [hipcc(), *HIP_FLAGS, *(SAN_FLAGS if sanitize else []), "-c", str(CSRC / src), "-o",
+           str(obj)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
@@ -52,19 +73,36 @@ def _compile(src: str) -> Path:
     return obj
 
 
+def _link(objs, lib: Path, extra=()) -> None:
+    tmp = lib.with_suffix(".so.tmp")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, "-o", str(tmp),
+           *map(str, objs)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, lib)
+
+
 def build(verbose: bool = True) -> Path:
     BUILD.mkdir(exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB.with_suffix(".so.tmp")
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs)]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    _link(objs, LIB)
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+def build_sanitized(verbose: bool = True) -> Path:
+    """The host-sanitized library (see SAN_FLAGS); the sanitizer runtime is not
+    linked in and must be preloaded (sanitizer_runtime())."""
+    SAN_BUILD.mkdir(parents=True, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(lambda src: _compile(src, True), SOURCES))
+    _link(objs, SAN_LIB, ["-shared-libsan"])
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
 
 
 if __name__ == "__main__":
