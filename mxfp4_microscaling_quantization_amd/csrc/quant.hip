@@ -245,7 +245,10 @@ __device__ __forceinline__ uint4 quant_col32(float v[32], uint32_t& byte_out, ui
 // Writes staged column-block codes/scales: output row (col0 + c) gets bytes
 // [row0/2, row0/2 + 16 nrb) of codes and [row0/32, row0/32 + nrb) of scales
 // (scale rows ld_s bytes apart, at least rows / 32), for c < ncols; staging
-// layout [c][rb], NRB row blocks per column.
+// layout [c][rb], NRB row blocks per column.  A column's scale bytes are
+// contiguous in its output row, so whole tiles write them as 32-bit words
+// (one store per four row blocks instead of four byte stores) when the scale
+// rows allow it.
 template <int NC, int NRB>
 __device__ __forceinline__ void store_col_tile(const uint4* s_codes, const uint8_t* s_scales,
                                                int64_t rows, int64_t ld_s, int64_t col0,
@@ -255,9 +258,23 @@ __device__ __forceinline__ void store_col_tile(const uint4* s_codes, const uint8
   const int64_t ld_c = rows / 2;
   for (int i = threadIdx.x; i < NC * NRB; i += blockDim.x) {
     const int c = i / NRB, rb = i % NRB;
-    if (c < ncols && rb < nrb) {
+    if (c < ncols && rb < nrb)
       *reinterpret_cast<uint4*>(codes + (col0 + c) * ld_c + row0 / 2 + rb * 16) = s_codes[i];
-      scales[(col0 + c) * ld_s + row0 / 32 + rb] = s_scales[i];
+  }
+  uint8_t* const s0 = scales + col0 * ld_s + row0 / 32;
+  const bool words = NRB % 4 == 0 && nrb == NRB && ld_s % 4 == 0 &&
+                     (reinterpret_cast<uintptr_t>(s0) & 3) == 0;  // uniform over the workgroup
+  if (words) {
+    constexpr int W = NRB / 4;  // scale words per column
+    const uint32_t* sw = reinterpret_cast<const uint32_t*>(s_scales);
+    for (int i = threadIdx.x; i < NC * W; i += blockDim.x) {
+      const int c = i / W, w = i % W;
+      if (c < ncols) *reinterpret_cast<uint32_t*>(s0 + c * ld_s + 4 * w) = sw[i];
+    }
+  } else {
+    for (int i = threadIdx.x; i < NC * NRB; i += blockDim.x) {
+      const int c = i / NRB, rb = i % NRB;
+      if (c < ncols && rb < nrb) s0[c * ld_s + rb] = s_scales[i];
     }
   }
 }
@@ -417,7 +434,7 @@ __global__ __launch_bounds__(256) void k_requant(const RqJob j0, const RqJob j1,
                                                  int64_t cols, const Segs segs) {
   constexpr int NRB = kRqR / 32;
   __shared__ uint4 s_codes[kRqC * NRB];
-  __shared__ uint8_t s_scales[kRqC * NRB];
+  __shared__ __align__(16) uint8_t s_scales[kRqC * NRB];
 
   const bool second = (int)blockIdx.y >= ty0;   // uniform over the workgroup
   const RqJob& job = second ? j1 : j0;
@@ -508,7 +525,7 @@ __global__ __launch_bounds__(256) void k_requant_rht(const RhtJobs jobs, int64_t
   constexpr int NRB = kRhtR / 32;
   __shared__ float s_x[kRhtR * kRhtC];  // [row][col]
   __shared__ uint4 s_codes[kRhtC * NRB];
-  __shared__ uint8_t s_scales[kRhtC * NRB];
+  __shared__ __align__(16) uint8_t s_scales[kRhtC * NRB];
 
   const bool t = (int)blockIdx.y >= jobs.ty0;  // uniform over the workgroup
   const uint8_t* __restrict__ codes_in = t ? jobs.codes_in1 : jobs.codes_in0;
