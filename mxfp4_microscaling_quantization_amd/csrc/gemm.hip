@@ -31,6 +31,7 @@
 
 #include <type_traits>
 
+#include "gemm_schedule.h"
 #include "mx_host.h"
 
 namespace mx {
@@ -182,7 +183,7 @@ __device__ __forceinline__ void dma1(const void* g, void* lds) {
 // kScShort -- K/32 % 2 == 0: two 2-byte loads per row and step, layout [2][rows]
 // dwords (bytes 0-1 and 2-3 of the step);
 // kScByte -- otherwise: one byte per row and step, layout [4][rows] dwords.
-enum { kScGroup = 0, kScDword = 1, kScByte = 2, kScShort = 3 };
+// (the mode constants kScGroup .. kScShort live in gemm_schedule.h)
 
 template <int ROWS, int SC>
 struct TileLds {
@@ -372,6 +373,8 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
   // share a CU.
   static_assert((STAGES == 4 || (STAGES == 3 && SC != kScGroup)) && 2 * LC + QW < 64,
                 "pipeline depth");
+  static_assert(mx_schedule_listed(BM, BN, NW, SC, LC, QW),
+                "tile configuration missing from the schedule table of gemm_schedule.h");
 
   // The LDS ring (contiguous, reused by the epilogue); every access uses a
   // compile-time stage index (with three stages, index 3 is on paths a short
@@ -696,6 +699,9 @@ __global__ __launch_bounds__(512) void k_gemm_pp(
   constexpr int LA = 2, LB = 2;  // code DMAs per wave per step (16 rows each)
   constexpr int LC = LA + LB;
   static_assert(LA * NW * 16 == BM && LB * NW * 16 == BN, "tile/wave mismatch");
+  static_assert(kPpLoads == LC && kPpGroupLoads == 1 && kPpLead == 3 && kPpWaitNear == LC &&
+                    kPpWaitFirst[0] == 0 && kPpWaitFirst[1] == LC && kPpWaitFirst[2] == 2 * LC,
+                "schedule constants of gemm_schedule.h");
   __shared__ StageLds<BM, BN, kScGroup> ring[4];
   __shared__ ScaleGroupLds<BM, BN> sg[2];
 
@@ -822,9 +828,10 @@ __global__ __launch_bounds__(512) void k_gemm_pp(
     // (in C(kt - 1)) and the scale groups issued in C(kt - 2) after that
     // step's loads and in C(kt - 1) (one per four steps)
     if constexpr (F) {
-      wait_vmcnt<LC + ((P == 1 || P == 2) ? 1 : 0)>();
+      static_assert(kPpWaitFull[P] == LC + ((P == 1 || P == 2) ? 1 : 0), "schedule constants");
+      wait_vmcnt<kPpWaitFull[P]>();
     } else {
-      if (kt + 2 < KT) wait_vmcnt<LC>();
+      if (kt + 2 < KT) wait_vmcnt<kPpWaitNear>();
       else wait_vmcnt<0>();
     }
 #pragma unroll
@@ -918,9 +925,9 @@ __global__ __launch_bounds__(512) void k_gemm_pp(
   if (0 < KT) issue(0, I0{});
   if (1 < KT) issue(1, I1{});
   if (2 < KT) issue(2, I2{});
-  if (2 < KT) wait_vmcnt<2 * LC>();
-  else if (1 < KT) wait_vmcnt<LC>();
-  else wait_vmcnt<0>();
+  if (2 < KT) wait_vmcnt<kPpWaitFirst[2]>();
+  else if (1 < KT) wait_vmcnt<kPpWaitFirst[1]>();
+  else wait_vmcnt<kPpWaitFirst[0]>();
   barrier();
   if (grp == 1) barrier();  // group 1 runs one phase behind group 0
 
