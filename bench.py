@@ -36,33 +36,106 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_FP4_TFLOPS = 10100.0
 # HBM bytes per GEMM launch (mean of the fwd, dX and dW launches of the step),
 # from rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB copy, valid for
-# the GEMM code with this sha256 only (of the source with comments and blank
-# lines removed; the per-launch table is kept with the committed profiles).
-GEMM_TRAFFIC = {"sha256": "765fa4d8343c4c33e630c12dd96af4cf19aafb89b7071a77624161b0642e7bb8",
-                "bytes_per_launch": 685656425}
+# the GEMM code with this sha256 only (of gemm.hip and gemm_schedule.h with
+# comments and blank lines removed; the per-launch table is kept with the
+# committed profiles).
+GEMM_TRAFFIC = {"sha256": "c4ca9497e5686f5e352f3f763e1799c2e7acdad77a4170cb4b6df9bfde6eba29",
+                 "bytes_per_launch": 668428405}
+GEMM_SOURCES = ("gemm.hip", "gemm_schedule.h")
+
+# VALU work per element of the stochastic-rounding kernels, valid for the
+# quantizer code with this sha256 only (quant.hip and mx_device.h, comments and
+# blank lines removed): `lane_ops` = SQ_INSTS_VALU x 64 lanes / elements from a
+# rocprofv3 counter run on the 8192^2 bf16 sweep; `counts` = the multi-cycle
+# instructions in the kernel's assembly, `elems` = elements one lane converts per
+# pass over that code.  Each such instruction occupies its SIMD VALU_COST times
+# as long as a simple one (measured by tests/valu_rate_probe.hip), so it adds
+# VALU_COST - 1 lane-op equivalents.
+QUANT_VALU = {"sha256": "cdc029b5fd1eafcbc56b5d50fa0bc38e353b5076194fc84610f53b1649905ffe",
+               "per_elem": {
+    "row_sr": {"kernel": "k_quant_row<bf16, SR>", "lane_ops": 16.78, "elems": 32,
+               "counts": {"v_mul_lo_u32": 65, "v_mad_u64_u32": 35, "v_lshrrev_b64": 32,
+                          "v_cvt_scalef32_sr_pk_fp4_f32": 32}},
+    "col_sr": {"kernel": "k_quant_tile<bf16, SR>", "lane_ops": 16.84, "elems": 64,
+               "counts": {"v_mul_lo_u32": 154, "v_mad_u64_u32": 79, "v_lshrrev_b64": 64,
+                          "v_cvt_scalef32_sr_pk_fp4_f32": 64}},
+    "dual_sr": {"kernel": "k_quant_tile<bf16, SR, row + column>", "lane_ops": 33.68, "elems": 64,
+                "counts": {"v_mul_lo_u32": 330, "v_mad_u64_u32": 167, "v_lshrrev_b64": 137,
+                           "v_cvt_scalef32_sr_pk_fp4_f32": 128}},
+    "requant_sr": {"kernel": "k_requant<SR>", "lane_ops": 19.16, "elems": 128,
+                   "counts": {"v_mul_lo_u32": 396, "v_mad_u64_u32": 202, "v_lshrrev_b64": 130,
+                              "v_cvt_scalef32_sr_pk_fp4_f32": 128}},
+}}
+# SIMD cycles per wave64 instruction relative to v_add_u32 (2 cycles), at four
+# waves per SIMD.
+VALU_COST = {"v_mul_lo_u32": 1.67, "v_mad_u64_u32": 2.03, "v_lshrrev_b64": 1.64,
+             "v_cvt_scalef32_sr_pk_fp4_f32": 4.74}
+QUANT_SOURCES = ("quant.hip", "mx_device.h")
+# 256 CUs x 4 SIMDs x 32 lanes per clock (one wave64 instruction every 2 cycles)
+# x 2.4 GHz
+PEAK_VALU_LANE_OPS = 78.6e12
 
 
-def gemm_code_sha256(path):
-    """sha256 of a C++ source with // comments and blank lines removed, so that
+def weighted_lane_ops(c):
+    """Lane-op equivalents per element: VALU lane-ops plus the extra SIMD time of
+    the multi-cycle instructions."""
+    extra = sum(n / c["elems"] * (VALU_COST[k] - 1.0) for k, n in c["counts"].items())
+    return c["lane_ops"] + extra
+
+
+def code_sha256(paths):
+    """sha256 of C++ sources with // comments and blank lines removed, so that
     only code changes (not documentation edits) change it."""
     import hashlib
     import re
     lines = []
-    for line in open(path, encoding="utf-8").read().splitlines():
-        line = re.sub(r"//.*$", "", line).rstrip()
-        if line.strip():
-            lines.append(line)
+    for path in paths:
+        for line in open(path, encoding="utf-8").read().splitlines():
+            line = re.sub(r"//.*$", "", line).rstrip()
+            if line.strip():
+                lines.append(line)
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
+def csrc(*names):
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                     "mxfp4_microscaling_quantization_amd", "csrc")
+    return [os.path.join(d, n) for n in names]
+
+
 def gemm_traffic():
-    src = os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                       "mxfp4_microscaling_quantization_amd", "csrc", "gemm.hip")
     try:
-        h = gemm_code_sha256(src)
+        h = code_sha256(csrc(*GEMM_SOURCES))
     except OSError:
         return None
     return GEMM_TRAFFIC["bytes_per_launch"] if h == GEMM_TRAFFIC["sha256"] else None
+
+
+def alu_roofline(sweep):
+    """ALU roofline of the stochastic-rounding kernels on the 8192^2 sweep:
+    weighted lane-op equivalents per element x elements / kernel time against the
+    78.6 T lane-op/s VALU peak (`frac`), and the plain VALU issue fraction
+    (`issue_frac`, lane-ops only); null when the quantizer code changed since the
+    counts were taken."""
+    try:
+        if code_sha256(csrc(*QUANT_SOURCES)) != QUANT_VALU["sha256"]:
+            return None
+    except OSError:
+        return None
+    n = 8192 * 8192
+    out = {}
+    for key, c in QUANT_VALU["per_elem"].items():
+        if key not in sweep:
+            continue
+        t = sweep[key]["us"] * 1e-6
+        w = weighted_lane_ops(c)
+        out[key] = {"kernel": c["kernel"], "bound": "alu", "unit": "T lane-op/s",
+                    "achieved": round(w * n / t / 1e12, 2), "peak": PEAK_VALU_LANE_OPS / 1e12,
+                    "frac": round(w * n / t / PEAK_VALU_LANE_OPS, 4),
+                    "issue_frac": round(c["lane_ops"] * n / t / PEAK_VALU_LANE_OPS, 4),
+                    "lane_ops_per_elem": c["lane_ops"], "weighted_per_elem": round(w, 2),
+                    "hbm_frac": round(sweep[key]["frac_hbm"], 4)}
+    return out
 
 
 METRIC = "MXFP4 quantize GB/s + MXFP4 linear fwd+bwd TFLOP/s (%roofline), 1 MI355X"
@@ -609,12 +682,14 @@ def main():
         "config": {"workload": "llama3-8b-mlp-up-proj-linear-fwd-bwd", "M": lin["M"],
                    "N": lin["N"], "K": lin["K"], "input_dtype": "bf16",
                    "parallelism": "single-gpu"},
-        "roofline": {"kernel": "k_gemm_mx (MXFP4 GEMM, 2MNK per launch)", "bound": "mfma",
+        "roofline": {"kernel": "k_gemm_pp (MXFP4 GEMM, 256x256 tiles, 2MNK per launch)",
+                     "bound": "mfma",
                      "achieved": round(ach, 2), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / PEAK_FP4_TFLOPS, 4), "traffic": gemm_traffic()},
         "cpu_baseline": cpu,
         "quantize_GBps": {k: round(v["GBps"], 1) for k, v in
                           parts.get("quantizer_sweep_8192sq_bf16", {}).items()},
+        "alu_roofline": alu_roofline(parts.get("quantizer_sweep_8192sq_bf16", {})),
         "parts": parts,
     }
     print(json.dumps(line))

@@ -83,13 +83,31 @@ def _link(objs, lib: Path, extra=()) -> None:
     os.replace(tmp, lib)
 
 
+# The VALU issue-rate probe (a stand-alone program, not part of the library):
+# its figures weight the quantizers' instruction counts in the ALU roofline.
+PROBE_SRC = ROOT / "tests" / "valu_rate_probe.hip"
+PROBE = BUILD / "valu_rate_probe"
+
+
+def build_probe() -> Path:
+    BUILD.mkdir(exist_ok=True)
+    cmd = [hipcc(), *[f for f in HIP_FLAGS if not f.startswith("-I")], str(PROBE_SRC), "-o",
+           str(PROBE)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC.name}:\n{' '.join(cmd)}\n{res.stderr}")
+    return PROBE
+
+
 def build(verbose: bool = True) -> Path:
     BUILD.mkdir(exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES) + 1, os.cpu_count() or 4)) as ex:
+        probe = ex.submit(build_probe)
         objs = list(ex.map(_compile, SOURCES))
+        probe.result()
     _link(objs, LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE}")
     return LIB
 
 

@@ -47,7 +47,7 @@ def test_attainable_time_of_the_deit_layer():
     assert abs(bench.linear_attainable_ms(M, N, K) - want_ms) < 1e-12
 
 
-def test_gemm_code_hash_ignores_comments_only(tmp_path):
+def test_code_hash_ignores_comments_only(tmp_path):
     sys.path.insert(0, ROOT)
     import bench
     a = tmp_path / "a.hip"
@@ -56,5 +56,29 @@ def test_gemm_code_hash_ignores_comments_only(tmp_path):
     a.write_text("int f() {\n  return 1;  // one\n}\n")
     b.write_text("// header\n\nint f() {\n  return 1;\n}\n\n")
     c.write_text("int f() {\n  return 2;\n}\n")
-    assert bench.gemm_code_sha256(a) == bench.gemm_code_sha256(b)
-    assert bench.gemm_code_sha256(a) != bench.gemm_code_sha256(c)
+    assert bench.code_sha256([a]) == bench.code_sha256([b])
+    assert bench.code_sha256([a]) != bench.code_sha256([c])
+    assert bench.code_sha256([a, c]) != bench.code_sha256([c, a])
+
+
+def test_alu_roofline_weights_multi_cycle_instructions():
+    """Weighted lane-op equivalents per element are the VALU lane-ops plus, for
+    each multi-cycle instruction, its count per element times its extra cost;
+    the figure is withheld when the quantizer code no longer matches the counted
+    one."""
+    sys.path.insert(0, ROOT)
+    import bench
+    c = {"lane_ops": 10.0, "elems": 32, "counts": {"v_mul_lo_u32": 64, "v_cvt_scalef32_sr_pk_fp4_f32": 16}}
+    want = 10.0 + 2 * (bench.VALU_COST["v_mul_lo_u32"] - 1) + 0.5 * (
+        bench.VALU_COST["v_cvt_scalef32_sr_pk_fp4_f32"] - 1)
+    assert abs(bench.weighted_lane_ops(c) - want) < 1e-12
+    sweep = {k: {"us": 100.0, "frac_hbm": 0.5} for k in bench.QUANT_VALU["per_elem"]}
+    got = bench.alu_roofline(sweep)
+    if bench.code_sha256(bench.csrc(*bench.QUANT_SOURCES)) != bench.QUANT_VALU["sha256"]:
+        assert got is None
+        return
+    for k, c in bench.QUANT_VALU["per_elem"].items():
+        w = bench.weighted_lane_ops(c) * 8192 * 8192 / 100e-6
+        assert abs(got[k]["achieved"] - w / 1e12) < 0.01
+        assert abs(got[k]["frac"] - w / 78.6e12) < 1e-4
+        assert got[k]["issue_frac"] < got[k]["frac"]
