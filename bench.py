@@ -60,6 +60,7 @@ QUANT_VALU = {"sha256": "cdc029b5fd1eafcbc56b5d50fa0bc38e353b5076194fc84610f53b1
                "counts": {"v_mul_lo_u32": 154, "v_mad_u64_u32": 79, "v_lshrrev_b64": 64,
                           "v_cvt_scalef32_sr_pk_fp4_f32": 64}},
     "dual_sr": {"kernel": "k_quant_tile<bf16, SR, row + column>", "lane_ops": 33.68, "elems": 64,
+                "quantizations": 2,
                 "counts": {"v_mul_lo_u32": 330, "v_mad_u64_u32": 167, "v_lshrrev_b64": 137,
                            "v_cvt_scalef32_sr_pk_fp4_f32": 128}},
     "requant_sr": {"kernel": "k_requant<SR>", "lane_ops": 19.16, "elems": 128,
@@ -70,6 +71,11 @@ QUANT_VALU = {"sha256": "cdc029b5fd1eafcbc56b5d50fa0bc38e353b5076194fc84610f53b1
 # waves per SIMD.
 VALU_COST = {"v_mul_lo_u32": 1.67, "v_mad_u64_u32": 2.03, "v_lshrrev_b64": 1.64,
              "v_cvt_scalef32_sr_pk_fp4_f32": 4.74}
+# Time one SR decision per element costs on an 8192^2 tensor with no memory
+# traffic (the library's SplitMix64 words + two stochastic conversions per element
+# pair, in registers; tests/valu_rate_probe.hip): the floor of every stochastic
+# quantization of such a tensor.
+SR_PAIR_FLOOR_US = 23.4
 QUANT_SOURCES = ("quant.hip", "mx_device.h")
 # 256 CUs x 4 SIMDs x 32 lanes per clock (one wave64 instruction every 2 cycles)
 # x 2.4 GHz
@@ -134,6 +140,7 @@ def alu_roofline(sweep):
                     "frac": round(w * n / t / PEAK_VALU_LANE_OPS, 4),
                     "issue_frac": round(c["lane_ops"] * n / t / PEAK_VALU_LANE_OPS, 4),
                     "lane_ops_per_elem": c["lane_ops"], "weighted_per_elem": round(w, 2),
+                    "sr_floor_us": SR_PAIR_FLOOR_US * c.get("quantizations", 1),
                     "hbm_frac": round(sweep[key]["frac_hbm"], 4)}
     return out
 

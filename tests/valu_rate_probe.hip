@@ -5,10 +5,17 @@
 // cycles a SIMD spends per wave-level instruction and the clock follow without
 // knowing the clock in advance; hip events give the chip-wide lane-op rate.
 //
-// Output: one JSON object per (instruction, waves per SIMD) on stdout.
-// The kernels read no memory and write one word per lane and two per wave, into
-// buffers sized from the same grid constants.
+// A second kernel runs the stochastic quantizers' per-pair sequence from the
+// library's own device helpers (one SplitMix64 output and two stochastic FP4
+// conversions per element pair), 8 independent pairs per lane: the rate at which
+// the chip can produce stochastic-rounding decisions with no memory traffic.
+//
+// Output: one JSON object per measurement on stdout.  The kernels read no memory
+// and write one word per lane and two per wave, into buffers sized from the same
+// grid constants.
 #include <hip/hip_runtime.h>
+
+#include "../mxfp4_microscaling_quantization_amd/csrc/mx_device.h"
 
 #include <algorithm>
 #include <cstdint>
@@ -127,19 +134,86 @@ int measure_all(int cus, uint32_t* out, uint64_t* times) {
   return 0;
 }
 
+// MODE 0: SplitMix64 words + two conversions + merge (the quantizers' pair);
+// MODE 1: the SplitMix64 words alone; MODE 2: one stochastic conversion alone.
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void k_sr_pairs(uint32_t* out, uint64_t seed, float a) {
+  constexpr int kPairs = 8;
+  constexpr int kRounds = 256;
+  float v0[kPairs], v1[kPairs];
+  uint64_t z[kPairs];
+  uint32_t acc[kPairs];
+  const uint32_t gid = blockIdx.x * kThreads + threadIdx.x;
+  for (int i = 0; i < kPairs; ++i) {
+    v0[i] = a * (float)(threadIdx.x + i);
+    v1[i] = -a * (float)(i + 3);
+    z[i] = mx::sm64_state(seed, (uint64_t)gid * kPairs + i);
+    acc[i] = 0;
+  }
+  for (int it = 0; it < kRounds; ++it) {
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) {
+      if constexpr (MODE == 0) {
+        uint32_t hi, lo;
+        mx::sm64_words(z[i], hi, lo);
+        const uint32_t b0 = mx::cvt_sr_pair(v0[i], v1[i], hi, 0.5f);
+        const uint32_t b1 = mx::cvt_sr_pair(v0[i], v1[i], lo, 0.5f);
+        acc[i] ^= (b0 & 0x0Fu) | (b1 & ~0x0Fu);
+      }
+      if constexpr (MODE == 1) {
+        uint32_t hi, lo;
+        mx::sm64_words(z[i], hi, lo);
+        acc[i] ^= hi ^ lo;
+      }
+      if constexpr (MODE == 2) acc[i] ^= mx::cvt_sr_pair(v0[i], v1[i], acc[i] + (uint32_t)z[i], 0.5f);
+      z[i] += 2 * mx::kGamma;
+    }
+  }
+  uint32_t r = 0;
+  for (int i = 0; i < kPairs; ++i) r ^= acc[i];
+  out[gid] = r;
+}
+
+template <int MODE>
+int measure_sr(int cus, uint32_t* out) {
+  const int blocks = cus * 8;  // eight waves per SIMD
+  const char* names[3] = {"sr_pair", "splitmix64_words", "cvt_sr_pair"};
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  k_sr_pairs<MODE><<<blocks, kThreads>>>(out, 1, 1.1f);
+  CHECK(hipGetLastError());
+  constexpr int kReps = 5;
+  CHECK(hipEventRecord(e0));
+  for (int r = 0; r < kReps; ++r) k_sr_pairs<MODE><<<blocks, kThreads>>>(out, 1, 1.1f);
+  CHECK(hipEventRecord(e1));
+  CHECK(hipEventSynchronize(e1));
+  float ms = 0.f;
+  CHECK(hipEventElapsedTime(&ms, e0, e1));
+  const double pairs = (double)blocks * kThreads * 256 * 8 * kReps;
+  const double per_s = pairs / (ms * 1e-3);
+  std::printf("{\"sequence\": \"%s\", \"pairs_per_s\": %.4e, \"us_per_8192sq_elements\": %.2f}\n",
+              names[MODE], per_s, 8192.0 * 8192.0 / 2.0 / per_s * 1e6);
+  std::fflush(stdout);
+  CHECK(hipEventDestroy(e0));
+  CHECK(hipEventDestroy(e1));
+  return 0;
+}
+
 }  // namespace
 
 int main() {
   hipDeviceProp_t prop;
   CHECK(hipGetDeviceProperties(&prop, 0));
   const int cus = prop.multiProcessorCount;
-  const int max_blocks = cus * 4;
+  const int max_blocks = cus * 8;
   uint32_t* out = nullptr;
   uint64_t* times = nullptr;
   CHECK(hipMalloc(&out, (size_t)max_blocks * kThreads * sizeof(uint32_t)));
   CHECK(hipMalloc(&times, (size_t)max_blocks * 4 * 2 * sizeof(uint64_t)));
   std::printf("{\"cus\": %d, \"arch\": \"%s\"}\n", cus, prop.gcnArchName);
-  const int rc = measure_all<0>(cus, out, times);
+  int rc = measure_all<0>(cus, out, times);
+  if (rc == 0) rc = measure_sr<0>(cus, out) || measure_sr<1>(cus, out) || measure_sr<2>(cus, out);
   CHECK(hipFree(out));
   CHECK(hipFree(times));
   return rc;
