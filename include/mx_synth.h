@@ -1,6 +1,7 @@
 /*
  * mx_synth.h -- device-side generator of the synthetic optimizer steps that
- * drive the de-oscillation workload.  It is a workload generator, not part of
+ * drive the de-oscillation workload, exported by libmx355_synth.so (not by the
+ * product library libmx355.so).  It is a workload generator, not part of
  * the method: it stands in for the AdamW updates of a real training run
  * ("ALTO MXFP4 training -- Weight de-oscillation": the hook runs after each
  * AdamW step, which moves every weight by a small step).

@@ -20,6 +20,10 @@ CSRC = PKG / "csrc"
 BUILD = ROOT / "_build"
 LIB = PKG / "libmx355.so"
 SOURCES = ["quant.hip", "gemm.hip", "linear.hip", "deosc.hip"]
+# The synthetic optimizer step that drives the de-oscillation workload (a
+# workload generator, not part of the method) lives in a library of its own.
+SYNTH_LIB = PKG / "libmx355_synth.so"
+SYNTH_SOURCES = ["synth_step.hip"]
 ARCH = os.environ.get("MX_OFFLOAD_ARCH", "gfx950")
 
 # -ffp-contract=off: the quantizer, Hadamard and de-oscillation arithmetic is
@@ -101,13 +105,15 @@ def build_probe() -> Path:
 
 def build(verbose: bool = True) -> Path:
     BUILD.mkdir(exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES) + 1, os.cpu_count() or 4)) as ex:
+    srcs = SOURCES + SYNTH_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs) + 1, os.cpu_count() or 4)) as ex:
         probe = ex.submit(build_probe)
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, srcs))
         probe.result()
-    _link(objs, LIB)
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], SYNTH_LIB)
     if verbose:
-        print(f"built {LIB} and {PROBE}")
+        print(f"built {LIB}, {SYNTH_LIB.name} and {PROBE}")
     return LIB
 
 

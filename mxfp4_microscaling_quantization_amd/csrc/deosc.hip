@@ -1,5 +1,4 @@
-// Weight de-oscillation as a post-optimizer-step pass, and the synthetic
-// optimizer step that drives its workload.
+// Weight de-oscillation as a post-optimizer-step pass.
 //
 // "ALTO MXFP4 training -- Weight de-oscillation": over a window of P = 200
 // optimizer steps, sum per element how far the master weight travelled (d_w)
@@ -17,7 +16,6 @@
 
 #include "mx_device.h"
 #include "mx_host.h"
-#include "../../include/mx_synth.h"
 
 namespace mx {
 
@@ -167,26 +165,6 @@ __global__ __launch_bounds__(256) void k_deosc_init(const float4* __restrict__ w
   }
 }
 
-// Synthetic optimizer step (workload generator): Irwin-Hall(4) step of
-// standard deviation 1e-4 from four 24-bit SplitMix64 draws per element.
-constexpr uint32_t kSynthScaleBits = 0x2D359E63u;  // f32(sqrt(3) * 1e-4 * 2^-24)
-
-__global__ __launch_bounds__(256) void k_synth_step(float* __restrict__ w, int64_t n,
-                                                    uint64_t seed, uint64_t step) {
-  const float c = __uint_as_float(kSynthScaleBits);
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    int32_t acc = 0;
-#pragma unroll
-    for (uint64_t k = 0; k < 4; ++k) {
-      const uint64_t ctr = (step << 42) | (k << 40) | (uint64_t)i;
-      acc += (int32_t)sm64_top24(sm64_state(seed, ctr));
-    }
-    const float dw = (float)(acc - (1 << 25)) * c;
-    w[i] = w[i] + dw;
-  }
-}
-
 static int deosc_launch(float* w, int64_t rows, int64_t cols, float* w_prev, float* d_w, float* d_q,
                         int end, float threshold, uint8_t* flags, uint32_t* wq_codes,
                         uint8_t* wq_scales, hipStream_t st) {
@@ -262,16 +240,5 @@ extern "C" int mx_qema_step(const float* w, float* ema, int64_t rows, int64_t co
   const dim3 grid((unsigned)hmin(cdiv(nblk, 64), 256 * 32));
   k_qema_step<<<grid, 256, 0, as_stream(stream)>>>(w, ema, nblk, beta,
                                                    reinterpret_cast<uint32_t*>(wq_codes), wq_scales);
-  return launch_status();
-}
-
-extern "C" int mx_synth_step(float* w, int64_t n, uint64_t seed, int64_t step, void* stream) {
-  MX_REQUIRE(n >= 0 && n < ((int64_t)1 << 40) && step >= 0 && step < ((int64_t)1 << 22),
-             MX_ERR_SHAPE);
-  if (n == 0) return MX_OK;
-  MX_REQUIRE(w, MX_ERR_NULL);
-  MX_REQUIRE(aligned16(w), MX_ERR_ALIGN);
-  const dim3 grid((unsigned)hmin(cdiv(n, 256), 256 * 64));
-  k_synth_step<<<grid, 256, 0, as_stream(stream)>>>(w, n, seed, (uint64_t)step);
   return launch_status();
 }

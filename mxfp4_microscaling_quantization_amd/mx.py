@@ -1,4 +1,5 @@
-"""ctypes binding of libmx355.so (include/mx.h, include/mx_synth.h).
+"""ctypes binding of libmx355.so (include/mx.h) and of the workload generator
+libmx355_synth.so (include/mx_synth.h).
 
 Argument marshalling only: every step of the hot path runs in the HIP library.
 The functions named like the C entry points take torch tensors (device memory)
@@ -21,6 +22,7 @@ MX_RNE, MX_SR = 0, 1
 MX_MAX_GROUPS = 128
 
 LIB_PATH = Path(__file__).resolve().parent / "libmx355.so"
+SYNTH_LIB_PATH = Path(__file__).resolve().parent / "libmx355_synth.so"
 
 _c_void_p, _i64, _u64, _u32, _i32, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
                                                   ctypes.c_uint32, ctypes.c_int, ctypes.c_float,
@@ -61,10 +63,13 @@ SIGNATURES = {
     "mx_deosc_step": ([_P, _i64, _i64, _P, _P, _P, _i32, _f32, _P, _P], _i32),
     "mx_deosc_step_quantize": ([_P, _i64, _i64, _P, _P, _P, _i32, _f32, _P, _P, _P, _P], _i32),
     "mx_qema_step": ([_P, _P, _i64, _i64, _f32, _P, _P, _P], _i32),
+}
+SYNTH_SIGNATURES = {
     "mx_synth_step": ([_P, _i64, _u64, _i64, _P], _i32),
 }
 
 _lib = None
+_synth_lib = None
 
 
 class MxError(RuntimeError):
@@ -87,6 +92,23 @@ def lib() -> ctypes.CDLL:
             fn.restype = res
         _lib = handle
     return _lib
+
+
+def synth_lib() -> ctypes.CDLL:
+    """The workload generator's library (the synthetic optimizer steps); raises if
+    it has not been built."""
+    global _synth_lib
+    if _synth_lib is None:
+        if not SYNTH_LIB_PATH.exists():
+            raise RuntimeError(f"{SYNTH_LIB_PATH} is missing: build it with "
+                               "`python -m mxfp4_microscaling_quantization_amd.build`")
+        handle = ctypes.CDLL(str(SYNTH_LIB_PATH))
+        for name, (args, res) in SYNTH_SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _synth_lib = handle
+    return _synth_lib
 
 
 def status_string(status: int) -> str:
@@ -324,7 +346,7 @@ def mx_qema_step(w, ema, rows, cols, beta, wq_codes, wq_scales, stream=None):
 
 
 def mx_synth_step(w, n, seed, step, stream=None):
-    _check("mx_synth_step", lib().mx_synth_step(_ptr(w), n, seed, step, _stream(stream)))
+    _check("mx_synth_step", synth_lib().mx_synth_step(_ptr(w), n, seed, step, _stream(stream)))
 
 
 # ------------------------------------------------------------------ tensor conveniences

@@ -9,16 +9,14 @@ import pytest
 from mxfp4_microscaling_quantization_amd import mx
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("mx.h", "mx_synth.h")]
+PRODUCT_HEADER = os.path.join(ROOT, "include", "mx.h")
+SYNTH_HEADER = os.path.join(ROOT, "include", "mx_synth.h")
 
 
-def declared_functions():
-    names = set()
-    for h in HEADERS:
-        text = open(h).read()
-        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        names |= set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", text))
-    return names
+def declared_functions(header):
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", text))
 
 
 @pytest.fixture(scope="module")
@@ -27,11 +25,22 @@ def L():
 
 
 def test_every_declared_symbol_is_exported_and_bound(L):
-    names = declared_functions()
+    names = declared_functions(PRODUCT_HEADER)
     assert len(names) >= 12
     for n in names:
         assert hasattr(L, n), n
     assert names == set(mx.SIGNATURES), names ^ set(mx.SIGNATURES)
+
+
+def test_workload_generator_lives_outside_the_product_library(L):
+    """mx_synth.h's generator is exported by libmx355_synth.so only: the product
+    library carries nothing but the method."""
+    S = mx.synth_lib()
+    names = declared_functions(SYNTH_HEADER)
+    assert names == set(mx.SYNTH_SIGNATURES), names ^ set(mx.SYNTH_SIGNATURES)
+    for n in names:
+        assert hasattr(S, n), n
+        assert not hasattr(L, n), n
 
 
 def test_status_strings(L):
@@ -255,8 +264,9 @@ def test_deosc_validation(L):
     assert e(GOOD, GOOD, 4, 32, 0.998, GOOD, None, None) == mx.MX_ERR_NULL
     assert e(BAD, GOOD, 4, 32, 0.998, GOOD, GOOD, None) == mx.MX_ERR_ALIGN
     assert e(None, None, 4, 0, 0.998, None, None, None) == mx.MX_OK
-    assert L.mx_synth_step(GOOD, 1 << 41, 0, 1, None) == mx.MX_ERR_SHAPE
-    assert L.mx_synth_step(BAD, 16, 0, 1, None) == mx.MX_ERR_ALIGN
+    S = mx.synth_lib()
+    assert S.mx_synth_step(GOOD, 1 << 41, 0, 1, None) == mx.MX_ERR_SHAPE
+    assert S.mx_synth_step(BAD, 16, 0, 1, None) == mx.MX_ERR_ALIGN
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
