@@ -690,6 +690,15 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm_mx(
 // step j+3 into the stage of step j-1 is issued in C(j), after barrier 2j+1.
 // Each wave waits for its own share of step j+1 at the end of its L(j), by
 // barrier 2j+2 at the latest, before any wave reads that stage.
+// UNAL: scale rows whose groups are not 16-byte aligned (a packed operand with
+// K / 32 not a multiple of 16, such as the 90-byte rows of K = 2880, or a
+// contraction range starting off a 512 boundary).  A lane then fetches the two
+// aligned 16-byte pieces holding its row's group (the second only when it holds
+// a byte of the range, so no load leaves the 16-byte blocks that hold the
+// row's bytes) into sg and sgx, and at the end of L(4g + 3), once they have
+// landed, shifts the group into place in sg: the readers see the same layout
+// as in the aligned case.
+template <bool UNAL>
 __global__ __launch_bounds__(512) void k_gemm_pp(
     const uint8_t* __restrict__ A0, const uint8_t* __restrict__ SA0, const uint8_t* __restrict__ B0,
     const uint8_t* __restrict__ SB0, int64_t N0, int64_t K0, float alpha0, float* __restrict__ C0,
@@ -698,12 +707,15 @@ __global__ __launch_bounds__(512) void k_gemm_pp(
   constexpr int TM = 4, TN = 2;  // 32 x 32 MFMA tiles per wave along m and n
   constexpr int LA = 2, LB = 2;  // code DMAs per wave per step (16 rows each)
   constexpr int LC = LA + LB;
+  constexpr int GL = UNAL ? kPpGroupLoadsUnal : kPpGroupLoads;  // loads per scale group
   static_assert(LA * NW * 16 == BM && LB * NW * 16 == BN, "tile/wave mismatch");
-  static_assert(kPpLoads == LC && kPpGroupLoads == 1 && kPpLead == 3 && kPpWaitNear == LC &&
-                    kPpWaitFirst[0] == 0 && kPpWaitFirst[1] == LC && kPpWaitFirst[2] == 2 * LC,
+  static_assert(kPpLoads == LC && kPpGroupLoads == 1 && kPpGroupLoadsUnal == 2 && kPpLead == 3 &&
+                    kPpWaitNear == LC && kPpWaitFirst[0] == 0 && kPpWaitFirst[1] == LC &&
+                    kPpWaitFirst[2] == 2 * LC,
                 "schedule constants of gemm_schedule.h");
   __shared__ StageLds<BM, BN, kScGroup> ring[4];
   __shared__ ScaleGroupLds<BM, BN> sg[2];
+  __shared__ ScaleGroupLds<UNAL ? BM : 1, UNAL ? BN : 1> sgx;  // second pieces (UNAL)
 
   const TileWork tw = tile_work<BM, BN, false>(A0, SA0, B0, SB0, N0, K0, alpha0, C0, ldc0,
                                                b_stride_codes, b_stride_scales, gg, sp,
@@ -753,6 +765,9 @@ __global__ __launch_bounds__(512) void k_gemm_pp(
   const uint8_t* s_src =
       s_isA ? tw.SA + lmin(tw.m0 + s_r0 + lane, tw.a_last) * tw.lds_a + tw.k0 / 32
             : tw.SB + lmin(tw.n0 + s_r0 + lane, tw.N - 1) * tw.lds_b + tw.k0 / 32;
+  // UNAL: offset of the row's first scale byte in its aligned 16-byte piece
+  const uint32_t s_sh = (uint32_t)(reinterpret_cast<uintptr_t>(s_src) & 15);
+  const int64_t kc_blocks = tw.kc_blocks;
 
   auto issue = [&](int kt, auto S) {
     constexpr int P = decltype(S)::value;
@@ -765,7 +780,40 @@ __global__ __launch_bounds__(512) void k_gemm_pp(
   };
   auto issue_scales = [&](int g) {
     ScaleGroupLds<BM, BN>& t = sg[g & 1];
-    dma16(s_src + (int64_t)g * 16, s_isA ? &t.a[s_r0] : &t.b[s_r0]);
+    if constexpr (UNAL) {
+      // group g's bytes [s_src + 16 g, + 16) lie in the pieces at p0 and p0 + 16;
+      // byte s_src + 16 g is in the range (16 g < kc_blocks for every group the
+      // kernel loads), and the second piece is read only if it holds one too
+      const uint8_t* p0 = s_src - s_sh + (int64_t)g * 16;
+      const uint8_t* p1 = 16 * g + 16 < kc_blocks + s_sh ? p0 + 16 : p0;
+      dma16(p0, s_isA ? &t.a[s_r0] : &t.b[s_r0]);
+      dma16(p1, s_isA ? &sgx.a[s_r0] : &sgx.b[s_r0]);
+    } else {
+      dma16(s_src + (int64_t)g * 16, s_isA ? &t.a[s_r0] : &t.b[s_r0]);
+    }
+  };
+  // UNAL: this lane's row of group g (both pieces landed) shifted into place:
+  // bytes [s_sh, s_sh + 16) of the 32-byte pair become the row's 16 bytes in sg
+  auto align_group = [&](int g) {
+    if constexpr (UNAL) {
+      uint4* row = s_isA ? &sg[g & 1].a[s_r0 + lane] : &sg[g & 1].b[s_r0 + lane];
+      const uint4 lo = *row;
+      const uint4 hi = s_isA ? sgx.a[s_r0 + lane] : sgx.b[s_r0 + lane];
+      const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      // shift by s_sh >> 2 dwords with bit selects (a select written as an
+      // index would be lowered to a private-memory array), then by s_sh & 3 bytes
+      const uint32_t m2 = 0u - ((s_sh >> 3) & 1), m1 = 0u - ((s_sh >> 2) & 1), r = s_sh & 3;
+      uint32_t t[6], u[5];
+#pragma unroll
+      for (int i = 0; i < 6; ++i) t[i] = (w[i + 2] & m2) | (w[i] & ~m2);
+#pragma unroll
+      for (int i = 0; i < 5; ++i) u[i] = (t[i + 1] & m1) | (t[i] & ~m1);
+      // v_alignbyte: ({u[i + 1], u[i]} >> 8 r) [31:0]
+      *row = make_uint4(__builtin_amdgcn_alignbyte(u[1], u[0], r),
+                        __builtin_amdgcn_alignbyte(u[2], u[1], r),
+                        __builtin_amdgcn_alignbyte(u[3], u[2], r),
+                        __builtin_amdgcn_alignbyte(u[4], u[3], r));
+    }
   };
 
   v16f acc[TN][TM];
@@ -828,12 +876,15 @@ __global__ __launch_bounds__(512) void k_gemm_pp(
     // (in C(kt - 1)) and the scale groups issued in C(kt - 2) after that
     // step's loads and in C(kt - 1) (one per four steps)
     if constexpr (F) {
-      static_assert(kPpWaitFull[P] == LC + ((P == 1 || P == 2) ? 1 : 0), "schedule constants");
-      wait_vmcnt<kPpWaitFull[P]>();
+      constexpr int W = UNAL ? kPpWaitFullUnal[P] : kPpWaitFull[P];
+      static_assert(W == LC + ((P == 1 || P == 2) ? GL : 0), "schedule constants");
+      wait_vmcnt<W>();
     } else {
       if (kt + 2 < KT) wait_vmcnt<kPpWaitNear>();
       else wait_vmcnt<0>();
     }
+    // the next group, read from sg in L(kt + 1), has landed with step kt + 1
+    if (P == 3 && (F || kt + 1 < KT)) align_group((kt >> 2) + 1);
 #pragma unroll
     for (int i = 0; i < TM; ++i) sa[i] = reinterpret_cast<const uint32_t*>(&ga[i])[P] >> (8 * lh);
 #pragma unroll
@@ -928,7 +979,8 @@ __global__ __launch_bounds__(512) void k_gemm_pp(
   if (2 < KT) wait_vmcnt<kPpWaitFirst[2]>();
   else if (1 < KT) wait_vmcnt<kPpWaitFirst[1]>();
   else wait_vmcnt<kPpWaitFirst[0]>();
-  barrier();
+  if (0 < KT) align_group(0);
+  barrier_lds();
   if (grp == 1) barrier();  // group 1 runs one phase behind group 0
 
   using Full = std::true_type;
@@ -1012,8 +1064,9 @@ static int launch_gemm(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
   return launch_status();
 }
 
-// The ping-pong kernel for 256 x 256 tiles with group scale loads (no paired
-// second product).
+// The ping-pong kernel for 256 x 256 tiles (no paired second product); unal:
+// scale groups not 16-byte aligned.
+template <bool UNAL>
 static int launch_gemm_pp(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                           const uint8_t* sb, const int64_t* offs, int64_t groups, int64_t N,
                           int64_t K, float alpha, float* c, int64_t ldc, int64_t b_stride_codes,
@@ -1036,8 +1089,8 @@ static int launch_gemm_pp(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
   gg.row_off[groups] = offs[groups];
   const int total = gg.tile_start[groups] * sp.n;
   if (total == 0) return MX_OK;
-  k_gemm_pp<<<dim3(total), dim3(512), 0, st>>>(a, sa, b, sb, N, K, alpha, c, ldc, b_stride_codes,
-                                                b_stride_scales, gg, sp);
+  k_gemm_pp<UNAL><<<dim3(total), dim3(512), 0, st>>>(a, sa, b, sb, N, K, alpha, c, ldc,
+                                                      b_stride_codes, b_stride_scales, gg, sp);
   return launch_status();
 }
 
@@ -1093,13 +1146,19 @@ static int gemm_launch(const uint8_t* a, const uint8_t* sa, const uint8_t* b, co
   const bool big = !p1 && tiles256 * sp.n >= 512;
 #define MX_GEMM_ARGS a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes, b_stride_scales, lds_a, lds_b, sp, p1, st
   if (big) {
-    // group-mode scale loads leave registers for eight waves (two per SIMD, 128 x 64
-    // per wave: one wave's LDS waits and barrier overlap the other's MFMAs); the
-    // other modes keep four waves, where eight would spill in the K loop
-    // the ping-pong kernel addresses 256 rows of an operand with 32-bit offsets
-    if (sc == kScGroup && 256 * (K / 2) < ((int64_t)1 << 31))
-      return launch_gemm_pp(a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes,
-                            b_stride_scales, lds_a, lds_b, sp, st);
+    // the ping-pong kernel (eight waves, two per SIMD, 128 x 64 per wave: one
+    // wave's LDS waits and barrier overlap the other's MFMAs) takes scale rows in
+    // 16-byte groups, shifted into place when they are not 16-byte aligned; it
+    // addresses 256 rows of an operand with 32-bit offsets
+    if (256 * (K / 2) < ((int64_t)1 << 31)) {
+      if (sc == kScGroup)
+        return launch_gemm_pp<false>(a, sa, b, sb, offs, groups, N, K, alpha, c, ldc,
+                                     b_stride_codes, b_stride_scales, lds_a, lds_b, sp, st);
+      return launch_gemm_pp<true>(a, sa, b, sb, offs, groups, N, K, alpha, c, ldc, b_stride_codes,
+                                  b_stride_scales, lds_a, lds_b, sp, st);
+    }
+    // the four-wave kernel with per-step scale loads otherwise (eight waves would
+    // spill in its K loop)
     if (sc == kScGroup) return launch_gemm<256, 256, 2, 4, kScGroup>(MX_GEMM_ARGS);
     if (sc == kScDword) return launch_gemm<256, 256, 2, 2, kScDword>(MX_GEMM_ARGS);
     if (sc == kScShort) return launch_gemm<256, 256, 2, 2, kScShort>(MX_GEMM_ARGS);

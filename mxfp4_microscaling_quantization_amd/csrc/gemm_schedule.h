@@ -43,5 +43,12 @@ constexpr int kPpLead = 3;
 constexpr int kPpWaitFull[4] = {4, 5, 5, 4};
 constexpr int kPpWaitNear = 4;
 constexpr int kPpWaitFirst[3] = {0, 4, 8};
+// The same kernel on scale rows that are not 16-byte aligned (K / 32 not a
+// multiple of 16, e.g. 90-byte rows at K = 2880): a scale group is fetched as
+// the two aligned 16-byte pieces that hold it (kPpGroupLoadsUnal loads) and
+// shifted into place in LDS at the end of L(j), j % 4 == 3.  Code loads, lead
+// and the other waits are as above.
+constexpr int kPpGroupLoadsUnal = 2;
+constexpr int kPpWaitFullUnal[4] = {4, 6, 6, 4};
 
 }  // namespace mx

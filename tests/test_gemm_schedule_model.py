@@ -42,10 +42,13 @@ def header_constants():
     pp = dict(loads=scalar("kPpLoads"), group_loads=scalar("kPpGroupLoads"),
               lead=scalar("kPpLead"), wait_full=array("kPpWaitFull"),
               wait_near=scalar("kPpWaitNear"), wait_first=array("kPpWaitFirst"))
-    return modes, rows, pp
+    # unaligned scale rows: two loads per group, their own full-step waits
+    pp_unal = dict(pp, group_loads=scalar("kPpGroupLoadsUnal"),
+                   wait_full=array("kPpWaitFullUnal"))
+    return modes, rows, pp, pp_unal
 
 
-MODES, MX_ROWS, PP = header_constants()
+MODES, MX_ROWS, PP, PP_UNAL = header_constants()
 
 
 class Issued:
@@ -165,6 +168,21 @@ def test_mx_kernel_waits_for_what_it_reads(row):
 def test_pp_kernel_waits_for_what_it_reads():
     bad = [e for KT in range(1, 65) if (e := pp_violation(KT, PP))]
     assert not bad, bad[:3]
+
+
+def test_pp_kernel_with_unaligned_scale_rows_waits_for_what_it_reads():
+    """Two loads per scale group; the group is shifted into place at the end of
+    L(j), j % 4 == 3, the same point where the model requires it landed."""
+    assert PP_UNAL["group_loads"] == 2
+    bad = [e for KT in range(1, 65) if (e := pp_violation(KT, PP_UNAL))]
+    assert not bad, bad[:3]
+    # waiting for more (the aligned thresholds) stays safe; one more load in
+    # flight at P == 1 or 2 leaves a piece of the group in flight
+    tight = dict(PP_UNAL, wait_full=PP["wait_full"])
+    assert not any(pp_violation(KT, tight) for KT in range(1, 65))
+    loose = dict(PP_UNAL, wait_full=[w + (1 if i in (1, 2) else 0)
+                                     for i, w in enumerate(PP_UNAL["wait_full"])])
+    assert any(pp_violation(KT, loose) for KT in range(1, 65))
 
 
 def test_models_catch_a_wait_that_is_one_too_loose():

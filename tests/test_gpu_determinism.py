@@ -26,9 +26,9 @@ def gemm(a, b, M, N, K):
 
 @pytest.mark.parametrize("K", [1024, 640])
 def test_gemm_rows_do_not_depend_on_the_tile_path(K):
-    """A 4096 x 8192 product takes 256 x 256 tiles (the ping-pong kernel when K % 512
-    == 0, the four-wave kernel with per-step scale loads otherwise); 256-row slices
-    of it, launched alone, take 128 x 128 tiles.  Both sum every output over K in
+    """A 4096 x 8192 product takes 256 x 256 tiles (the ping-pong kernel, whose scale
+    groups are shifted into place when K % 512 != 0); 256-row slices of it, launched
+    alone, take 128 x 128 tiles.  Both sum every output over K in
     the same order (64-wide MFMA chunks in K order, no split), so the slices must
     equal the big product's rows bit for bit."""
     M, N = 4096, 8192

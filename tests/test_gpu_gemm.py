@@ -117,16 +117,42 @@ def test_gemm_tiny_config_end_to_end():
 
 @pytest.mark.parametrize("M,N,K", [(6144, 6144, 512),     # 16-byte scale groups: 2 x 4 waves
                                    (4000, 9000, 1536),    # the same, ragged M and N tiles
-                                   (6144, 6144, 640),     # dword scale loads: 2 x 2 waves
-                                   (5000, 7000, 2880),    # 2-byte scale loads, K tail
-                                   (6144, 6144, 480)])    # byte scale loads
+                                   (6144, 6144, 640),     # 20-byte scale rows
+                                   (5000, 7000, 2880),    # 90-byte scale rows, K tail
+                                   (6144, 6144, 480)])    # 15-byte scale rows
 def test_gemm_large_tile_path_sampled(M, N, K):
-    """Shapes that take the 256 x 256 workgroup tile in each of its wave layouts; 64
-    sampled rows (the last one always included) x all columns."""
+    """Shapes that take the 256 x 256 workgroup tile with aligned and unaligned scale
+    groups; 64 sampled rows (the last one always included) x all columns."""
     rng = np.random.default_rng(5)
     a = random_operand(rng, M, K)
     b = random_operand(rng, N, K)
     got = run_gemm(a, b, M, N, K)
+    rows = np.sort(np.append(rng.choice(M - 1, 63, replace=False), M - 1))
+    want = O.gemm(a[0][rows], a[1][rows], *b, 64, N, K)
+    assert_gemm_close(got[rows], want, O.gemm_abs(a[0][rows], a[1][rows], *b, 64, N, K), "sampled")
+
+
+@pytest.mark.parametrize("K,a_off,b_off", [(1056, 3, 0), (2880, 0, 7), (640, 5, 10)])
+def test_gemm_large_tiles_unaligned_scale_rows(K, a_off, b_off):
+    """256 x 256 tiles on scale rows that are not 16-byte aligned: rows of 33 (odd), 90 and
+    20 bytes, and scale arrays starting 3 to 10 bytes past a 16-byte boundary, so every
+    row's scale groups are shifted into place by a different amount; 64 sampled rows
+    (the last one always included, whose last group ends at the array's end)."""
+    M, N = 4096, 8192
+    rng = np.random.default_rng(K + a_off)
+    a = random_operand(rng, M, K)
+    b = random_operand(rng, N, K)
+
+    def shifted(scales, off):   # the same bytes, starting `off` bytes into a buffer
+        buf = torch.zeros(scales.size + 16, dtype=torch.uint8, device=DEV)
+        buf[off:off + scales.size] = to_dev_u8(scales.reshape(-1))
+        return buf[off:off + scales.size]
+
+    c = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    print(f"gemm {M}x{N}x{K} scales at +{a_off} / +{b_off}", flush=True)
+    mx.mx_gemm(to_dev_u8(a[0]), shifted(a[1], a_off), to_dev_u8(b[0]), shifted(b[1], b_off),
+               M, N, K, 1.0, c, N)
+    got = host(c)
     rows = np.sort(np.append(rng.choice(M - 1, 63, replace=False), M - 1))
     want = O.gemm(a[0][rows], a[1][rows], *b, 64, N, K)
     assert_gemm_close(got[rows], want, O.gemm_abs(a[0][rows], a[1][rows], *b, 64, N, K), "sampled")
