@@ -87,33 +87,36 @@ def _link(objs, lib: Path, extra=()) -> None:
     os.replace(tmp, lib)
 
 
-# The VALU issue-rate probe (a stand-alone program, not part of the library):
-# its figures weight the quantizers' instruction counts in the ALU roofline.
-PROBE_SRC = ROOT / "tests" / "valu_rate_probe.hip"
+# Rate probes (stand-alone programs, not part of the library): the VALU issue
+# rates weight the quantizers' instruction counts in the ALU roofline; the MFMA
+# probe measures the FP4 matrix instruction's sustained rate on register data.
+PROBE_NAMES = ("valu_rate_probe", "mfma_rate_probe")
 PROBE = BUILD / "valu_rate_probe"
 
 
-def build_probe() -> Path:
+def build_probe(name: str = "valu_rate_probe") -> Path:
     BUILD.mkdir(exist_ok=True)
-    cmd = [hipcc(), *[f for f in HIP_FLAGS if not f.startswith("-I")], str(PROBE_SRC), "-o",
-           str(PROBE)]
+    src = ROOT / "tests" / f"{name}.hip"
+    out = BUILD / name
+    cmd = [hipcc(), *[f for f in HIP_FLAGS if not f.startswith("-I")], str(src), "-o", str(out)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {PROBE_SRC.name}:\n{' '.join(cmd)}\n{res.stderr}")
-    return PROBE
+        raise RuntimeError(f"hipcc failed on {src.name}:\n{' '.join(cmd)}\n{res.stderr}")
+    return out
 
 
 def build(verbose: bool = True) -> Path:
     BUILD.mkdir(exist_ok=True)
     srcs = SOURCES + SYNTH_SOURCES
-    with cf.ThreadPoolExecutor(max_workers=min(len(srcs) + 1, os.cpu_count() or 4)) as ex:
-        probe = ex.submit(build_probe)
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs) + 2, os.cpu_count() or 4)) as ex:
+        probes = [ex.submit(build_probe, n) for n in PROBE_NAMES]
         objs = list(ex.map(_compile, srcs))
-        probe.result()
+        for f in probes:
+            f.result()
     _link(objs[:len(SOURCES)], LIB)
     _link(objs[len(SOURCES):], SYNTH_LIB)
     if verbose:
-        print(f"built {LIB}, {SYNTH_LIB.name} and {PROBE}")
+        print(f"built {LIB}, {SYNTH_LIB.name} and the probes {', '.join(PROBE_NAMES)} in {BUILD}")
     return LIB
 
 
