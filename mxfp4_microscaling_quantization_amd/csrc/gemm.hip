@@ -883,8 +883,6 @@ __global__ __launch_bounds__(512) void k_gemm_pp(
       if (kt + 2 < KT) wait_vmcnt<kPpWaitNear>();
       else wait_vmcnt<0>();
     }
-    // the next group, read from sg in L(kt + 1), has landed with step kt + 1
-    if (P == 3 && (F || kt + 1 < KT)) align_group((kt >> 2) + 1);
 #pragma unroll
     for (int i = 0; i < TM; ++i) sa[i] = reinterpret_cast<const uint32_t*>(&ga[i])[P] >> (8 * lh);
 #pragma unroll
@@ -906,6 +904,9 @@ __global__ __launch_bounds__(512) void k_gemm_pp(
         }
       }
     }
+    // the next group, read from sg in L(kt + 1), has landed with step kt + 1
+    // (after the scale dwords are taken, so the group registers are free)
+    if (P == 3 && (F || kt + 1 < KT)) align_group((kt >> 2) + 1);
     barrier_lds();
   };
   // MFMA i of a step: K-half i / 8, tile (a, b) = ((i % 8) / TM, i % TM)
