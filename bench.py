@@ -9,7 +9,10 @@ channels x30, weights N(0, 0.02), dY N(0, 1e-3)):
   one launch), GEMM dX, GEMM dW
 
 -- the kernels mx_linear_fwd / mx_linear_bwd launch, issued one entry point at
-a time on one stream.  value = 6 M N K / step time (TFLOP/s), the steps timed
+a time on one stream.  Before the warm-up steps the bench checks the composed
+step against the library's linear entry points (bit for bit) and then runs
+REPEAT_CHECK_STEPS steps whose outputs must equal the first step's (bit for
+bit); both checks are reported in the line.  value = 6 M N K / step time (TFLOP/s), the steps timed
 back to back with events at the two ends of the timed region only (an event
 record between kernels stops the next one from starting while the previous one
 drains).  The GEMM's launch duration for its roofline comes from a second pass
@@ -76,6 +79,8 @@ VALU_COST = {"v_mul_lo_u32": 1.67, "v_mad_u64_u32": 2.03, "v_lshrrev_b64": 1.64,
 # pair, in registers; tests/valu_rate_probe.hip): the floor of every stochastic
 # quantization of such a tensor.
 SR_PAIR_FLOOR_US = 23.4
+# steps of the determinism check that runs before the warm-up steps
+REPEAT_CHECK_STEPS = 25
 QUANT_SOURCES = ("quant.hip", "mx_device.h")
 # 256 CUs x 4 SIMDs x 32 lanes per clock (one wave64 instruction every 2 cycles)
 # x 2.4 GHz
@@ -252,6 +257,17 @@ def bench_linear(torch, mx, synth, dev, steps, warmup, seed=3):
     torch.cuda.synchronize()
     same = all(torch.equal(a, b) for a, b in ((y, y2), (dx, dx2), (dw, dw2)))
     del y2, xq2, wq2, dx2, dw2
+    # determinism over repeated steps: REPEAT_CHECK_STEPS more steps back to back
+    # must reproduce the first step's outputs bit for bit (stochastic rounding is
+    # keyed by seed and index, the GEMMs sum in a fixed order).  The device stays
+    # busy through this check, so after the host-side setup above its clock has
+    # left its idle state before the warm-up steps begin.
+    first = [t.clone() for t in (y, dx, dw, *q3, *q4, *q5, *q6)]
+    for _ in range(REPEAT_CHECK_STEPS):
+        step(None)
+    torch.cuda.synchronize()
+    repeat_same = all(torch.equal(a, b) for a, b in zip(first, (y, dx, dw, *q3, *q4, *q5, *q6)))
+    del first
     torch.cuda.synchronize()
     for _ in range(warmup):
         step(None)
@@ -301,6 +317,7 @@ def bench_linear(torch, mx, synth, dev, steps, warmup, seed=3):
         "gemm_ms": gemm_ms, "gemm_tflops": gemm_tf,
         "gemm_launches": T.count("gemm"), "kernels_us": {k: v * 1e3 for k, v in kern.items()},
         "quantizers": quant, "matches_linear_entry_points": bool(same),
+        "repeat_steps_identical": bool(repeat_same), "repeat_check_steps": REPEAT_CHECK_STEPS,
     }
 
 
@@ -671,7 +688,9 @@ def main():
                                "step_attainable_ms": lin["attainable_ms"],
                                "step_frac_attainable": lin["frac_attainable"],
                                "ms_per_step_with_gemm_events": lin["ms_per_step_with_gemm_events"],
-                               "matches_linear_entry_points": lin["matches_linear_entry_points"]}
+                               "matches_linear_entry_points": lin["matches_linear_entry_points"],
+                               "repeat_steps_identical": lin["repeat_steps_identical"],
+                               "repeat_check_steps": lin["repeat_check_steps"]}
     ach = lin["gemm_tflops"]
     line = {
         "metric": METRIC,
