@@ -47,6 +47,8 @@ int gemm_split_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const
                     SplitPlan plan, float* part, int64_t lds_a, int64_t lds_b, hipStream_t st);
 bool gemm_pairable(int64_t M0, int64_t N0, SplitPlan plan0, int64_t M1, int64_t N1,
                    SplitPlan plan1);
+SplitPlan gemm_paired_split_plan(int64_t M0, int64_t N0, int64_t K0, SplitPlan most, int64_t M1,
+                                 int64_t N1, int64_t K1);
 int gemm_pair_impl(const uint8_t* a0, const uint8_t* sa0, const uint8_t* b0, const uint8_t* sb0,
                    int64_t M0, int64_t N0, int64_t K0, float alpha0, float* c0, int64_t ldc0,
                    SplitPlan plan0, float* part0, int64_t lds_a0, int64_t lds_b0,
@@ -226,8 +228,11 @@ static int linear_bwd_impl(const void* dy, int dtype, int64_t M, int64_t N, int6
   const float alpha = had ? kHadamardAlpha : 1.0f;
   float* part = reinterpret_cast<float*>(ws + L.part);
   if (gemm_pairable(N, K, L.dw, M, K, L.dx)) {  // small products: dW and dX in one launch
+    // dW's split balanced against dX in the shared launch (at most the workspace's
+    // partial sums)
+    const SplitPlan pw = gemm_paired_split_plan(N, K, M, L.dw, M, K, N);
     return gemm_pair_impl(ws + L.q5c, ws + L.q5s, ws + L.q6c, ws + L.q6s, N, K, M, alpha, dw, K,
-                          L.dw, part, p5, p6, ws + L.q3c, ws + L.q3s, ws + L.q4c, ws + L.q4s, M,
+                          pw, part, p5, p6, ws + L.q3c, ws + L.q3s, ws + L.q4c, ws + L.q4s, M,
                           K, N, alpha, dx, K, p3, p4, st);
   }
   s = gemm_split_impl(ws + L.q3c, ws + L.q3s, ws + L.q4c, ws + L.q4s, M, K, N, alpha, dx, K, L.dx,
