@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
 #include <mutex>
 
 #include "mx_host.h"
@@ -47,8 +48,7 @@ int gemm_split_impl(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const
                     SplitPlan plan, float* part, int64_t lds_a, int64_t lds_b, hipStream_t st);
 bool gemm_pairable(int64_t M0, int64_t N0, SplitPlan plan0, int64_t M1, int64_t N1,
                    SplitPlan plan1);
-SplitPlan gemm_paired_split_plan(int64_t M0, int64_t N0, int64_t K0, SplitPlan most, int64_t M1,
-                                 int64_t N1, int64_t K1);
+
 int gemm_pair_impl(const uint8_t* a0, const uint8_t* sa0, const uint8_t* b0, const uint8_t* sb0,
                    int64_t M0, int64_t N0, int64_t K0, float alpha0, float* c0, int64_t ldc0,
                    SplitPlan plan0, float* part0, int64_t lds_a0, int64_t lds_b0,
@@ -74,6 +74,79 @@ int64_t segments_padded_rows(const int64_t* offs, int64_t groups, int64_t pad);
 void segments_padded_offsets(const int64_t* offs, int64_t groups, int64_t* out, int64_t pad);
 
 static size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Compute units of the current device (queried once per device).
+static int device_cus() {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static int cus[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+// Finish time of list scheduling n0 jobs of length a, then n1 of length b, on
+// `slots` machines (every job starts on the machine that frees first).
+static double list_makespan(int64_t n0, double a, int64_t n1, double b, int64_t slots) {
+  std::map<double, int64_t> free_at;  // finish time -> machines free from then on
+  free_at[0.0] = slots;
+  double end = 0.0;
+  auto run = [&](int64_t n, double len) {
+    while (n > 0) {
+      auto it = free_at.begin();
+      const double t = it->first;
+      const int64_t k = hmin(it->second, n);
+      n -= k;
+      if (k == it->second) free_at.erase(it);
+      else it->second -= k;
+      free_at[t + len] += k;
+      end = t + len > end ? t + len : end;
+    }
+  };
+  run(n0, a);
+  run(n1, b);
+  return end;
+}
+
+// The split of the first product of a paired launch (C0 [M0][N0], contraction
+// K0, at most most.n chunks: the workspace holds that many partial sums) that
+// finishes the launch and the pass adding its partial sums soonest, next to the
+// plain second product (C1 [M1][N1], contraction K1).  Both take 128 x 128
+// tiles, two workgroups per CU; a workgroup costs a fixed kWgSteps plus one per
+// K-step, dispatched first product first; the partial-sum pass costs
+// kSumStepsPerMB per MB of partial sums read plus kSumSteps.  (Constants from
+// the DeiT-S fc1 backward: ~0.5 us per K-step, ~3 us per workgroup outside its
+// K loop, ~4 TB/s for the pass.)  Chunks are multiples of 512 K-values.
+static SplitPlan gemm_paired_split_plan(int64_t M0, int64_t N0, int64_t K0, SplitPlan most, int64_t M1,
+                                 int64_t N1, int64_t K1) {
+  constexpr double kWgSteps = 6.0, kSumSteps = 4.0, kSumStepsPerMB = 0.5;
+  const int64_t slots = 2 * (int64_t)device_cus();
+  const int64_t t0 = cdiv(M0, 128) * cdiv(N0, 128), t1 = cdiv(M1, 128) * cdiv(N1, 128);
+  const double b = (double)cdiv(K1, 128) + kWgSteps;
+  const double mb = (double)M0 * N0 * 4 / 1e6;
+  SplitPlan best = {1, K0};
+  double best_cost = list_makespan(t0, (double)cdiv(K0, 128) + kWgSteps, t1, b, slots);
+  for (int n = 2; n <= most.n; ++n) {
+    const int64_t chunk = cdiv(cdiv(K0, n), 512) * 512;
+    if (cdiv(K0, chunk) != n) continue;  // the same split as a smaller n
+    const double cost = list_makespan(t0 * n, (double)cdiv(chunk, 128) + kWgSteps, t1, b, slots) +
+                        kSumSteps + kSumStepsPerMB * mb * n;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = SplitPlan{n, chunk};
+    }
+  }
+  return best;
+}
+
 
 // Scale rows of the backward operands in the workspace are padded to a
 // multiple of 16 bytes, so every product can load four steps' scales of a row
