@@ -75,24 +75,6 @@ void segments_padded_offsets(const int64_t* offs, int64_t groups, int64_t* out, 
 
 static size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Compute units of the current device (queried once per device).
-static int device_cus() {
-  constexpr int kMaxDev = 64;
-  static std::mutex mu;
-  static int cus[kMaxDev] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
-  std::lock_guard<std::mutex> lock(mu);
-  if (cus[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        v <= 0)
-      v = 256;
-    cus[dev] = v;
-  }
-  return cus[dev];
-}
-
 // Finish time of list scheduling n0 jobs of length a, then n1 of length b, on
 // `slots` machines (every job starts on the machine that frees first).
 static double list_makespan(int64_t n0, double a, int64_t n1, double b, int64_t slots) {
@@ -128,7 +110,7 @@ static double list_makespan(int64_t n0, double a, int64_t n1, double b, int64_t 
 static SplitPlan gemm_paired_split_plan(int64_t M0, int64_t N0, int64_t K0, SplitPlan most, int64_t M1,
                                  int64_t N1, int64_t K1) {
   constexpr double kWgSteps = 6.0, kSumSteps = 4.0, kSumStepsPerMB = 0.5;
-  const int64_t slots = 2 * (int64_t)device_cus();
+  const int64_t slots = 2 * (int64_t)device_cu_count();
   const int64_t t0 = cdiv(M0, 128) * cdiv(N0, 128), t1 = cdiv(M1, 128) * cdiv(N1, 128);
   const double b = (double)cdiv(K1, 128) + kWgSteps;
   const double mb = (double)M0 * N0 * 4 / 1e6;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/mx.h"
 
 namespace mx {
@@ -25,6 +27,25 @@ struct SplitPlan {
   int64_t kchunk;
 };
 inline int64_t hmin(int64_t a, int64_t b) { return a < b ? a : b; }
+
+// Compute units of the current device (queried once per device; 256 if the
+// runtime cannot tell).
+inline int device_cu_count() {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static int cus[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
 
 }  // namespace mx
 
