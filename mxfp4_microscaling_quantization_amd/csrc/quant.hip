@@ -317,13 +317,21 @@ __global__ __launch_bounds__(256) void k_quant_tile(
 
   // ---- load: chunk (r, c) = (j * 16 + tid / 16, tid % 16)
   const int lc = tid % CPR;
+  // Every lane issues all of its loads: a chunk outside the tile reads the
+  // tensor's first chunk instead and is zeroed by a mask.  The mask is opaque
+  // to the compiler, which would otherwise turn the zeroing back into a branch
+  // around each load, and the register copies at those branches' joins wait
+  // for the loads (all eight were not in flight together).
   uint4 ch[NLOAD];
 #pragma unroll
   for (int j = 0; j < NLOAD; ++j) {
     const int r = j * (256 / CPR) + tid / CPR;
-    ch[j] = make_uint4(0, 0, 0, 0);
-    if (r < nrows && lc * E < ncols)
-      ch[j] = *reinterpret_cast<const uint4*>(x + (row0 + r) * cols + col0 + lc * E);
+    const bool ok = r < nrows && lc * E < ncols;
+    const T* p = ok ? x + (row0 + r) * cols + col0 + lc * E : x;
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+    asm("" : "+v"(m));
+    ch[j] = make_uint4(w.x & m, w.y & m, w.z & m, w.w & m);
   }
 #pragma unroll
   for (int j = 0; j < NLOAD; ++j) {
