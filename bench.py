@@ -54,20 +54,20 @@ GEMM_SOURCES = ("gemm.hip", "gemm_schedule.h")
 # pass over that code.  Each such instruction occupies its SIMD VALU_COST times
 # as long as a simple one (measured by tests/valu_rate_probe.hip), so it adds
 # VALU_COST - 1 lane-op equivalents.
-QUANT_VALU = {"sha256": "204f4a46c458483570d848a9148ae7397c6a37e6b1e4dce1b8e84e20ec70640a",
+QUANT_VALU = {"sha256": "2326e7cc4e3dbb4c692234e2ddcb80d1004dc72ae0523a365f96b690686682cc",
                "per_elem": {
-    "row_sr": {"kernel": "k_quant_row<bf16, SR>", "lane_ops": 16.78, "elems": 32,
-               "counts": {"v_mul_lo_u32": 65, "v_mad_u64_u32": 35, "v_lshrrev_b64": 32,
+    "row_sr": {"kernel": "k_quant_row<bf16, SR>", "lane_ops": 16.56, "elems": 32,
+               "counts": {"v_mul_lo_u32": 65, "v_mad_u64_u32": 33, "v_lshrrev_b64": 32,
                           "v_cvt_scalef32_sr_pk_fp4_f32": 32}},
-    "col_sr": {"kernel": "k_quant_tile<bf16, SR>", "lane_ops": 17.05, "elems": 64,
+    "col_sr": {"kernel": "k_quant_tile<bf16, SR>", "lane_ops": 16.51, "elems": 64,
                "counts": {"v_mul_lo_u32": 154, "v_mad_u64_u32": 79, "v_lshrrev_b64": 64,
                           "v_cvt_scalef32_sr_pk_fp4_f32": 64}},
-    "dual_sr": {"kernel": "k_quant_tile<bf16, SR, row + column>", "lane_ops": 34.05, "elems": 64,
+    "dual_sr": {"kernel": "k_quant_tile<bf16, SR, row + column>", "lane_ops": 32.37, "elems": 64,
                 "quantizations": 2,
-                "counts": {"v_mul_lo_u32": 330, "v_mad_u64_u32": 167, "v_lshrrev_b64": 137,
+                "counts": {"v_mul_lo_u32": 288, "v_mad_u64_u32": 163, "v_lshrrev_b64": 137,
                            "v_cvt_scalef32_sr_pk_fp4_f32": 128}},
-    "requant_sr": {"kernel": "k_requant<SR>", "lane_ops": 19.16, "elems": 128,
-                   "counts": {"v_mul_lo_u32": 396, "v_mad_u64_u32": 202, "v_lshrrev_b64": 130,
+    "requant_sr": {"kernel": "k_requant<SR>", "lane_ops": 18.80, "elems": 128,
+                   "counts": {"v_mul_lo_u32": 272, "v_mad_u64_u32": 208, "v_lshrrev_b64": 130,
                               "v_cvt_scalef32_sr_pk_fp4_f32": 128}},
 }}
 # SIMD cycles per wave64 instruction relative to v_add_u32 (2 cycles), at four

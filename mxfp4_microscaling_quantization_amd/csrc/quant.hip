@@ -65,15 +65,15 @@ __device__ __forceinline__ uint32_t low_bytes4(uint32_t b0, uint32_t b1, uint32_
 
 // Quantize N = 4 or 8 consecutive values of a row block a lane holds (v[0] at an
 // even position in its block), given the block's scale byte; returns the packed
-// codes (element i in nibble i).  idx0 = logical index of v[0].
+// codes (element i in nibble i).  z = generator state keyed by v[0]'s logical
+// index (sm64_state(seed, index)); callers step it along with the index, since
+// the state is linear in the index.
 template <int ROUND, int N>
-__device__ __forceinline__ uint32_t quant_run(const float v[N], uint32_t byte, uint64_t seed,
-                                              uint64_t idx0) {
+__device__ __forceinline__ uint32_t quant_run(const float v[N], uint32_t byte, uint64_t z) {
   static_assert(N == 4 || N == 8, "runs of 4 or 8 values");
   if (byte == 255u) return 0u;
   const float sc = scale_of(byte);
   uint32_t b[N / 2];
-  uint64_t z = ROUND == MX_SR ? sm64_state(seed, idx0) : 0;
 #pragma unroll
   for (int p = 0; p < N / 2; ++p) {
     b[p] = code_pair<ROUND>(v[2 * p], v[2 * p + 1], sc, z);
@@ -84,9 +84,8 @@ __device__ __forceinline__ uint32_t quant_run(const float v[N], uint32_t byte, u
 }
 
 template <int ROUND>
-__device__ __forceinline__ uint32_t quant8(const float v[8], uint32_t byte, uint64_t seed,
-                                           uint64_t idx0) {
-  return quant_run<ROUND, 8>(v, byte, seed, idx0);
+__device__ __forceinline__ uint32_t quant8(const float v[8], uint32_t byte, uint64_t z) {
+  return quant_run<ROUND, 8>(v, byte, z);
 }
 
 // A workgroup takes 64 x kRowU consecutive blocks per iteration; its quad j
@@ -132,8 +131,10 @@ __global__ __launch_bounds__(256) void k_quant_row(const RowJobs<T> jobs, uint32
       const int64_t b = min(base + u * 64 + j, nblk - 1);
       load8<T>(x + b * 32 + q * 8, v[u]);
     }
+    // generator state of this lane's first element; block b + 64 is 2048 elements on
+    uint64_t z = ROUND == MX_SR ? sm64_state(seed, (uint64_t)(base + j) * 32 + q * 8) : 0;
 #pragma unroll
-    for (int u = 0; u < kRowU; ++u) {
+    for (int u = 0; u < kRowU; ++u, z += 2048 * kGamma) {
       const int64_t b = base + u * 64 + j;
       if (b >= nblk) break;  // quads past the end: whole quads, so the DPP partners agree
       if (HAD) {
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(256) void k_quant_row(const RowJobs<T> jobs, uint32
       for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[u][i]) & 0x7FFFFFFFu);
       m = quad_max_u32(m);
       const uint32_t byte = scale_byte_of(m);
-      codes[b * 4 + q] = quant8<ROUND>(v[u], byte, seed, (uint64_t)b * 32 + q * 8);
+      codes[b * 4 + q] = quant8<ROUND>(v[u], byte, z);
       if (q == 0) scales[LD ? (b / jobs.nbr) * jobs.sld + b % jobs.nbr : b] = (uint8_t)byte;
     }
   }
@@ -213,13 +214,25 @@ __device__ __forceinline__ TileRows tile_rows(const Segs& s, int TR, int64_t row
 constexpr int kTileR = 128;
 constexpr int kTileRowBytes = 256;
 
-// Quantize 32 values of one column block; returns the 16 code bytes as uint4.
-template <int ROUND>
-__device__ __forceinline__ uint4 quant_col32(float v[32], uint32_t& byte_out, uint64_t seed,
-                                             uint64_t idx0, uint64_t idx_step) {
-  uint32_t m = 0;
+// Largest sign-cleared bf16 pattern in each half of the words w[0..n), the two
+// halves at once (packed 16-bit max: exact, NaN and Inf patterns win).
+template <int N>
+__device__ __forceinline__ uint32_t bf16_pair_max(const uint32_t* w) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = {0, 0};
 #pragma unroll
-  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  for (int i = 0; i < N; ++i)
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+  return __builtin_bit_cast(uint32_t, m);
+}
+
+// Quantize 32 values of one column block whose largest sign-cleared float32
+// pattern is m; returns the 16 code bytes as uint4.  z = generator state keyed
+// by the block's first element (sm64_state(seed, index)); the block's elements
+// are idx_step apart in the logical tensor.
+template <int ROUND>
+__device__ __forceinline__ uint4 quant_col32_m(const float v[32], uint32_t m, uint32_t& byte_out,
+                                               uint64_t z0, uint64_t idx_step) {
   const uint32_t byte = scale_byte_of(m);
   byte_out = byte;
   uint32_t w[4] = {0, 0, 0, 0};
@@ -227,7 +240,7 @@ __device__ __forceinline__ uint4 quant_col32(float v[32], uint32_t& byte_out, ui
     const float sc = scale_of(byte);
     uint64_t z = 0, dz = 0;
     if (ROUND == MX_SR) {
-      z = sm64_state(seed, idx0);
+      z = z0;
       dz = 2 * idx_step * kGamma;   // next pair's key: two elements further down
     }
     uint32_t b[16];
@@ -240,6 +253,15 @@ __device__ __forceinline__ uint4 quant_col32(float v[32], uint32_t& byte_out, ui
     for (int q = 0; q < 4; ++q) w[q] = low_bytes4(b[4 * q], b[4 * q + 1], b[4 * q + 2], b[4 * q + 3]);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int ROUND>
+__device__ __forceinline__ uint4 quant_col32(const float v[32], uint32_t& byte_out, uint64_t z0,
+                                             uint64_t idx_step) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  return quant_col32_m<ROUND>(v, m, byte_out, z0, idx_step);
 }
 
 // Writes staged column-block codes/scales: output row (col0 + c) gets bytes
@@ -342,6 +364,14 @@ __global__ __launch_bounds__(256) void k_quant_tile(
   // ---- row pass (1x32 blocks) from registers
   static_assert(!(ROW && HAD) || E == 8, "rotated row pass needs one quad per block");
   if constexpr (ROW) {
+    // Chunk j lies 256 / CPR rows below chunk j - 1: its logical index, generator
+    // state and output addresses step by amounts uniform over the workgroup (the
+    // state is linear in the index), so no 64-bit products are formed per chunk.
+    const int64_t r_a = row0 + tid / CPR;
+    const uint64_t idx_a = (uint64_t)r_a * (uint64_t)cols + (uint64_t)(col0 + lc * E);
+    const uint64_t d_idx = (uint64_t)(256 / CPR) * (uint64_t)cols;
+    const uint64_t z_a = ROUND == MX_SR ? sm64_state(seed_row, idx_a) : 0;
+    uint8_t* const s_a = scales_row + r_a * sp_row + (col0 + lc * E) / 32;
 #pragma unroll
     for (int j = 0; j < NLOAD; ++j) {
       const int r = j * (256 / CPR) + tid / CPR;
@@ -360,15 +390,20 @@ __global__ __launch_bounds__(256) void k_quant_tile(
         fwht32_quad(v, qq);
       }
       uint32_t m = 0;
+      if constexpr (sizeof(T) == 2 && !HAD) {  // on the packed words: both halves at once
+        const uint32_t pm = bf16_pair_max<4>(w);
+        m = max(pm << 16, pm & 0xFFFF0000u);
+      } else {
 #pragma unroll
-      for (int i = 0; i < E; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+        for (int i = 0; i < E; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+      }
       m = rowblock_max_u32<E>(m);
       const uint32_t byte = scale_byte_of(m);
-      const uint64_t idx0 = (uint64_t)(row0 + r) * (uint64_t)cols + (uint64_t)(col0 + lc * E);
-      const uint32_t packed = quant_run<ROUND, E>(v, byte, seed_row, idx0);
+      const uint64_t idx0 = idx_a + (uint64_t)j * d_idx;
+      const uint32_t packed = quant_run<ROUND, E>(v, byte, z_a + (uint64_t)j * (d_idx * kGamma));
       if constexpr (E == 8) reinterpret_cast<uint32_t*>(codes_row)[idx0 / 8] = packed;
       else reinterpret_cast<uint16_t*>(codes_row)[idx0 / 4] = (uint16_t)packed;
-      if (lc % (32 / E) == 0) scales_row[(row0 + r) * sp_row + (col0 + lc * E) / 32] = (uint8_t)byte;
+      if (lc % (32 / E) == 0) s_a[(int64_t)j * (256 / CPR) * sp_row] = (uint8_t)byte;
     }
   }
   __syncthreads();
@@ -384,6 +419,13 @@ __global__ __launch_bounds__(256) void k_quant_tile(
     }
     __syncthreads();  // every thread has read the tile: s_codes may overwrite it
     if (active) {
+      // generator state of column p * CPT's block; column p * CPT + cc is cc elements on
+      const uint64_t zc =
+          ROUND == MX_SR ? sm64_state(seed_col, (uint64_t)(row0 + rb * 32) * (uint64_t)cols +
+                                                    (uint64_t)(col0 + p * CPT))
+                         : 0;
+      // bf16 without rotation: both columns' block maxima from the packed words
+      const uint32_t pm = sizeof(T) == 2 && !HAD ? bf16_pair_max<32>(raw) : 0u;
 #pragma unroll
       for (int cc = 0; cc < CPT; ++cc) {
         float v[32];
@@ -399,8 +441,14 @@ __global__ __launch_bounds__(256) void k_quant_tile(
         }
         const int c = p * CPT + cc;
         uint32_t byte;
-        const uint64_t idx0 = (uint64_t)(row0 + rb * 32) * (uint64_t)cols + (uint64_t)(col0 + c);
-        s_codes[c * NRB + rb] = quant_col32<ROUND>(v, byte, seed_col, idx0, (uint64_t)cols);
+        if constexpr (sizeof(T) == 2 && !HAD) {
+          const uint32_t m = cc ? (pm & 0xFFFF0000u) : (pm << 16);
+          s_codes[c * NRB + rb] =
+              quant_col32_m<ROUND>(v, m, byte, zc + (uint64_t)cc * kGamma, (uint64_t)cols);
+        } else {
+          s_codes[c * NRB + rb] =
+              quant_col32<ROUND>(v, byte, zc + (uint64_t)cc * kGamma, (uint64_t)cols);
+        }
         s_scales[c * NRB + rb] = (uint8_t)byte;
       }
     }
@@ -464,13 +512,20 @@ __global__ __launch_bounds__(256) void k_requant(const RqJob j0, const RqJob j1,
 
   if (rb < nrb && o * 4 < ncols) {
     const int64_t c0 = col0 + o * 4;
-    // rows at or past nreal are padding: load a valid row (never used) and zero it
+    // rows at or past nreal are padding: load the segment's last row instead (never
+    // used) and zero it.  Row i's addresses step from row 0's by i pitches, a
+    // product uniform over the workgroup.
+    const int64_t r_first = row0 + rb * 32, r_last = row0 + tr.nreal - 1;
+    const uint8_t* const cp0 = codes_in + r_first * ld_in + c0 / 2;
+    const uint8_t* const cpl = codes_in + r_last * ld_in + c0 / 2;
+    const uint8_t* const sp0 = scales_in + r_first * ld_sin + c0 / 32;
+    const uint8_t* const spl = scales_in + r_last * ld_sin + c0 / 32;
     uint32_t cw[32], sw[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const int64_t r = row0 + min(rb * 32 + i, tr.nreal - 1);
-      cw[i] = *reinterpret_cast<const uint16_t*>(codes_in + r * ld_in + c0 / 2);
-      sw[i] = scales_in[r * ld_sin + c0 / 32];
+      const bool real = rb * 32 + i < tr.nreal;
+      cw[i] = *reinterpret_cast<const uint16_t*>(real ? cp0 + i * ld_in : cpl);
+      sw[i] = *(real ? sp0 + i * ld_sin : spl);
     }
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
@@ -479,6 +534,10 @@ __global__ __launch_bounds__(256) void k_requant(const RqJob j0, const RqJob j1,
         sw[i] = 127;   // any finite scale
       }
     }
+    // generator state of column 4o's block; column 4o + cc is cc elements on
+    const uint64_t zc = ROUND == MX_SR ? sm64_state(seed, (uint64_t)(z * rows + row0 + rb * 32) *
+                                                              (uint64_t)cols + (uint64_t)(col0 + o * 4))
+                                       : 0;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {  // column 4o + cc: code byte cc / 2 of each row
       float v[32];
@@ -490,9 +549,7 @@ __global__ __launch_bounds__(256) void k_requant(const RqJob j0, const RqJob j1,
       }
       uint32_t byte;
       const int c = o * 4 + cc;
-      const uint64_t idx0 = (uint64_t)(z * rows + row0 + rb * 32) * (uint64_t)cols +
-                            (uint64_t)(col0 + c);
-      s_codes[c * NRB + rb] = quant_col32<ROUND>(v, byte, seed, idx0, (uint64_t)cols);
+      s_codes[c * NRB + rb] = quant_col32<ROUND>(v, byte, zc + (uint64_t)cc * kGamma, (uint64_t)cols);
       s_scales[c * NRB + rb] = (uint8_t)byte;
     }
   }
@@ -582,7 +639,8 @@ __global__ __launch_bounds__(256) void k_requant_rht(const RhtJobs jobs, int64_t
       fwht32_lane(v);
       uint32_t byte;
       const uint64_t idx0 = (uint64_t)(row0 + rb * 32) * (uint64_t)cols + (uint64_t)(col0 + c);
-      s_codes[c * NRB + rb] = quant_col32<ROUND>(v, byte, seed, idx0, (uint64_t)cols);
+      s_codes[c * NRB + rb] =
+          quant_col32<ROUND>(v, byte, ROUND == MX_SR ? sm64_state(seed, idx0) : 0, (uint64_t)cols);
       s_scales[c * NRB + rb] = (uint8_t)byte;
     }
   }
