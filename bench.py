@@ -54,17 +54,17 @@ GEMM_SOURCES = ("gemm.hip", "gemm_schedule.h")
 # pass over that code.  Each such instruction occupies its SIMD VALU_COST times
 # as long as a simple one (measured by tests/valu_rate_probe.hip), so it adds
 # VALU_COST - 1 lane-op equivalents.
-QUANT_VALU = {"sha256": "2326e7cc4e3dbb4c692234e2ddcb80d1004dc72ae0523a365f96b690686682cc",
+QUANT_VALU = {"sha256": "dc9a8e61fa6ea3b6a51138516eeb42eab9c7960f1a2aa2b8c4b04ec6920795f4",
                "per_elem": {
     "row_sr": {"kernel": "k_quant_row<bf16, SR>", "lane_ops": 16.56, "elems": 32,
                "counts": {"v_mul_lo_u32": 65, "v_mad_u64_u32": 33, "v_lshrrev_b64": 32,
                           "v_cvt_scalef32_sr_pk_fp4_f32": 32}},
-    "col_sr": {"kernel": "k_quant_tile<bf16, SR>", "lane_ops": 16.51, "elems": 64,
-               "counts": {"v_mul_lo_u32": 154, "v_mad_u64_u32": 79, "v_lshrrev_b64": 64,
+    "col_sr": {"kernel": "k_quant_tile<bf16, SR>", "lane_ops": 14.34, "elems": 64,
+               "counts": {"v_mul_lo_u32": 140, "v_mad_u64_u32": 73, "v_lshrrev_b64": 64,
                           "v_cvt_scalef32_sr_pk_fp4_f32": 64}},
-    "dual_sr": {"kernel": "k_quant_tile<bf16, SR, row + column>", "lane_ops": 32.37, "elems": 64,
+    "dual_sr": {"kernel": "k_quant_tile<bf16, SR, row + column>", "lane_ops": 30.56, "elems": 64,
                 "quantizations": 2,
-                "counts": {"v_mul_lo_u32": 288, "v_mad_u64_u32": 163, "v_lshrrev_b64": 137,
+                "counts": {"v_mul_lo_u32": 272, "v_mad_u64_u32": 163, "v_lshrrev_b64": 137,
                            "v_cvt_scalef32_sr_pk_fp4_f32": 128}},
     "requant_sr": {"kernel": "k_requant<SR>", "lane_ops": 18.80, "elems": 128,
                    "counts": {"v_mul_lo_u32": 272, "v_mad_u64_u32": 208, "v_lshrrev_b64": 130,

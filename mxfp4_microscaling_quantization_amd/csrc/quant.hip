@@ -339,21 +339,28 @@ __global__ __launch_bounds__(256) void k_quant_tile(
 
   // ---- load: chunk (r, c) = (j * 16 + tid / 16, tid % 16)
   const int lc = tid % CPR;
-  // Every lane issues all of its loads: a chunk outside the tile reads the
-  // tensor's first chunk instead and is zeroed by a mask.  The mask is opaque
-  // to the compiler, which would otherwise turn the zeroing back into a branch
-  // around each load, and the register copies at those branches' joins wait
-  // for the loads (all eight were not in flight together).
+  // Every lane issues all of its loads before the first wait.  Chunk j lies
+  // 256 / CPR rows below chunk j - 1 (a uniform step).  In a partial tile a chunk
+  // outside it reads the tensor's first chunk instead and is zeroed by a mask;
+  // the mask is opaque to the compiler, which would otherwise turn the zeroing
+  // back into a branch around each load, and the register copies at those
+  // branches' joins wait for the loads one by one.
   uint4 ch[NLOAD];
+  const T* const p_a = x + (row0 + tid / CPR) * cols + col0 + lc * E;
+  const int64_t d_p = (int64_t)(256 / CPR) * cols;
+  if (nrows >= kTileR && ncols >= TC) {  // whole tile (uniform)
 #pragma unroll
-  for (int j = 0; j < NLOAD; ++j) {
-    const int r = j * (256 / CPR) + tid / CPR;
-    const bool ok = r < nrows && lc * E < ncols;
-    const T* p = ok ? x + (row0 + r) * cols + col0 + lc * E : x;
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
-    uint32_t m = ok ? 0xFFFFFFFFu : 0u;
-    asm("" : "+v"(m));
-    ch[j] = make_uint4(w.x & m, w.y & m, w.z & m, w.w & m);
+    for (int j = 0; j < NLOAD; ++j) ch[j] = *reinterpret_cast<const uint4*>(p_a + j * d_p);
+  } else {
+#pragma unroll
+    for (int j = 0; j < NLOAD; ++j) {
+      const int r = j * (256 / CPR) + tid / CPR;
+      const bool ok = r < nrows && lc * E < ncols;
+      const uint4 w = *reinterpret_cast<const uint4*>(ok ? p_a + j * d_p : x);
+      uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+      asm("" : "+v"(m));
+      ch[j] = make_uint4(w.x & m, w.y & m, w.z & m, w.w & m);
+    }
   }
 #pragma unroll
   for (int j = 0; j < NLOAD; ++j) {
@@ -412,11 +419,11 @@ __global__ __launch_bounds__(256) void k_quant_tile(
   {
     const int p = tid % 64, rb = tid / 64;
     const bool active = rb < nrb && p * CPT < ncols;
+    // every thread reads (rb < NRB, p < 64: inside the tile) so that the values
+    // need no copies where the inactive threads' path joins
     uint32_t raw[32];
-    if (active) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) raw[i] = s_in[(rb * 32 + i) * (kTileRowBytes / 4) + p];
-    }
+    for (int i = 0; i < 32; ++i) raw[i] = s_in[(rb * 32 + i) * (kTileRowBytes / 4) + p];
     __syncthreads();  // every thread has read the tile: s_codes may overwrite it
     if (active) {
       // generator state of column p * CPT's block; column p * CPT + cc is cc elements on
