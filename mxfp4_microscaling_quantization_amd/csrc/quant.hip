@@ -528,18 +528,37 @@ __global__ __launch_bounds__(256) void k_requant(const RqJob j0, const RqJob j1,
     const uint8_t* const sp0 = scales_in + r_first * ld_sin + c0 / 32;
     const uint8_t* const spl = scales_in + r_last * ld_sin + c0 / 32;
     uint32_t cw[32], sw[32];
+    if (rb * 32 + 32 <= tr.nreal) {  // a whole row block: no padding rows
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const bool real = rb * 32 + i < tr.nreal;
-      cw[i] = *reinterpret_cast<const uint16_t*>(real ? cp0 + i * ld_in : cpl);
-      sw[i] = *(real ? sp0 + i * ld_sin : spl);
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (rb * 32 + i >= tr.nreal) {
-        cw[i] = 0;     // code +0
-        sw[i] = 127;   // any finite scale
+      for (int i = 0; i < 32; ++i) {
+        cw[i] = *reinterpret_cast<const uint16_t*>(cp0 + i * ld_in);
+        sw[i] = sp0[i * ld_sin];
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const bool real = rb * 32 + i < tr.nreal;
+        cw[i] = *reinterpret_cast<const uint16_t*>(real ? cp0 + i * ld_in : cpl);
+        sw[i] = *(real ? sp0 + i * ld_sin : spl);
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (rb * 32 + i >= tr.nreal) {
+          cw[i] = 0;     // code +0
+          sw[i] = 127;   // any finite scale
+        }
+      }
+    }
+    // Row scales 2^(byte - 127) as floats (byte 0: the subnormal 2^-127; 0xFF: +Inf,
+    // which makes every decoded value of the row NaN), and whether any row has the
+    // NaN scale: the column blocks' maxima are then taken on the decoded floats
+    // (|.| as an operand modifier), where a max would drop NaN.
+    float rs[32];
+    bool nan_row = false;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      rs[i] = __builtin_amdgcn_ldexpf(1.0f, (int)sw[i] - 127);
+      nan_row |= sw[i] == 255u;
     }
     // generator state of column 4o's block; column 4o + cc is cc elements on
     const uint64_t zc = ROUND == MX_SR ? sm64_state(seed, (uint64_t)(z * rows + row0 + rb * 32) *
@@ -550,13 +569,18 @@ __global__ __launch_bounds__(256) void k_requant(const RqJob j0, const RqJob j1,
       float v[32];
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        const float s = scale_of(sw[i]);
-        const mx_v2f r = cc < 2 ? decode_byte<0>(cw[i], s) : decode_byte<1>(cw[i], s);
+        const mx_v2f r = cc < 2 ? decode_byte<0>(cw[i], rs[i]) : decode_byte<1>(cw[i], rs[i]);
         v[i] = (cc & 1) ? r.y : r.x;
       }
+      // largest magnitude: non-negative floats order as their bit patterns
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[i]));
+      const uint32_t m = nan_row ? 0x7FC00000u : __float_as_uint(a);
       uint32_t byte;
       const int c = o * 4 + cc;
-      s_codes[c * NRB + rb] = quant_col32<ROUND>(v, byte, zc + (uint64_t)cc * kGamma, (uint64_t)cols);
+      s_codes[c * NRB + rb] =
+          quant_col32_m<ROUND>(v, m, byte, zc + (uint64_t)cc * kGamma, (uint64_t)cols);
       s_scales[c * NRB + rb] = (uint8_t)byte;
     }
   }
