@@ -54,9 +54,9 @@ GEMM_SOURCES = ("gemm.hip", "gemm_schedule.h")
 # pass over that code.  Each such instruction occupies its SIMD VALU_COST times
 # as long as a simple one (measured by tests/valu_rate_probe.hip), so it adds
 # VALU_COST - 1 lane-op equivalents.
-QUANT_VALU = {"sha256": "5bfc44a8ce06cc1bb7fb80b3f8cb1cbf644cd7163ee62fb24617fac11947da44",
+QUANT_VALU = {"sha256": "ccc96e99b6ec45bbf2099332e37b8308361e08a3d94e89033a51b0627dc3cd6e",
                "per_elem": {
-    "row_sr": {"kernel": "k_quant_row<bf16, SR>", "lane_ops": 16.56, "elems": 32,
+    "row_sr": {"kernel": "k_quant_row<bf16, SR>", "lane_ops": 15.56, "elems": 32,
                "counts": {"v_mul_lo_u32": 65, "v_mad_u64_u32": 33, "v_lshrrev_b64": 32,
                           "v_cvt_scalef32_sr_pk_fp4_f32": 32}},
     "col_sr": {"kernel": "k_quant_tile<bf16, SR>", "lane_ops": 14.34, "elems": 64,
@@ -66,7 +66,7 @@ QUANT_VALU = {"sha256": "5bfc44a8ce06cc1bb7fb80b3f8cb1cbf644cd7163ee62fb24617fac
                 "quantizations": 2,
                 "counts": {"v_mul_lo_u32": 272, "v_mad_u64_u32": 163, "v_lshrrev_b64": 137,
                            "v_cvt_scalef32_sr_pk_fp4_f32": 128}},
-    "requant_sr": {"kernel": "k_requant<SR>", "lane_ops": 14.98, "elems": 128,
+    "requant_sr": {"kernel": "k_requant<SR>", "lane_ops": 14.68, "elems": 128,
                    "counts": {"v_mul_lo_u32": 272, "v_mad_u64_u32": 208, "v_lshrrev_b64": 130,
                               "v_cvt_scalef32_sr_pk_fp4_f32": 128}},
 }}

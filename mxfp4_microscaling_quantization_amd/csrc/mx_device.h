@@ -137,6 +137,20 @@ __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+// Largest magnitude of v[0..n) as a float32 bit pattern, with gfx950's
+// NaN-propagating maximum and |.| operand modifiers (v_maximum3_f32: half an
+// instruction per value).  Non-negative floats order as their bit patterns, so
+// this is the integer maximum of the sign-cleared patterns, except that a NaN
+// input may come out as another NaN pattern; every NaN pattern (exponent field
+// 255) gives the same scale byte 0xFF.
+template <int N>
+__device__ __forceinline__ uint32_t amax_bits(const float* v) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) m = __builtin_elementwise_maximum(m, __builtin_fabsf(v[i]));
+  return __float_as_uint(m);
+}
+
 // Largest sign-cleared bit pattern over the 4 lanes of a quad (integer max of
 // |x| patterns: exact, and NaN/Inf patterns win).
 __device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {

@@ -142,10 +142,7 @@ __global__ __launch_bounds__(256) void k_quant_row(const RowJobs<T> jobs, uint32
         for (int i = 0; i < 8; ++i) v[u][i] = apply_sign(v[u][i], sign_mask, q * 8 + i);
         fwht32_quad(v[u], q);
       }
-      uint32_t m = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[u][i]) & 0x7FFFFFFFu);
-      m = quad_max_u32(m);
+      const uint32_t m = quad_max_u32(amax_bits<8>(v[u]));
       const uint32_t byte = scale_byte_of(m);
       codes[b * 4 + q] = quant8<ROUND>(v[u], byte, z);
       if (q == 0) scales[LD ? (b / jobs.nbr) * jobs.sld + b % jobs.nbr : b] = (uint8_t)byte;
@@ -258,10 +255,7 @@ __device__ __forceinline__ uint4 quant_col32_m(const float v[32], uint32_t m, ui
 template <int ROUND>
 __device__ __forceinline__ uint4 quant_col32(const float v[32], uint32_t& byte_out, uint64_t z0,
                                              uint64_t idx_step) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
-  return quant_col32_m<ROUND>(v, m, byte_out, z0, idx_step);
+  return quant_col32_m<ROUND>(v, amax_bits<32>(v), byte_out, z0, idx_step);
 }
 
 // Writes staged column-block codes/scales: output row (col0 + c) gets bytes
@@ -401,8 +395,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(
         const uint32_t pm = bf16_pair_max<4>(w);
         m = max(pm << 16, pm & 0xFFFF0000u);
       } else {
-#pragma unroll
-        for (int i = 0; i < E; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+        m = amax_bits<E>(v);
       }
       m = rowblock_max_u32<E>(m);
       const uint32_t byte = scale_byte_of(m);
@@ -550,16 +543,10 @@ __global__ __launch_bounds__(256) void k_requant(const RqJob j0, const RqJob j1,
       }
     }
     // Row scales 2^(byte - 127) as floats (byte 0: the subnormal 2^-127; 0xFF: +Inf,
-    // which makes every decoded value of the row NaN), and whether any row has the
-    // NaN scale: the column blocks' maxima are then taken on the decoded floats
-    // (|.| as an operand modifier), where a max would drop NaN.
+    // which makes every decoded value of the row NaN).
     float rs[32];
-    bool nan_row = false;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      rs[i] = __builtin_amdgcn_ldexpf(1.0f, (int)sw[i] - 127);
-      nan_row |= sw[i] == 255u;
-    }
+    for (int i = 0; i < 32; ++i) rs[i] = __builtin_amdgcn_ldexpf(1.0f, (int)sw[i] - 127);
     // generator state of column 4o's block; column 4o + cc is cc elements on
     const uint64_t zc = ROUND == MX_SR ? sm64_state(seed, (uint64_t)(z * rows + row0 + rb * 32) *
                                                               (uint64_t)cols + (uint64_t)(col0 + o * 4))
@@ -572,11 +559,7 @@ __global__ __launch_bounds__(256) void k_requant(const RqJob j0, const RqJob j1,
         const mx_v2f r = cc < 2 ? decode_byte<0>(cw[i], rs[i]) : decode_byte<1>(cw[i], rs[i]);
         v[i] = (cc & 1) ? r.y : r.x;
       }
-      // largest magnitude: non-negative floats order as their bit patterns
-      float a = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[i]));
-      const uint32_t m = nan_row ? 0x7FC00000u : __float_as_uint(a);
+      const uint32_t m = amax_bits<32>(v);
       uint32_t byte;
       const int c = o * 4 + cc;
       s_codes[c * NRB + rb] =
