@@ -130,6 +130,30 @@ def test_requantize_of_extreme_scales():
     assert_bytes_equal(host(co), wc, "codes")
 
 
+@pytest.mark.parametrize("rnd", [mx.MX_RNE, mx.MX_SR])
+def test_requantize_of_nan_and_overflowing_scales(rnd):
+    """Input scale bytes at the top of the E8M0 range: 0xFF decodes every value of
+    its row block to NaN (the column blocks through that row take the NaN scale and
+    zero codes, reading R4), and bytes 253 / 254 put the larger magnitudes past the
+    float32 range (decoded as +-Inf: non-finite column blocks as well), beside
+    ordinary bytes; rows past the first 32 keep finite scales."""
+    rng = np.random.default_rng(21)
+    rows, cols = 96, 128
+    codes = rng.integers(0, 16, (rows, cols)).astype(np.uint8)
+    c = O.pack_codes(codes)
+    s = rng.choice(np.array([0, 1, 100, 127, 200, 252], np.uint8), (rows, cols // 32))
+    s[3, 0] = 255
+    s[40, 2] = 254
+    s[41, 2] = 253
+    s[70, 1] = 255
+    co, so = mx.requantize(to_dev_u8(c), to_dev_u8(s), rows, cols, rnd, 17)
+    with np.errstate(over="ignore", invalid="ignore"):
+        wc, ws = O.requantize(c, s, rows, cols, rnd, 17)
+    assert (ws == 255).any() and (ws < 255).any()
+    assert_bytes_equal(host(so), ws, "scales")
+    assert_bytes_equal(host(co), wc, "codes")
+
+
 @pytest.mark.parametrize("rows,cols", [(64, 96), (288, 160)])
 def test_quantize_dual_equals_two_quantizations(rows, cols):
     for dtype in ("f32", "bf16"):
