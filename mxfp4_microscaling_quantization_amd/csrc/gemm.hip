@@ -749,7 +749,10 @@ __global__ __launch_bounds__(512) void k_gemm_pp(
     b_src[j] = tw.B + row * tw.ldk + tw.k0 / 2 + dc * 16;
   }
   // the same sources as 32-bit offsets from the tile's first row at the range's
-  // first K byte (the host guarantees 256 rows of either operand span < 2^31 B)
+  // first K byte (the host guarantees 256 rows of either operand span < 2^31 B);
+  // every load addresses through them, so no 64-bit per-lane pointer stays live
+  // across the K loop (held there, they spilled in the unaligned-scale variant:
+  // ~90 MB of scratch traffic per grouped MoE launch)
   const uint8_t* a_base = tw.A + tw.m0 * tw.ldk + tw.k0 / 2;
   const uint8_t* b_base = tw.B + tw.n0 * tw.ldk + tw.k0 / 2;
   uint32_t a_off[LA], b_off[LB];
@@ -774,9 +777,11 @@ __global__ __launch_bounds__(512) void k_gemm_pp(
     const int64_t kc = (int64_t)kt * 64;
     const int64_t coff = lmin(kc, lmax(kc_bytes - 16 - dc * 16, -dc * 16));
 #pragma unroll
-    for (int j = 0; j < LA; ++j) dma16(a_src[j] + coff, &ring[P].a.codes[((wave * LA + j) * 16) * 4]);
+    for (int j = 0; j < LA; ++j)
+      dma16(a_base + a_off[j] + coff, &ring[P].a.codes[((wave * LA + j) * 16) * 4]);
 #pragma unroll
-    for (int j = 0; j < LB; ++j) dma16(b_src[j] + coff, &ring[P].b.codes[((wave * LB + j) * 16) * 4]);
+    for (int j = 0; j < LB; ++j)
+      dma16(b_base + b_off[j] + coff, &ring[P].b.codes[((wave * LB + j) * 16) * 4]);
   };
   auto issue_scales = [&](int g) {
     ScaleGroupLds<BM, BN>& t = sg[g & 1];
@@ -932,11 +937,11 @@ __global__ __launch_bounds__(512) void k_gemm_pp(
     const uint8_t* bk = b_base + kc;
     auto load_a = [&](int j) {
       if (F) dma16s(ak, a_off[j], &ring[S3].a.codes[((wave * LA + j) * 16) * 4]);
-      else if (load) dma16(a_src[j] + coff, &ring[S3].a.codes[((wave * LA + j) * 16) * 4]);
+      else if (load) dma16(a_base + a_off[j] + coff, &ring[S3].a.codes[((wave * LA + j) * 16) * 4]);
     };
     auto load_b = [&](int j) {
       if (F) dma16s(bk, b_off[j], &ring[S3].b.codes[((wave * LB + j) * 16) * 4]);
-      else if (load) dma16(b_src[j] + coff, &ring[S3].b.codes[((wave * LB + j) * 16) * 4]);
+      else if (load) dma16(b_base + b_off[j] + coff, &ring[S3].b.codes[((wave * LB + j) * 16) * 4]);
     };
     auto one = [&](auto I) {
       constexpr int i = decltype(I)::value;
